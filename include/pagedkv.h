@@ -1,0 +1,201 @@
+/*
+ * pagedkv.h -- C ABI of the paged KV-cache decode library for AMD Instinct MI355X (gfx950).
+ *
+ * Single-query decode attention over a KV cache that lives in fixed-size physical blocks and
+ * is addressed through a per-sequence block table, plus the two calls that mutate the cache
+ * (append of new tokens, copy-on-write of a shared block) and a host-side refcounted block
+ * pool.
+ *
+ * Sources, cited by page title and section:
+ *   [P1] "PagedAttention: Virtual Memory for the KV Cache"
+ *   [P2] "Paged Attention and vLLM"
+ *   [P3] "KV Cache Optimization and Management"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers: "device" pointers address GPU memory that the caller allocated (hipMalloc or a
+ *   framework allocator); "host" pointers address CPU memory. The library never allocates,
+ *   frees or retains device memory: the caller owns every buffer, including the decode
+ *   workspace, whose size it queries first.
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream). Every device
+ *   call only enqueues work on that stream, in call order, and never synchronizes; ordering
+ *   between calls (append, then decode) comes from the stream.
+ * Errors: every int-returning call returns PKV_OK (0) or a negative PKV_ERR_* code and then
+ *   pkv_last_error() describes the failure. On an error nothing has been enqueued.
+ *   Host-side checks cover pointers, sizes, supported shapes and workspace size. Device-
+ *   resident contents (table entries, lengths, positions) are the caller's contract; the
+ *   kernels never access memory outside the pools for out-of-range contents (an attention row
+ *   whose table holds an out-of-range entry comes out as NaN; an append or copy with an
+ *   out-of-range target is skipped). Setting the environment variable PAGEDKV_VALIDATE=1
+ *   makes each call copy those contents to the host first (a synchronizing debug mode) and
+ *   return PKV_ERR_VALIDATION when they break the contract (pkv_set_validate switches the mode
+ *   at run time).
+ *
+ * Cache layout (the pages leave it to the kernel, [P1] "Block size is a kernel choice too"):
+ *   k_pool  [num_blocks][num_kv_heads][block_size][head_dim]   key rows of a block
+ *   v_pool  [num_blocks][num_kv_heads][head_dim][block_size]   values, transposed in a block
+ *   Both pools hold one layer and share the element type `kv_dtype`.
+ * Token p of sequence s sits in physical block block_tables[s][p / block_size] at offset
+ * p % block_size ([P1] "A block table preserves token order"; [P2] "Block Table and
+ * Logical-to-Physical Mapping", tau_s).
+ *
+ * Supported shapes: head_dim in {64, 128}; block_size in {16, 32}; kv_dtype PKV_F32, PKV_F16
+ * or PKV_BF16; G = num_q_heads / num_kv_heads an integer in 1..16 for 16-bit caches and in
+ * {1, 2, 4, 8} for PKV_F32.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,          /* null pointer, negative size, inconsistent sizes   */
+  PKV_ERR_UNSUPPORTED = -2,          /* head_dim / block_size / dtype / G not supported    */
+  PKV_ERR_WORKSPACE_TOO_SMALL = -3,  /* decode workspace smaller than the queried size     */
+  PKV_ERR_LAUNCH = -4,               /* the HIP runtime rejected a launch                  */
+  PKV_ERR_POOL_EXHAUSTED = -5,       /* no free block in a pkv_pool                        */
+  PKV_ERR_REFCOUNT = -6,             /* refcount would drop below zero / block not free    */
+  PKV_ERR_VALIDATION = -7            /* PAGEDKV_VALIDATE=1 found a contract violation      */
+};
+
+/* Message for the last error on the calling thread ("" if none). Owned by the library. */
+const char* pkv_last_error(void);
+
+/* ---------------------------------------------------------------------------------------
+ * Decode attention
+ *
+ * For every sequence s < num_seqs and query head h < num_q_heads, with g = h / G:
+ *   out[s][h][:] = softmax( q[s][h] . K_s^T * scale ) . V_s
+ * where K_s, V_s are the first context_lens[s] key and value rows of sequence s, read
+ * through its block table: [P2] "Block Table and Logical-to-Physical Mapping" (the equation
+ * for a_t, with V applied) -- the gather is fused, no contiguous copy is made. Keys and values
+ * of KV head g serve the G query heads g*G .. g*G+G-1 (grouped-query attention, [P1] "Where
+ * contiguous allocation wastes space" notes that GQA stores fewer KV heads).
+ * Long contexts are cut into partitions of `partition_tokens` tokens; each partition yields a
+ * partial (m, l, acc) and a second kernel merges them with the log-sum-exp rule of
+ * [P2] "Paged Attention CUDA Kernel". context_lens[s] == 0 gives a zero row.
+ *
+ *   out           device [num_seqs][num_q_heads][head_dim], element type out_dtype
+ *                 (PKV_F32, or the same 16-bit type as kv_dtype: round to nearest even)
+ *   q             device [num_seqs][num_q_heads][head_dim], element type kv_dtype
+ *   k_pool,v_pool device, layout above
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                 ceil(context_lens[s] / block_size) are never read
+ *   context_lens  device int32 [num_seqs], each in [0, max_context_len]
+ *   max_context_len  host int, an upper bound of context_lens (sizes the launch), at most
+ *                 max_blocks_per_seq * block_size
+ *   scale         softmax scale; <= 0 selects 1/sqrt(head_dim)
+ *   partition_tokens  0 = automatic, else a positive multiple of 32, at most 64*block_size
+ *   workspace     device scratch of at least pkv_decode_workspace_size(...) bytes (may be
+ *                 NULL when that size is 0); contents need no initialisation
+ * --------------------------------------------------------------------------------------- */
+size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int max_context_len, int partition_tokens);
+
+/* The partition length that partition_tokens = 0 selects for these sizes. */
+int pkv_decode_auto_partition(int num_seqs, int num_kv_heads, int max_context_len);
+
+int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_pool,
+                      const void* v_pool, int kv_dtype, const int32_t* block_tables,
+                      int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                      int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, float scale, int partition_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Append: store the keys and values of new tokens into their slots
+ * ([P1] "Growing a request"; [P2] "KV Cache Fundamentals": the cache grows by one row per
+ * head per generated token). For every i < num_tokens and KV head g:
+ *   slot = (block_tables[seq_ids[i]][positions[i] / block_size], positions[i] % block_size)
+ *   k_pool[slot.block][g][slot.offset][:] = k_new[i][g][:]
+ *   v_pool[slot.block][g][:][slot.offset] = v_new[i][g][:]
+ * The caller has already grown the table (and made shared blocks private, see
+ * cow_block_copy). Slots must be distinct; a bitwise copy, no rounding.
+ *   k_new, v_new  device [num_tokens][num_kv_heads][head_dim], element type kv_dtype
+ *   seq_ids, positions  device int32 [num_tokens]
+ * --------------------------------------------------------------------------------------- */
+int kv_cache_append(void* k_pool, void* v_pool, int kv_dtype, const void* k_new,
+                    const void* v_new, const int32_t* seq_ids, const int32_t* positions,
+                    int num_tokens, const int32_t* block_tables, int max_blocks_per_seq,
+                    int num_seqs, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                    void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Copy-on-write: copy the first n token slots of block src into block dst, for every KV
+ * head, keys and values ([P1] "Sharing a prefix and copying a partial block"; [P2]
+ * "Continuous Batching and Scheduler", the copy-on-write rule). Slots >= n of dst are left as
+ * they are. The host redirects the table entry and adjusts reference counts (pkv_pool_*).
+ *   src_blocks, dst_blocks  device int32 [num_pairs]; src != dst, all destinations distinct
+ *   num_tokens  device int32 [num_pairs] in [0, block_size], or NULL = whole blocks
+ * --------------------------------------------------------------------------------------- */
+int cow_block_copy(void* k_pool, void* v_pool, int kv_dtype, const int32_t* src_blocks,
+                   const int32_t* dst_blocks, const int32_t* num_tokens, int num_pairs,
+                   int num_kv_heads, int head_dim, int block_size, int num_blocks, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Host block pool: free list and reference counts of `num_blocks` physical block ids. No
+ * device memory. A block returns to the free list only when its count reaches zero
+ * ([P3] "PagedAttention: borrowing virtual memory", answer A6); a full pool is reported, not
+ * overwritten ([P1] "Growing a request": the scheduler needs an explicit policy).
+ * A pkv_pool is not thread-safe.
+ * --------------------------------------------------------------------------------------- */
+typedef struct pkv_pool pkv_pool;
+
+pkv_pool* pkv_pool_create(int num_blocks);            /* NULL on bad size / no memory      */
+void pkv_pool_destroy(pkv_pool* pool);
+int pkv_pool_alloc(pkv_pool* pool, int32_t* out_block);  /* lowest free id, count 1         */
+int pkv_pool_claim(pkv_pool* pool, int32_t block);       /* take a named free block         */
+int pkv_pool_incref(pkv_pool* pool, int32_t block);      /* +1 on a live block              */
+int pkv_pool_decref(pkv_pool* pool, int32_t block, int* freed);  /* -1; *freed = 1 at zero  */
+int pkv_pool_refcount(const pkv_pool* pool, int32_t block);      /* count, or <0 on error   */
+int pkv_pool_num_free(const pkv_pool* pool);
+
+/* Table helpers on one host table row (int32 [max_blocks]) of a sequence that currently
+ * holds `length` tokens.
+ *
+ * pkv_seq_prepare_write: make the slot of token `length` writable by this sequence alone.
+ *   If it starts a new logical block, a block is allocated and appended to the row
+ *   (*cow_n = -1). If it falls in a block whose count is > 1 (shared, partially filled), a
+ *   fresh block is allocated, the row entry is redirected to it, the old block loses one
+ *   reference, and (*cow_src, *cow_dst, *cow_n) name the copy the caller must enqueue with
+ *   cow_block_copy before writing (n = length % block_size). Otherwise nothing changes
+ *   (*cow_n = -1). *block and *offset receive the slot of token `length`.
+ * pkv_seq_fork: dst_row = src_row[0:num_blocks_used], one more reference on each block.
+ * pkv_seq_release: drop one reference on each of the first num_blocks_used entries; returns
+ *   the number of blocks that went back to the free list (or an error code).
+ */
+int pkv_seq_prepare_write(pkv_pool* pool, int32_t* table_row, int max_blocks, int length,
+                          int block_size, int32_t* block, int32_t* offset, int32_t* cow_src,
+                          int32_t* cow_dst, int32_t* cow_n);
+int pkv_seq_fork(pkv_pool* pool, const int32_t* src_row, int32_t* dst_row, int num_blocks_used);
+int pkv_seq_release(pkv_pool* pool, const int32_t* table_row, int num_blocks_used);
+
+/* ---------------------------------------------------------------------------------------
+ * Kernel timing (for tests and benchmarks). While enabled, every kernel this library
+ * launches is bracketed by a pair of hipEvents recorded on its launch stream.
+ * pkv_timing_query waits for the recorded events of kernels whose name contains `name`
+ * ("decode_partial", "splitk_reduce", "append", "cow", or "" for all) and returns their
+ * summed duration and launch count. Enabling clears earlier records.
+ * --------------------------------------------------------------------------------------- */
+int pkv_timing_enable(int on);
+int pkv_timing_query(const char* name, double* total_ms, int64_t* launches);
+
+/* Contract validation on (1) or off (0) for this process, overriding PAGEDKV_VALIDATE. */
+int pkv_set_validate(int on);
+
+/* Library version string. */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

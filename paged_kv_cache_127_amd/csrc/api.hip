@@ -1,0 +1,369 @@
+// C-ABI entry points: argument checks, kernel selection, launches on the caller's stream,
+// optional contract validation (PAGEDKV_VALIDATE=1) and kernel timing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "kernels.h"
+#include "pagedkv.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return PKV_OK;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* e = std::getenv(name);
+  if (!e || !*e) return dflt;
+  return std::atoi(e);
+}
+
+int g_validate = -1;   // -1: not decided yet, then 0 / 1
+
+bool validate_mode() {
+  if (g_validate < 0) g_validate = env_int("PAGEDKV_VALIDATE", 0) != 0 ? 1 : 0;
+  return g_validate == 1;
+}
+
+int elem_bytes(int dt) {
+  if (dt == PKV_F32) return 4;
+  if (dt == PKV_F16 || dt == PKV_BF16) return 2;
+  return 0;
+}
+
+int launch_error(hipError_t e, const char* what) {
+  return fail(PKV_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- kernel timing --------------------------------------------------------------------
+struct TimingRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_spare;
+
+hipEvent_t take_event() {
+  if (!g_spare.empty()) {
+    hipEvent_t e = g_spare.back();
+    g_spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t st, F&& launch) {
+  std::unique_lock<std::mutex> lk(g_tmu);
+  if (!g_timing) {
+    lk.unlock();
+    return launch();
+  }
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, st);
+  if (e != hipSuccess) return e;
+  e = launch();
+  hipError_t e2 = hipEventRecord(b, st);
+  g_recs.push_back({name, a, b});
+  return e != hipSuccess ? e : e2;
+}
+
+// ---- host copies for PAGEDKV_VALIDATE ------------------------------------------------
+bool copy_ints(std::vector<int32_t>& dst, const int32_t* src, size_t n, hipStream_t st) {
+  dst.resize(n);
+  if (n == 0) return true;
+  if (hipMemcpyAsync(dst.data(), src, n * sizeof(int32_t), hipMemcpyDeviceToHost, st) !=
+      hipSuccess)
+    return false;
+  return hipStreamSynchronize(st) == hipSuccess;
+}
+
+int choose_partition(int partition_tokens, int num_seqs, int num_kv_heads, int max_ctx) {
+  return partition_tokens > 0 ? partition_tokens
+                              : pkv_decode_auto_partition(num_seqs, num_kv_heads, max_ctx);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_err.c_str(); }
+
+const char* pkv_version(void) { return "pagedkv-gfx950 0.1"; }
+
+int pkv_decode_auto_partition(int num_seqs, int num_kv_heads, int max_context_len) {
+  (void)num_seqs;
+  (void)num_kv_heads;
+  (void)max_context_len;
+  return 512;
+}
+
+size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int max_context_len, int partition_tokens) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  const int P = choose_partition(partition_tokens, num_seqs, num_kv_heads, max_context_len);
+  if (P <= 0) return 0;
+  const size_t n_part = (size_t)((max_context_len + P - 1) / P);
+  if (n_part <= 1) return 0;
+  return (size_t)num_seqs * num_q_heads * n_part * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_pool,
+                      const void* v_pool, int kv_dtype, const int32_t* block_tables,
+                      int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                      int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, float scale, int partition_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+      num_blocks <= 0 || max_context_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "paged_attn_decode: non-positive size");
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
+    return fail(PKV_ERR_INVALID_ARG, "paged_attn_decode: null pointer");
+  if (elem_bytes(kv_dtype) == 0)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: kv_dtype %d", kv_dtype);
+  if (!(out_dtype == PKV_F32 || out_dtype == kv_dtype))
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: out_dtype %d with kv_dtype %d",
+                out_dtype, kv_dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: head_dim %d (64 or 128)", head_dim);
+  if (block_size != 16 && block_size != 32)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: block_size %d (16 or 32)", block_size);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "paged_attn_decode: %d query heads not a multiple of %d KV heads",
+                num_q_heads, num_kv_heads);
+  const int G = num_q_heads / num_kv_heads;
+  const bool wide = kv_dtype != PKV_F32;
+  bool use_mfma;
+  if (wide && G >= 2 && G <= 16) {
+    use_mfma = true;
+  } else if (G == 1 || (!wide && (G == 2 || G == 4 || G == 8))) {
+    use_mfma = false;
+  } else {
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: %d query heads per KV head", G);
+  }
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PKV_ERR_INVALID_ARG,
+                "paged_attn_decode: max_context_len %d exceeds table capacity %d x %d",
+                max_context_len, max_blocks_per_seq, block_size);
+  const int P = choose_partition(partition_tokens, num_seqs, num_kv_heads, max_context_len);
+  if (P <= 0 || P % 32 != 0 || P > 64 * block_size)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "paged_attn_decode: partition_tokens %d (a multiple of 32, at most 64 * block_size)",
+                P);
+  const int n_part_max = max_context_len > 0 ? (max_context_len + P - 1) / P : 1;
+  const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                max_context_len, P);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "paged_attn_decode: workspace %zu < %zu bytes",
+                workspace_bytes, need);
+  if ((int64_t)num_kv_heads * num_seqs * n_part_max > 0x7fffffffLL)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: grid too large");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+  if (validate_mode()) {
+    std::vector<int32_t> lens, tabs;
+    if (!copy_ints(lens, context_lens, num_seqs, st) ||
+        !copy_ints(tabs, block_tables, (size_t)num_seqs * max_blocks_per_seq, st))
+      return fail(PKV_ERR_LAUNCH, "paged_attn_decode: validation copy failed");
+    for (int s = 0; s < num_seqs; ++s) {
+      if (lens[s] < 0 || lens[s] > max_context_len)
+        return fail(PKV_ERR_VALIDATION, "context_lens[%d] = %d outside [0, %d]", s, lens[s],
+                    max_context_len);
+      const int nb = (lens[s] + block_size - 1) / block_size;
+      for (int j = 0; j < nb; ++j) {
+        const int b = tabs[(size_t)s * max_blocks_per_seq + j];
+        if (b < 0 || b >= num_blocks)
+          return fail(PKV_ERR_VALIDATION, "block_tables[%d][%d] = %d outside [0, %d)", s, j, b,
+                      num_blocks);
+      }
+    }
+  }
+
+  pkv::DecodeParams p{};
+  p.out = out;
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.tables = block_tables;
+  p.lens = context_lens;
+  p.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.num_blocks = num_blocks;
+  p.block_size = block_size;
+  p.partition = P;
+  p.n_part_max = n_part_max;
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim);
+  p.scale_log2 = sc * 1.4426950408889634f;
+  if (need > 0) {
+    const size_t rows = (size_t)num_seqs * num_q_heads * n_part_max;
+    float* ws = reinterpret_cast<float*>(workspace);
+    p.ws_acc = ws;
+    p.ws_m = ws + rows * head_dim;
+    p.ws_l = p.ws_m + rows;
+  }
+  static const int waves_env = env_int("PAGEDKV_DECODE_WAVES", 4);
+  const int waves = (waves_env == 1 || waves_env == 2 || waves_env == 4) ? waves_env : 4;
+
+  hipError_t e;
+  if (use_mfma) {
+    e = timed("decode_partial_mfma", st, [&] {
+      return pkv::launch_decode_mfma(p, kv_dtype, head_dim, block_size, waves, st);
+    });
+  } else {
+    e = timed("decode_partial_valu", st, [&] {
+      return pkv::launch_decode_valu(p, kv_dtype, head_dim, block_size, G, waves, st);
+    });
+  }
+  if (e != hipSuccess) return launch_error(e, "paged_attn_decode: decode kernel");
+  if (n_part_max > 1) {
+    e = timed("splitk_reduce", st,
+              [&] { return pkv::launch_splitk_reduce(p, kv_dtype, head_dim, st); });
+    if (e != hipSuccess) return launch_error(e, "paged_attn_decode: reduce kernel");
+  }
+  return ok();
+}
+
+int kv_cache_append(void* k_pool, void* v_pool, int kv_dtype, const void* k_new,
+                    const void* v_new, const int32_t* seq_ids, const int32_t* positions,
+                    int num_tokens, const int32_t* block_tables, int max_blocks_per_seq,
+                    int num_seqs, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                    void* stream) {
+  if (num_tokens < 0 || num_seqs <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "kv_cache_append: non-positive size");
+  if (num_tokens == 0) return ok();
+  if (!k_pool || !v_pool || !k_new || !v_new || !seq_ids || !positions || !block_tables)
+    return fail(PKV_ERR_INVALID_ARG, "kv_cache_append: null pointer");
+  const int es = elem_bytes(kv_dtype);
+  if (es == 0) return fail(PKV_ERR_UNSUPPORTED, "kv_cache_append: kv_dtype %d", kv_dtype);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (validate_mode()) {
+    std::vector<int32_t> sid, pos, tabs;
+    if (!copy_ints(sid, seq_ids, num_tokens, st) || !copy_ints(pos, positions, num_tokens, st) ||
+        !copy_ints(tabs, block_tables, (size_t)num_seqs * max_blocks_per_seq, st))
+      return fail(PKV_ERR_LAUNCH, "kv_cache_append: validation copy failed");
+    std::unordered_set<int64_t> slots;
+    for (int i = 0; i < num_tokens; ++i) {
+      if (sid[i] < 0 || sid[i] >= num_seqs)
+        return fail(PKV_ERR_VALIDATION, "seq_ids[%d] = %d outside [0, %d)", i, sid[i], num_seqs);
+      if (pos[i] < 0 || pos[i] / block_size >= max_blocks_per_seq)
+        return fail(PKV_ERR_VALIDATION, "positions[%d] = %d outside the table", i, pos[i]);
+      const int b = tabs[(size_t)sid[i] * max_blocks_per_seq + pos[i] / block_size];
+      if (b < 0 || b >= num_blocks)
+        return fail(PKV_ERR_VALIDATION, "token %d maps to block %d outside [0, %d)", i, b,
+                    num_blocks);
+      if (!slots.insert((int64_t)b * block_size + pos[i] % block_size).second)
+        return fail(PKV_ERR_VALIDATION, "token %d writes a slot another token writes", i);
+    }
+  }
+  pkv::AppendParams p{k_pool, v_pool, k_new, v_new, seq_ids, positions, block_tables,
+                      num_tokens, max_blocks_per_seq, num_seqs, num_kv_heads, head_dim,
+                      block_size, num_blocks};
+  hipError_t e = timed("append", st, [&] { return pkv::launch_append(p, es, st); });
+  if (e != hipSuccess) return launch_error(e, "kv_cache_append");
+  return ok();
+}
+
+int cow_block_copy(void* k_pool, void* v_pool, int kv_dtype, const int32_t* src_blocks,
+                   const int32_t* dst_blocks, const int32_t* num_tokens, int num_pairs,
+                   int num_kv_heads, int head_dim, int block_size, int num_blocks, void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "cow_block_copy: non-positive size");
+  if (num_pairs == 0) return ok();
+  if (!k_pool || !v_pool || !src_blocks || !dst_blocks)
+    return fail(PKV_ERR_INVALID_ARG, "cow_block_copy: null pointer");
+  const int es = elem_bytes(kv_dtype);
+  if (es == 0) return fail(PKV_ERR_UNSUPPORTED, "cow_block_copy: kv_dtype %d", kv_dtype);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (validate_mode()) {
+    std::vector<int32_t> src, dst, nt;
+    if (!copy_ints(src, src_blocks, num_pairs, st) || !copy_ints(dst, dst_blocks, num_pairs, st) ||
+        (num_tokens && !copy_ints(nt, num_tokens, num_pairs, st)))
+      return fail(PKV_ERR_LAUNCH, "cow_block_copy: validation copy failed");
+    std::unordered_set<int32_t> dsts;
+    for (int i = 0; i < num_pairs; ++i) {
+      if (src[i] < 0 || src[i] >= num_blocks || dst[i] < 0 || dst[i] >= num_blocks)
+        return fail(PKV_ERR_VALIDATION, "pair %d: block outside [0, %d)", i, num_blocks);
+      if (src[i] == dst[i]) return fail(PKV_ERR_VALIDATION, "pair %d: src == dst", i);
+      if (!dsts.insert(dst[i]).second)
+        return fail(PKV_ERR_VALIDATION, "pair %d: destination used twice", i);
+      if (num_tokens && (nt[i] < 0 || nt[i] > block_size))
+        return fail(PKV_ERR_VALIDATION, "pair %d: %d tokens", i, nt[i]);
+    }
+    for (int i = 0; i < num_pairs; ++i)
+      if (dsts.count(src[i]))
+        return fail(PKV_ERR_VALIDATION, "pair %d: source is another pair's destination", i);
+  }
+  pkv::CowParams p{k_pool, v_pool, src_blocks, dst_blocks, num_tokens, num_pairs,
+                   num_kv_heads, head_dim, block_size, num_blocks};
+  hipError_t e = timed("cow", st, [&] { return pkv::launch_cow(p, es, st); });
+  if (e != hipSuccess) return launch_error(e, "cow_block_copy");
+  return ok();
+}
+
+int pkv_set_validate(int on) {
+  g_validate = on ? 1 : 0;
+  return ok();
+}
+
+int pkv_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (auto& r : g_recs) {
+    g_spare.push_back(r.start);
+    g_spare.push_back(r.stop);
+  }
+  g_recs.clear();
+  g_timing = on != 0;
+  return ok();
+}
+
+int pkv_timing_query(const char* name, double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return fail(PKV_ERR_INVALID_ARG, "pkv_timing_query: null pointer");
+  std::lock_guard<std::mutex> lk(g_tmu);
+  double tot = 0.0;
+  int64_t n = 0;
+  for (auto& r : g_recs) {
+    if (name && *name && !std::strstr(r.name, name)) continue;
+    if (hipEventSynchronize(r.stop) != hipSuccess)
+      return fail(PKV_ERR_LAUNCH, "pkv_timing_query: event wait failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+      return fail(PKV_ERR_LAUNCH, "pkv_timing_query: elapsed time failed");
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Cache mutations: bitwise stores of new tokens into their slots, and copy-on-write of the
+// valid slots of a shared block.
+//
+// Append ("PagedAttention: Virtual Memory for the KV Cache", section "Growing a request";
+// "Paged Attention and vLLM", section "KV Cache Fundamentals"): token i of sequence
+// seq_ids[i] at position positions[i] goes to block table[seq][pos / B], offset pos % B.
+// Copy-on-write (first page, section "Sharing a prefix and copying a partial block"; second
+// page, the copy-on-write rule under "Continuous Batching and Scheduler"): slots [0, n) of
+// every KV head, keys and values, from block src to block dst.
+// Out-of-range sequence ids, positions or block ids are skipped (never dereferenced).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace pkv {
+
+template <typename E>
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+  const int D = p.head_dim, B = p.block_size, H = p.num_kv_heads;
+  const int64_t total = (int64_t)p.num_tokens * H * D;
+  E* kp = reinterpret_cast<E*>(p.k_pool);
+  E* vp = reinterpret_cast<E*>(p.v_pool);
+  const E* kn = reinterpret_cast<const E*>(p.k_new);
+  const E* vn = reinterpret_cast<const E*>(p.v_new);
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int d = (int)(idx % D);
+    const int64_t t = idx / D;
+    const int g = (int)(t % H);
+    const int i = (int)(t / H);
+    const int s = p.seq_ids[i];
+    const int pos = p.positions[i];
+    if ((unsigned)s >= (unsigned)p.num_seqs || pos < 0) continue;
+    const int j = pos / B;
+    if (j >= p.max_blocks) continue;
+    const int blk = p.tables[(size_t)s * p.max_blocks + j];
+    if ((unsigned)blk >= (unsigned)p.num_blocks) continue;
+    const int off = pos - j * B;
+    const size_t hb = (size_t)blk * H + g;
+    kp[(hb * B + off) * D + d] = kn[idx];
+    vp[(hb * D + d) * B + off] = vn[idx];
+  }
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void cow_kernel(CowParams p) {
+  const int D = p.head_dim, B = p.block_size, H = p.num_kv_heads;
+  const int pair = blockIdx.x / H;
+  const int g = blockIdx.x % H;
+  const int src = p.src[pair];
+  const int dst = p.dst[pair];
+  const int n = p.ntok ? p.ntok[pair] : B;
+  if ((unsigned)src >= (unsigned)p.num_blocks || (unsigned)dst >= (unsigned)p.num_blocks ||
+      src == dst || n < 0 || n > B)
+    return;
+  E* kp = reinterpret_cast<E*>(p.k_pool);
+  E* vp = reinterpret_cast<E*>(p.v_pool);
+  const size_t sb = ((size_t)src * H + g) * B * D;
+  const size_t db = ((size_t)dst * H + g) * B * D;
+  // keys: rows [0, n) are contiguous
+  for (int e = threadIdx.x; e < n * D; e += blockDim.x) kp[db + e] = kp[sb + e];
+  // values: head-dim row r holds its B slots contiguously; copy the first n of each row
+  for (int e = threadIdx.x; e < n * D; e += blockDim.x) {
+    const int r = e / n, t = e - r * n;
+    vp[db + (size_t)r * B + t] = vp[sb + (size_t)r * B + t];
+  }
+}
+
+hipError_t launch_append(const AppendParams& p, int elem_bytes, hipStream_t st) {
+  const int64_t total = (int64_t)p.num_tokens * p.num_kv_heads * p.head_dim;
+  if (total <= 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (elem_bytes == 4)
+    hipLaunchKernelGGL(append_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL(append_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_cow(const CowParams& p, int elem_bytes, hipStream_t st) {
+  const int64_t grid = (int64_t)p.num_pairs * p.num_kv_heads;
+  if (grid <= 0) return hipSuccess;
+  if (elem_bytes == 4)
+    hipLaunchKernelGGL(cow_kernel<uint32_t>, dim3((unsigned)grid), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL(cow_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

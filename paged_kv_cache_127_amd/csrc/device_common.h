@@ -1,0 +1,130 @@
+// Device helpers shared by the gfx950 kernels: element types, 16-byte loads, conversions,
+// wavefront reductions (DPP within 16-lane rows, cross-row swaps), launch parameter blocks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct bf16_t { uint16_t bits; };   // storage tag for bfloat16 caches
+struct f16_t { uint16_t bits; };    // storage tag for IEEE half caches
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kBytes = 4;
+  __device__ static float to_f32(uint32_t u) { return __uint_as_float(u); }
+};
+template <> struct Elem<f16_t> {
+  static constexpr int kBytes = 2;
+  typedef f16x8 mfma_vec;
+  __device__ static float to_f32(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)u);
+  }
+  __device__ static uint16_t from_f32(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+};
+template <> struct Elem<bf16_t> {
+  static constexpr int kBytes = 2;
+  typedef bf16x8 mfma_vec;
+  __device__ static float to_f32(uint32_t u) { return __uint_as_float(u << 16); }
+  __device__ static uint16_t from_f32(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+};
+
+// 16-byte global load (global_load_dwordx4).
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// low / high 16-bit halves of a packed word, widened to fp32
+template <typename T> __device__ __forceinline__ float lo16(uint32_t w) {
+  return Elem<T>::to_f32(w & 0xffffu);
+}
+template <typename T> __device__ __forceinline__ float hi16(uint32_t w) {
+  return Elem<T>::to_f32(w >> 16);
+}
+
+// ---- wavefront data movement ----------------------------------------------------------
+// DPP controls (GCN/CDNA encoding)
+constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7-i inside each half row
+constexpr int kRowMirror = 0x140;      // lane i <-> 15-i inside each row
+
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float xor_lane(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+// Sum over aligned groups of N lanes (N = 2..64); every lane of a group receives the sum.
+template <int N> __device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp<kQuadXor1>(v);
+  if constexpr (N >= 4) v += dpp<kQuadXor2>(v);
+  if constexpr (N >= 8) v += dpp<kRowHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp<kRowMirror>(v);
+  if constexpr (N >= 32) v += xor_lane(v, 16);
+  if constexpr (N >= 64) v += xor_lane(v, 32);
+  return v;
+}
+
+// Max over lanes that differ only in the lane-index bits from FIRST_BIT up to bit 5.
+template <int FIRST> __device__ __forceinline__ float cross_max(float v) {
+  if constexpr (FIRST <= 1) v = fmaxf(v, dpp<kQuadXor1>(v));
+  if constexpr (FIRST <= 2) v = fmaxf(v, dpp<kQuadXor2>(v));
+  if constexpr (FIRST <= 4) v = fmaxf(v, xor_lane(v, 4));
+  if constexpr (FIRST <= 8) v = fmaxf(v, xor_lane(v, 8));
+  if constexpr (FIRST <= 16) v = fmaxf(v, xor_lane(v, 16));
+  if constexpr (FIRST <= 32) v = fmaxf(v, xor_lane(v, 32));
+  return v;
+}
+template <int FIRST> __device__ __forceinline__ float cross_sum(float v) {
+  if constexpr (FIRST <= 1) v += dpp<kQuadXor1>(v);
+  if constexpr (FIRST <= 2) v += dpp<kQuadXor2>(v);
+  if constexpr (FIRST <= 4) v += xor_lane(v, 4);
+  if constexpr (FIRST <= 8) v += xor_lane(v, 8);
+  if constexpr (FIRST <= 16) v += xor_lane(v, 16);
+  if constexpr (FIRST <= 32) v += xor_lane(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ---- launch parameter blocks ----------------------------------------------------------
+struct DecodeParams {
+  void* out;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* tables;
+  const int32_t* lens;
+  float* ws_acc;   // [S][Hq][n_part_max][D]
+  float* ws_m;     // [S][Hq][n_part_max]
+  float* ws_l;     // [S][Hq][n_part_max]
+  int out_f32;     // 1: fp32 output, 0: output in the cache's 16-bit type
+  int max_blocks;
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int num_blocks;
+  int block_size;
+  int partition;   // tokens per partition, multiple of 32, <= 64 * block_size
+  int n_part_max;  // ceil(max_context_len / partition)
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+}  // namespace pkv

@@ -1,0 +1,51 @@
+// Internal launch interface between the C-ABI layer and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+namespace pkv {
+
+// Decode, one partial state per (sequence, KV head, partition). kv_dtype: 0 f32, 1 f16, 2 bf16.
+hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, int head_dim, int block_size,
+                              int waves, hipStream_t st);
+hipError_t launch_decode_valu(const DecodeParams& p, int kv_dtype, int head_dim, int block_size,
+                              int group, int waves, hipStream_t st);
+hipError_t launch_splitk_reduce(const DecodeParams& p, int kv_dtype, int head_dim,
+                                hipStream_t st);
+
+struct AppendParams {
+  void* k_pool;
+  void* v_pool;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* seq_ids;
+  const int32_t* positions;
+  const int32_t* tables;
+  int num_tokens;
+  int max_blocks;
+  int num_seqs;
+  int num_kv_heads;
+  int head_dim;
+  int block_size;
+  int num_blocks;
+};
+hipError_t launch_append(const AppendParams& p, int elem_bytes, hipStream_t st);
+
+struct CowParams {
+  void* k_pool;
+  void* v_pool;
+  const int32_t* src;
+  const int32_t* dst;
+  const int32_t* ntok;   // may be null: whole blocks
+  int num_pairs;
+  int num_kv_heads;
+  int head_dim;
+  int block_size;
+  int num_blocks;
+};
+hipError_t launch_cow(const CowParams& p, int elem_bytes, hipStream_t st);
+
+}  // namespace pkv
