@@ -1,0 +1,214 @@
+"""Benchmark of the paged decode step on one MI355X.
+
+Workload (one "step" = one pass of the whole decode path over one batch): the GQA decode
+batch -- 256 sequences, 64 query / 8 KV heads, head_dim 128, bf16 cache, 16-token blocks at
+seeded random physical placement, context lengths log-normal (median 512, sigma 1) clipped to
+[16, 4096]. Each step stores one new token per sequence with ``kv_cache_append`` (it rewrites
+the current token's slot, so the batch shape is the same every step) and then runs
+``paged_attn_decode`` (partition kernel + split-K merge). Inputs are resident in HBM before
+timing starts.
+
+Prints ONE JSON line. ``value`` is KV bytes per step (2 * sum(L) * H_kv * d * 2 B, each KV head
+once) divided by the measured step time. ``roofline`` reports the decode partition kernel: the
+same KV bytes divided by that kernel's average duration (hipEvents recorded by the library
+around each launch, on the launch stream), against the 8 TB/s HBM peak. ``cpu_baseline`` times
+the CPU oracle (fp64, one thread) on the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode attention KV GB/s (fraction of HBM peak) and seq-steps/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_mfma_gqa256_b16_traffic.json")
+KERNEL_SOURCES = ["paged_kv_cache_127_amd/csrc/decode_mfma.hip",
+                  "paged_kv_cache_127_amd/csrc/device_common.h"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(block_size: int, partition: int):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
+    current kernel source and the same launch configuration; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    if t.get("block_size") != block_size or t.get("partition") != partition:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(batch, steps: int):
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            oracle.paged_decode(batch.q, batch.k_pool, batch.v_pool, batch.tables, batch.lengths,
+                                batch.block_size)
+        dt = time.perf_counter() - t0
+    per_step = dt / steps
+    return {
+        "value": round(batch.kv_bytes / per_step / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"the full batch ({batch.num_seqs} sequences, sum L = {int(batch.lengths.sum())}), "
+                   f"{steps} decode steps, numpy fp64 with one BLAS thread"),
+        "seq_steps_per_s": round(batch.num_seqs / per_step, 2),
+        "seconds": round(dt, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--block-size", type=int, default=16, choices=(16, 32))
+    ap.add_argument("--partition", type=int, default=0)
+    ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_127_amd as pkv
+    import workloads as W
+
+    dev = "cuda:0"
+    t_gen = time.perf_counter()
+    b = W.config3(args.block_size)
+    S, Hq, Hkv, d = b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim
+    q = b.q.to(dev)
+    k_pool = b.k_pool.to(dev)
+    v_pool = b.v_pool.to(dev)
+    tables = torch.from_numpy(b.tables).to(dev)
+    lens = torch.from_numpy(b.lengths).to(dev)
+    max_ctx = int(b.lengths.max())
+    out = torch.empty(S, Hq, d, dtype=torch.float32, device=dev)
+    ws_bytes = pkv.pkv_decode_workspace_size(S, Hq, Hkv, d, max_ctx, args.partition)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    k_new, v_new = (x.to(dev) for x in W.new_tokens(b.seed, 1, S, Hkv, d, b.dtype))
+    seq_ids = torch.arange(S, dtype=torch.int32, device=dev)
+    positions = (lens - 1).to(torch.int32)
+    partition = args.partition or pkv.pkv_decode_auto_partition(S, Hkv, max_ctx)
+    gen_s = time.perf_counter() - t_gen
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step():
+        pkv.kv_cache_append(k_pool, v_pool, k_new, v_new, seq_ids, positions, tables)
+        pkv.paged_attn_decode(out, q, k_pool, v_pool, tables, lens, max_ctx,
+                              partition_tokens=args.partition, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    pkv.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernel_ms, kernel_n = pkv.timing_query("decode_partial")
+    reduce_ms, reduce_n = pkv.timing_query("splitk_reduce")
+    append_ms, append_n = pkv.timing_query("append")
+    pkv.timing_enable(False)
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kv_bytes = b.kv_bytes
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    kern_avg_ms = kernel_ms / max(kernel_n, 1)
+    achieved = kv_bytes / (kern_avg_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.block_size, partition)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"GQA decode batch: {S} sequences, {Hq} query / {Hkv} KV heads, "
+                         f"head_dim {d}, bf16 cache, block size {args.block_size}, log-normal "
+                         "context lengths (median 512, sigma 1, clipped to [16, 4096]), seeded "
+                         "random block placement in a 1.25x pool; one appended token per "
+                         "sequence per step"),
+            "num_seqs": S,
+            "sum_context_tokens": int(b.lengths.sum()),
+            "block_size": args.block_size,
+            "partition_tokens": partition,
+            "kv_bytes_per_step": kv_bytes,
+        },
+        "seq_steps_per_s": round(S / (ms_per_step * 1e-3), 1),
+        "hbm_fraction_of_step": round(value / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_partial_mfma",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "avg_kernel_us": round(kern_avg_ms * 1e3, 3),
+            "launches": kernel_n,
+        },
+        "other_kernels_avg_us": {
+            "splitk_reduce": round(reduce_ms / max(reduce_n, 1) * 1e3, 3),
+            "append": round(append_ms / max(append_n, 1) * 1e3, 3),
+        },
+        "setup_s": round(gen_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(b, args.cpu_steps)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
