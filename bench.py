@@ -42,7 +42,7 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(block_size: int, partition: int):
+def measured_traffic(block_size: int, workers: int):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
     current kernel source and the same launch configuration; else None."""
     try:
@@ -52,7 +52,7 @@ def measured_traffic(block_size: int, partition: int):
         return None
     if t.get("kernel_source_sha") != kernel_source_sha():
         return None
-    if t.get("block_size") != block_size or t.get("partition") != partition:
+    if t.get("block_size") != block_size or t.get("num_workers") != workers:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -87,7 +87,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--block-size", type=int, default=16, choices=(16, 32))
-    ap.add_argument("--partition", type=int, default=0)
+    ap.add_argument("--workers", type=int, default=0, help="decode wavefronts (0 = automatic)")
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -116,12 +116,11 @@ def main():
     lens = torch.from_numpy(b.lengths).to(dev)
     max_ctx = int(b.lengths.max())
     out = torch.empty(S, Hq, d, dtype=torch.float32, device=dev)
-    ws_bytes = pkv.pkv_decode_workspace_size(S, Hq, Hkv, d, max_ctx, args.partition)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = pkv.pkv_decode_workspace_size(S, Hq, Hkv, d, args.workers)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     k_new, v_new = (x.to(dev) for x in W.new_tokens(b.seed, 1, S, Hkv, d, b.dtype))
     seq_ids = torch.arange(S, dtype=torch.int32, device=dev)
     positions = (lens - 1).to(torch.int32)
-    partition = args.partition or pkv.pkv_decode_auto_partition(S, Hkv, max_ctx)
     gen_s = time.perf_counter() - t_gen
 
     if args.copy_probe_mib > 0:
@@ -136,7 +135,7 @@ def main():
     def step():
         pkv.kv_cache_append(k_pool, v_pool, k_new, v_new, seq_ids, positions, tables)
         pkv.paged_attn_decode(out, q, k_pool, v_pool, tables, lens, max_ctx,
-                              partition_tokens=args.partition, workspace=ws)
+                              num_workers=args.workers, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -159,7 +158,7 @@ def main():
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     kern_avg_ms = kernel_ms / max(kernel_n, 1)
     achieved = kv_bytes / (kern_avg_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.block_size, partition)
+    traffic = measured_traffic(args.block_size, args.workers)
 
     result = {
         "metric": METRIC,
@@ -183,7 +182,7 @@ def main():
             "num_seqs": S,
             "sum_context_tokens": int(b.lengths.sum()),
             "block_size": args.block_size,
-            "partition_tokens": partition,
+            "num_workers": args.workers or "auto",
             "kv_bytes_per_step": kv_bytes,
         },
         "seq_steps_per_s": round(S / (ms_per_step * 1e-3), 1),

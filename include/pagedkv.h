@@ -79,9 +79,12 @@ const char* pkv_last_error(void);
  * for a_t, with V applied) -- the gather is fused, no contiguous copy is made. Keys and values
  * of KV head g serve the G query heads g*G .. g*G+G-1 (grouped-query attention, [P1] "Where
  * contiguous allocation wastes space" notes that GQA stores fewer KV heads).
- * Long contexts are cut into partitions of `partition_tokens` tokens; each partition yields a
- * partial (m, l, acc) and a second kernel merges them with the log-sum-exp rule of
- * [P2] "Paged Attention CUDA Kernel". context_lens[s] == 0 gives a zero row.
+ * Work split: the 32-token steps of all (sequence, KV head) pairs form one line that
+ * `num_workers` wavefronts cut into equal contiguous ranges, so each reads the same number of
+ * K/V bytes whatever the length mix. A pair finished inside one range is written directly; a
+ * pair split across ranges leaves one partial (m, l, acc) per range and a second kernel merges
+ * them with the log-sum-exp rule of [P2] "Paged Attention CUDA Kernel" (exact up to rounding).
+ * context_lens[s] == 0 gives a zero row.
  *
  *   out           device [num_seqs][num_q_heads][head_dim], element type out_dtype
  *                 (PKV_F32, or the same 16-bit type as kv_dtype: round to nearest even)
@@ -90,24 +93,28 @@ const char* pkv_last_error(void);
  *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries past
  *                 ceil(context_lens[s] / block_size) are never read
  *   context_lens  device int32 [num_seqs], each in [0, max_context_len]
- *   max_context_len  host int, an upper bound of context_lens (sizes the launch), at most
+ *   max_context_len  host int, an upper bound of context_lens, at most
  *                 max_blocks_per_seq * block_size
+ *   num_seqs      at most 4096 per call
  *   scale         softmax scale; <= 0 selects 1/sqrt(head_dim)
- *   partition_tokens  0 = automatic, else a positive multiple of 32, at most 64*block_size
- *   workspace     device scratch of at least pkv_decode_workspace_size(...) bytes (may be
- *                 NULL when that size is 0); contents need no initialisation
+ *   num_workers   0 = automatic (8 wavefronts per compute unit of the current device, all
+ *                 resident at once), else 1 .. 2^20 (any count gives the same result up to
+ *                 rounding)
+ *   workspace     device scratch, 256-byte aligned, of at least
+ *                 pkv_decode_workspace_size(...) bytes for the same num_workers; contents need
+ *                 no initialisation. Two decode calls in flight at once need two workspaces.
  * --------------------------------------------------------------------------------------- */
 size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                                 int max_context_len, int partition_tokens);
+                                 int num_workers);
 
-/* The partition length that partition_tokens = 0 selects for these sizes. */
-int pkv_decode_auto_partition(int num_seqs, int num_kv_heads, int max_context_len);
+/* The worker count that num_workers = 0 selects on the current device. */
+int pkv_decode_auto_workers(void);
 
 int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_pool,
                       const void* v_pool, int kv_dtype, const int32_t* block_tables,
                       int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
                       int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                      int block_size, int num_blocks, float scale, int partition_tokens,
+                      int block_size, int num_blocks, float scale, int num_workers,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------

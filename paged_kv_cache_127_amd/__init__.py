@@ -15,7 +15,7 @@ import torch  # loaded first: the library then binds to the HIP runtime torch al
 
 __all__ = [
     "PagedKVError", "paged_attn_decode", "kv_cache_append", "cow_block_copy",
-    "pkv_decode_workspace_size", "pkv_decode_auto_partition", "BlockPool", "timing_enable",
+    "pkv_decode_workspace_size", "pkv_decode_auto_workers", "BlockPool", "timing_enable",
     "timing_query", "set_validate", "library_path", "load_library", "PKV_F32", "PKV_F16", "PKV_BF16",
 ]
 
@@ -49,8 +49,8 @@ def _declare(L):
     sig = {
         "pkv_last_error": (ctypes.c_char_p, []),
         "pkv_version": (ctypes.c_char_p, []),
-        "pkv_decode_workspace_size": (c_size, [c_int] * 6),
-        "pkv_decode_auto_partition": (c_int, [c_int] * 3),
+        "pkv_decode_workspace_size": (c_size, [c_int] * 5),
+        "pkv_decode_auto_workers": (c_int, []),
         "paged_attn_decode": (c_int, [c_void, c_int, c_void, c_void, c_void, c_int, c_void, c_int,
                                       c_void, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                       c_float, c_int, c_void, c_size, c_void]),
@@ -126,21 +126,20 @@ def _kv_dtype(t: torch.Tensor) -> int:
     return _DT[t.dtype]
 
 
-def pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                              partition_tokens=0) -> int:
+def pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                              num_workers=0) -> int:
     return int(load_library().pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads,
-                                                         head_dim, max_context_len,
-                                                         partition_tokens))
+                                                         head_dim, num_workers))
 
 
-def pkv_decode_auto_partition(num_seqs, num_kv_heads, max_context_len) -> int:
-    return int(load_library().pkv_decode_auto_partition(num_seqs, num_kv_heads, max_context_len))
+def pkv_decode_auto_workers() -> int:
+    return int(load_library().pkv_decode_auto_workers())
 
 
 def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
                       v_pool: torch.Tensor, block_tables: torch.Tensor,
                       context_lens: torch.Tensor, max_context_len: int, scale: float = 0.0,
-                      partition_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
+                      num_workers: int = 0, workspace: Optional[torch.Tensor] = None,
                       stream=None) -> torch.Tensor:
     """out[s][h] = softmax(q[s][h] . K_s^T * scale) . V_s over the paged cache (C:
     ``paged_attn_decode``). Shapes: q, out [S][H_q][d]; k_pool [N][H_kv][B][d];
@@ -157,7 +156,7 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
         raise ValueError("block_tables must be [S][max_blocks] and context_lens [S]")
     if out.dtype not in (torch.float32, k_pool.dtype):
         raise TypeError("out must be float32 or the cache dtype")
-    ws_need = pkv_decode_workspace_size(S, Hq, Hkv, d, int(max_context_len), partition_tokens)
+    ws_need = pkv_decode_workspace_size(S, Hq, Hkv, d, num_workers)
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
@@ -166,7 +165,7 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
         _dev(out, "out"), _DT[out.dtype], _dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"),
         _dev(v_pool, "v_pool", k_pool.dtype), kdt, _dev(block_tables, "block_tables", torch.int32),
         int(block_tables.shape[1]), _dev(context_lens, "context_lens", torch.int32),
-        int(max_context_len), S, Hq, Hkv, d, B, N, float(scale), int(partition_tokens), ws_ptr,
+        int(max_context_len), S, Hq, Hkv, d, B, N, float(scale), int(num_workers), ws_ptr,
         ws_bytes, _stream(stream)))
     return out
 

@@ -43,15 +43,17 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, jobs: int = 8, out: str = LIB, defines=(),
+          build_dir: str = BUILD) -> str:
+    os.makedirs(build_dir, exist_ok=True)
     jobs_list = []
+    dflags = [f"-D{d}" for d in defines]
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        jobs_list.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(build_dir, src + ".o")
+        jobs_list.append([HIPCC, *HIP_FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", obj])
     cxx = shutil.which("g++") or "g++"
     for src in CXX_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(build_dir, src + ".o")
         jobs_list.append([cxx, *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         outs = list(ex.map(_run, jobs_list))
@@ -60,10 +62,10 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             if o.strip():
                 print(o)
     objs = [c[c.index("-o") + 1] for c in jobs_list]
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -12,6 +12,7 @@
 
 #include "kernels.h"
 #include "pagedkv.h"
+#include "schedule.h"
 
 namespace {
 
@@ -103,9 +104,38 @@ bool copy_ints(std::vector<int32_t>& dst, const int32_t* src, size_t n, hipStrea
   return hipStreamSynchronize(st) == hipSuccess;
 }
 
-int choose_partition(int partition_tokens, int num_seqs, int num_kv_heads, int max_ctx) {
-  return partition_tokens > 0 ? partition_tokens
-                              : pkv_decode_auto_partition(num_seqs, num_kv_heads, max_ctx);
+constexpr int kWorkersPerCU = 8;   // two resident wavefronts per SIMD, four SIMDs per CU
+
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev] = v;
+  return v;
+}
+
+int choose_workers(int num_workers) {
+  return num_workers > 0 ? num_workers : pkv_decode_auto_workers();
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t acc, m, l, prefix, total;
+};
+
+WsLayout ws_layout(int num_seqs, int G, int head_dim, int n) {
+  WsLayout L;
+  const size_t slots = 2 * (size_t)n * G;
+  L.acc = 0;
+  L.m = align256(slots * head_dim * sizeof(float));
+  L.l = L.m + align256(slots * sizeof(float));
+  L.prefix = L.l + align256(slots * sizeof(float));
+  L.total = L.prefix + align256(((size_t)num_seqs + 1) * sizeof(int64_t));
+  return L;
 }
 
 }  // namespace
@@ -116,28 +146,25 @@ const char* pkv_last_error(void) { return g_err.c_str(); }
 
 const char* pkv_version(void) { return "pagedkv-gfx950 0.1"; }
 
-int pkv_decode_auto_partition(int num_seqs, int num_kv_heads, int max_context_len) {
-  (void)num_seqs;
-  (void)num_kv_heads;
-  (void)max_context_len;
-  return 512;
+int pkv_decode_auto_workers(void) {
+  const int cus = cu_count();
+  return cus > 0 ? cus * kWorkersPerCU : 256 * kWorkersPerCU;
 }
 
 size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                                 int max_context_len, int partition_tokens) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
-  const int P = choose_partition(partition_tokens, num_seqs, num_kv_heads, max_context_len);
-  if (P <= 0) return 0;
-  const size_t n_part = (size_t)((max_context_len + P - 1) / P);
-  if (n_part <= 1) return 0;
-  return (size_t)num_seqs * num_q_heads * n_part * ((size_t)head_dim + 2) * sizeof(float);
+                                 int num_workers) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_q_heads % num_kv_heads != 0 || num_workers < 0)
+    return 0;
+  return ws_layout(num_seqs, num_q_heads / num_kv_heads, head_dim, choose_workers(num_workers))
+      .total;
 }
 
 int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_pool,
                       const void* v_pool, int kv_dtype, const int32_t* block_tables,
                       int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
                       int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                      int block_size, int num_blocks, float scale, int partition_tokens,
+                      int block_size, int num_blocks, float scale, int num_workers,
                       void* workspace, size_t workspace_bytes, void* stream) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
       num_blocks <= 0 || max_context_len < 0)
@@ -171,19 +198,36 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
     return fail(PKV_ERR_INVALID_ARG,
                 "paged_attn_decode: max_context_len %d exceeds table capacity %d x %d",
                 max_context_len, max_blocks_per_seq, block_size);
-  const int P = choose_partition(partition_tokens, num_seqs, num_kv_heads, max_context_len);
-  if (P <= 0 || P % 32 != 0 || P > 64 * block_size)
-    return fail(PKV_ERR_UNSUPPORTED,
-                "paged_attn_decode: partition_tokens %d (a multiple of 32, at most 64 * block_size)",
-                P);
-  const int n_part_max = max_context_len > 0 ? (max_context_len + P - 1) / P : 1;
-  const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                max_context_len, P);
-  if (need > 0 && (!workspace || workspace_bytes < need))
+  if (num_seqs > pkv::kMaxSeqsPerCall)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: %d sequences (at most %d per call)",
+                num_seqs, pkv::kMaxSeqsPerCall);
+  if (num_workers < 0 || num_workers > (1 << 20))
+    return fail(PKV_ERR_INVALID_ARG, "paged_attn_decode: num_workers %d", num_workers);
+  const int waves_env = env_int("PAGEDKV_DECODE_WAVES", 4);
+  const int waves = (waves_env == 1 || waves_env == 2 || waves_env == 4) ? waves_env : 4;
+  int n = num_workers;
+  if (n == 0) {
+    // every worker resident at once: the resident wavefronts per CU of the chosen kernel,
+    // capped by the per-CU count the automatic workspace size assumes
+    int per_cu = use_mfma ? pkv::decode_mfma_resident_waves(kv_dtype, head_dim, block_size,
+                                                            waves, num_seqs)
+                          : pkv::decode_valu_resident_waves(kv_dtype, head_dim, block_size, G,
+                                                            waves, num_seqs);
+    if (per_cu <= 0 || per_cu > kWorkersPerCU) per_cu = kWorkersPerCU;
+    const int cus = cu_count();
+    n = (cus > 0 ? cus : 256) * per_cu;
+  }
+  {
+    // the step line must fit the 64-bit worker arithmetic: N * n < 2^62
+    const double steps_max = (double)num_kv_heads * num_seqs *
+                             ((double)max_blocks_per_seq * block_size / 32.0 + 1.0);
+    if (steps_max * (double)n >= 4.0e18)
+      return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: problem too large for one call");
+  }
+  const WsLayout wl = ws_layout(num_seqs, G, head_dim, n);
+  if (!workspace || workspace_bytes < wl.total)
     return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "paged_attn_decode: workspace %zu < %zu bytes",
-                workspace_bytes, need);
-  if ((int64_t)num_kv_heads * num_seqs * n_part_max > 0x7fffffffLL)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: grid too large");
+                workspace_bytes, wl.total);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
   if (validate_mode()) {
@@ -219,19 +263,14 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
   p.num_kv_heads = num_kv_heads;
   p.num_blocks = num_blocks;
   p.block_size = block_size;
-  p.partition = P;
-  p.n_part_max = n_part_max;
+  p.num_workers = n;
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim);
   p.scale_log2 = sc * 1.4426950408889634f;
-  if (need > 0) {
-    const size_t rows = (size_t)num_seqs * num_q_heads * n_part_max;
-    float* ws = reinterpret_cast<float*>(workspace);
-    p.ws_acc = ws;
-    p.ws_m = ws + rows * head_dim;
-    p.ws_l = p.ws_m + rows;
-  }
-  static const int waves_env = env_int("PAGEDKV_DECODE_WAVES", 4);
-  const int waves = (waves_env == 1 || waves_env == 2 || waves_env == 4) ? waves_env : 4;
+  char* ws = reinterpret_cast<char*>(workspace);
+  p.ws_acc = reinterpret_cast<float*>(ws + wl.acc);
+  p.ws_m = reinterpret_cast<float*>(ws + wl.m);
+  p.ws_l = reinterpret_cast<float*>(ws + wl.l);
+  p.prefix = reinterpret_cast<int64_t*>(ws + wl.prefix);
 
   hipError_t e;
   if (use_mfma) {
@@ -244,11 +283,9 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
     });
   }
   if (e != hipSuccess) return launch_error(e, "paged_attn_decode: decode kernel");
-  if (n_part_max > 1) {
-    e = timed("splitk_reduce", st,
-              [&] { return pkv::launch_splitk_reduce(p, kv_dtype, head_dim, st); });
-    if (e != hipSuccess) return launch_error(e, "paged_attn_decode: reduce kernel");
-  }
+  e = timed("splitk_reduce", st,
+            [&] { return pkv::launch_splitk_reduce(p, kv_dtype, head_dim, st); });
+  if (e != hipSuccess) return launch_error(e, "paged_attn_decode: merge kernel");
   return ok();
 }
 

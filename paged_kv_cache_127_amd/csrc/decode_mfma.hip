@@ -1,17 +1,12 @@
 // Grouped-query paged decode attention on CDNA4 matrix cores (16-bit caches, G = 2..16).
 //
 // What it computes ("Paged Attention and vLLM", sections "Block Table and Logical-to-
-// Physical Mapping" and "Paged Attention CUDA Kernel"): for one sequence s, one KV head g and
-// one partition of the context, the partial softmax state (m, l, acc) of the G query heads
-// g*G .. g*G+G-1 over the partition's tokens, with keys and values read straight from the
-// physical blocks named by the block table (no contiguous copy). A single-partition sequence
-// writes its normalised output directly; otherwise the split-K reduce kernel merges the
-// partials with the log-sum-exp rule.
-//
-// Work decomposition. One workgroup = one (sequence, KV head, partition); W wavefronts share
-// the partition's 32-token steps round-robin. The workgroup id is decoded KV-head-fastest, so
-// with 8 KV heads every head stays on one XCD (consecutive ids go to consecutive XCDs): the L2
-// of that XCD sees all reads of that head's blocks, which helps shared-prefix blocks.
+// Physical Mapping" and "Paged Attention CUDA Kernel"): for every piece of a (sequence, KV
+// head) segment in this wavefront's range of the balanced step line (schedule.h), the
+// softmax state (m, l, acc) of the G query heads g*G .. g*G+G-1 over the piece's tokens, with
+// keys and values read straight from the physical blocks named by the block table (no
+// contiguous copy). Whole segments are normalised and written to the output; split pieces
+// write partial states that the merge kernel combines.
 //
 // Per 32-token step a wavefront issues (per lane) 8 + 8 16-byte loads:
 //   K operand, sub-tile a (0/1), d-chunk c: key row tau(a, i) = 8*(i/4) + 4a + i%4 of the
@@ -25,8 +20,10 @@
 // Probabilities are split into a 16-bit high part and a 16-bit remainder (two MFMAs), which
 // keeps P.V at close to fp32 accuracy. Scores and the online softmax stay in fp32; the scale
 // (times log2 e) is applied to the fp32 scores and exp2 is used throughout.
+// The next step's loads (with the next piece's query rows) are in flight while a step computes.
 #include "device_common.h"
 #include "kernels.h"
+#include "schedule.h"
 
 namespace pkv {
 
@@ -45,6 +42,7 @@ template <int D>
 struct StepRegs {
   u32x4 k[2][D / 32];   // K operand per sub-tile and d-chunk
   u32x4 v[D / 16];      // V operand per d-chunk
+  u32x4 q[D / 32];      // Q operand, loaded only for the first step of a piece
 };
 
 // Split two fp32 probabilities into packed 16-bit high parts and remainders.
@@ -56,109 +54,150 @@ __device__ __forceinline__ void split_pair(float p0, float p1, uint32_t& hi, uin
   lo = (uint32_t)Elem<T>::from_f32(r0) | ((uint32_t)Elem<T>::from_f32(r1) << 16);
 }
 
+#ifndef PKV_MFMA_WAVES_PER_EU
+#define PKV_MFMA_WAVES_PER_EU 1
+#endif
+
+// At least PKV_MFMA_WAVES_PER_EU resident wavefronts per SIMD: the compiler keeps the whole
+// state (two steps of K/V/Q operands, accumulators) within that register budget.
 template <typename T, int D, int B, int W>
-__global__ __launch_bounds__(64 * W) void decode_partial_mfma(DecodeParams p) {
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES_PER_EU)))
+void decode_mfma(DecodeParams p) {
   static_assert(B == 16 || B == 32, "block size");
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int NC = D / 32;   // QK MFMAs per sub-tile
   constexpr int NF = D / 16;   // PV MFMA output chunks
   constexpr int ES = 2;        // element bytes
 
+  extern __shared__ int64_t smem[];
+  const int S = p.num_seqs;
+  int64_t* sm_prefix = smem;
+  int64_t* sm_wave = smem + S + 1;
+  int32_t* sm_len = reinterpret_cast<int32_t*>(smem + S + 1 + 16);
+  const int cap = p.max_blocks * B;
+  stage_lengths(p.lens, S, cap, sm_len);
+  build_step_prefix(p.lens, S, cap, sm_prefix, sm_wave);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= S; i += blockDim.x) p.prefix[i] = sm_prefix[i];
+
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int jg = lane >> 4;
-
-  int wg = blockIdx.x;
   const int Hkv = p.num_kv_heads;
-  const int g = wg % Hkv;
-  wg /= Hkv;
-  const int s = wg % p.num_seqs;
-  const int part = wg / p.num_seqs;
   const int G = p.num_q_heads / Hkv;
-
-  // lengths beyond the table or the launch are clamped: never read past either
-  const int cap = min(p.max_blocks * B, p.n_part_max * p.partition);
-  int L = p.lens[s];
-  L = L < 0 ? 0 : (L > cap ? cap : L);
-  const int n_part = L > 0 ? ceil_div(L, p.partition) : 1;
-  if (part >= n_part) return;   // uniform for the whole workgroup
-  const int t0 = part * p.partition;
-  const int t1 = min(t0 + p.partition, L);
-  const int n_steps = t1 > t0 ? ceil_div(t1 - t0, 32) : 0;
-
-  // Query operand: Q^T[d][head], lane holds head r16, d-slice [32c + 8jg, +8) of chunk c.
-  u32x4 qv[NC];
-  {
-    const char* qp = reinterpret_cast<const char*>(p.q) +
-                     (((size_t)s * p.num_q_heads + (size_t)g * G + r16) * D + 8 * jg) * ES;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      qv[c] = r16 < G ? load16(qp + 32 * c * ES) : u32x4{0, 0, 0, 0};
-  }
-
-  // This partition's block-table entries (<= 64), one per lane.
-  const int jb0 = t0 / B;
-  const int nbp = t1 > t0 ? ceil_div(t1 - t0, B) : 0;
-  int tbl = 0;
-  bool bad = false;
-  if (lane < nbp) {
-    tbl = p.tables[(size_t)s * p.max_blocks + jb0 + lane];
-    bad = (unsigned)tbl >= (unsigned)p.num_blocks;
-    if (bad) tbl = 0;
-  }
-  const bool poisoned = __builtin_amdgcn_ballot_w64(bad) != 0;
+  const int n = p.num_workers;
+  const int w = blockIdx.x * W + wave;
+  if (w >= n) return;
+  const int64_t N = (int64_t)Hkv * sm_prefix[S];
+  const int64_t R0 = range_begin(N, n, w);
+  const int nsteps = (int)(range_begin(N, n, w + 1) - R0);
+  if (nsteps <= 0) return;
+  const int64_t R1 = R0 + nsteps;
 
   const char* kbase = reinterpret_cast<const char*>(p.k_pool);
   const char* vbase = reinterpret_cast<const char*>(p.v_pool);
+  const char* qbase = reinterpret_cast<const char*>(p.q);
   const size_t kv_block_stride = (size_t)B * D * ES;   // bytes per (block, head)
+  const int tokA0 = 8 * (r16 >> 2) + (r16 & 3);        // sub-tile 0 key row (sub-tile 1: +4)
+  const int vtok = 8 * jg;                             // first of this lane's 8 value tokens
+  // per-lane byte offsets inside a (block, head) tile
+  const int kofs0 = ((tokA0 & (B - 1)) * D + 8 * jg) * ES;
+  const int kofs1 = (((tokA0 + 4) & (B - 1)) * D + 8 * jg) * ES;
+  const int vofs = (r16 * B + (vtok & (B - 1))) * ES;
 
-  // Fixed per-lane parts of the addresses.
-  const int tokA0 = 8 * (r16 >> 2) + (r16 & 3);      // sub-tile 0 token (sub-tile 1: +4)
-  const size_t k_lane_off = (size_t)(8 * jg) * ES;
-  const int vtok = 8 * jg;                           // first of this lane's 8 value tokens
+  // block ids of the current and the next 32-step chunk; the walk itself is a scalar cursor
+  int cur_chunk = 0;
+  int tcur = chunk_blocks<B>(sm_prefix, sm_len, p.tables, S, Hkv, p.max_blocks, p.num_blocks,
+                             R0, R1, lane);
+  int tnext = chunk_blocks<B>(sm_prefix, sm_len, p.tables, S, Hkv, p.max_blocks, p.num_blocks,
+                              R0 + 32, R1, lane);
+  Cursor cur = cursor_at(sm_prefix, sm_len, S, Hkv, R0);   // next step to load
 
-  auto load_step = [&](StepRegs<D>& r, int step) {
-    const int rel = (step * 32) / B;                 // partition-relative block of the step
-    int b0 = __builtin_amdgcn_readlane(tbl, rel);
-    int b1 = b0;
-    if constexpr (B == 16) {
-      if (t0 + step * 32 + 16 < t1) b1 = __builtin_amdgcn_readlane(tbl, rel + 1);
-    }
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int tok = tokA0 + 4 * a;
-      const int blk = (B == 16 && tok >= 16) ? b1 : b0;
-      const int off = tok & (B - 1);
-      const char* kp = kbase + ((size_t)blk * Hkv + g) * kv_block_stride +
-                       (size_t)off * D * ES + k_lane_off;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) r.k[a][c] = load16(kp + 32 * c * ES);
-    }
-    {
-      const int blk = (B == 16 && vtok >= 16) ? b1 : b0;
-      const int off = vtok & (B - 1);
-      const char* vp = vbase + ((size_t)blk * Hkv + g) * kv_block_stride +
-                       ((size_t)r16 * B + off) * ES;
-#pragma unroll
-      for (int f = 0; f < NF; ++f) r.v[f] = load16(vp + (size_t)16 * f * B * ES);
-    }
-  };
-
+  u32x4 qcur[NC];
   float m_run = kNegInf, l_run = 0.f;
+  bool poison = false;
+  int piece_first = 0, piece_k0 = 0;
   f32x4 oacc[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) oacc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute_step = [&](StepRegs<D>& r, int step) {
-    const int tb = t0 + step * 32;
-    const int nvalid = t1 - tb;                      // valid tokens in this step (>= 1)
+  // Loads of step i (the cursor's position); returns the step's description.
+  auto load_step = [&](StepRegs<D>& r, int i) {
+    StepInfo si;
+    si.s = cur.s;
+    si.g = cur.g;
+    si.k = cur.k;
+    si.ns = cur.ns;
+    si.L = cur.L;
+    // read the next chunk's block ids only when the step is in it: a select would make every
+    // step wait for that chunk's table load
+    if ((i >> 5) == cur_chunk) {
+      si.b0 = __builtin_amdgcn_readlane(tcur, i & 31);
+      si.b1 = B == 16 ? __builtin_amdgcn_readlane(tcur, (i & 31) + 32) : si.b0;
+    } else {
+      si.b0 = __builtin_amdgcn_readlane(tnext, i & 31);
+      si.b1 = B == 16 ? __builtin_amdgcn_readlane(tnext, (i & 31) + 32) : si.b0;
+    }
+    if (i == 0 || si.k == 0) {   // first step of a piece: its query rows
+      const char* qp = qbase + (((size_t)si.s * p.num_q_heads + (size_t)si.g * G + r16) * D +
+                                8 * jg) * ES;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        r.q[c] = r16 < G ? load16(qp + 32 * c * ES) : u32x4{0, 0, 0, 0};
+    }
+    const int b0 = si.b0 < 0 ? 0 : si.b0;     // out-of-range entries read block 0, then poison
+    const int b1 = si.b1 < 0 ? 0 : si.b1;
+    const char* t0 = kbase + ((size_t)b0 * Hkv + si.g) * kv_block_stride;
+    const char* t1 = kbase + ((size_t)b1 * Hkv + si.g) * kv_block_stride;
+    const char* ka = (B == 16 && tokA0 >= 16) ? t1 : t0;
+    const char* kb = (B == 16 && tokA0 + 4 >= 16) ? t1 : t0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      r.k[0][c] = load16(ka + kofs0 + 32 * c * ES);
+      r.k[1][c] = load16(kb + kofs1 + 32 * c * ES);
+    }
+    const char* vt = vbase + ((size_t)((B == 16 && vtok >= 16) ? b1 : b0) * Hkv + si.g) *
+                                 kv_block_stride + vofs;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) r.v[f] = load16(vt + (size_t)16 * f * B * ES);
+    return si;
+  };
+
+  // Start of step i: move the block window, and open a new piece.
+  auto begin_step = [&](const StepInfo& si, int i) {
+    if ((i >> 5) != cur_chunk) {
+      cur_chunk = i >> 5;
+      tcur = tnext;
+      tnext = chunk_blocks<B>(sm_prefix, sm_len, p.tables, S, Hkv, p.max_blocks, p.num_blocks,
+                              R0 + 32 * (int64_t)(cur_chunk + 1), R1, lane);
+    }
+    if (i == 0 || si.k == 0) {
+      m_run = kNegInf;
+      l_run = 0.f;
+      poison = false;
+      piece_first = i;
+      piece_k0 = si.k;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) oacc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  auto compute_step = [&](StepRegs<D>& r, const StepInfo& si, int i) {
+    // a new piece takes its query rows here, after the next step's loads were issued, so the
+    // wait for them never drains the load pipeline
+    if (i == 0 || si.k == 0) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qcur[c] = r.q[c];
+    }
+    const int nvalid = si.L - 32 * si.k;             // valid tokens in this step (>= 1)
+    poison = poison || si.b0 < 0 || (B == 16 && nvalid > 16 && si.b1 < 0);
     f32x4 sacc[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       sacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) sacc[a] = mfma16x16x32<T>(r.k[a][c], qv[c], sacc[a]);
+      for (int c = 0; c < NC; ++c) sacc[a] = mfma16x16x32<T>(r.k[a][c], qcur[c], sacc[a]);
     }
     float z[8];
 #pragma unroll
@@ -170,16 +209,16 @@ __global__ __launch_bounds__(64 * W) void decode_partial_mfma(DecodeParams p) {
       }
     float mx = z[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
+    for (int t = 1; t < 8; ++t) mx = fmaxf(mx, z[t]);
     mx = cross_max<16>(mx);
     const float m_new = fmaxf(m_run, mx);
     const float alpha = fast_exp2(m_run - m_new);
     float pr[8];
     float ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pr[i] = fast_exp2(z[i] - m_new);
-      ps += pr[i];
+    for (int t = 0; t < 8; ++t) {
+      pr[t] = fast_exp2(z[t] - m_new);
+      ps += pr[t];
     }
     l_run = l_run * alpha + ps;
     m_run = m_new;
@@ -188,19 +227,19 @@ __global__ __launch_bounds__(64 * W) void decode_partial_mfma(DecodeParams p) {
 
     u32x4 phi, plo;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int u = 0; u < 4; ++u) {
       uint32_t h, l;
-      split_pair<T>(pr[2 * w], pr[2 * w + 1], h, l);
-      phi[w] = h;
-      plo[w] = l;
+      split_pair<T>(pr[2 * u], pr[2 * u + 1], h, l);
+      phi[u] = h;
+      plo[u] = l;
     }
     if (nvalid < 32) {
       // zero the value entries of slots past the context (they may hold anything)
       const int nv = nvalid - vtok;
       u32x4 msk;
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        msk[w] = (2 * w < nv ? 0xffffu : 0u) | (2 * w + 1 < nv ? 0xffff0000u : 0u);
+      for (int u = 0; u < 4; ++u)
+        msk[u] = (2 * u < nv ? 0xffffu : 0u) | (2 * u + 1 < nv ? 0xffff0000u : 0u);
 #pragma unroll
       for (int f = 0; f < NF; ++f) r.v[f] &= msk;
     }
@@ -209,118 +248,112 @@ __global__ __launch_bounds__(64 * W) void decode_partial_mfma(DecodeParams p) {
       oacc[f] = mfma16x16x32<T>(r.v[f], phi, oacc[f]);
       oacc[f] = mfma16x16x32<T>(r.v[f], plo, oacc[f]);
     }
+
+    // end of a piece: write the output (whole segment) or a partial state
+    if (si.k == si.ns - 1 || i == nsteps - 1) {
+      float l_tot = cross_sum<16>(l_run);
+      if (poison) l_tot = __builtin_nanf("");
+      const bool whole = piece_k0 == 0 && si.k == si.ns - 1;
+      if (r16 < G) {
+        const int h = si.g * G + r16;
+        if (whole) {
+          const size_t row = (size_t)si.s * p.num_q_heads + h;
+          const float inv = l_tot == 0.f ? 0.f : 1.0f / l_tot;
+#pragma unroll
+          for (int f = 0; f < NF; ++f) {
+            const f32x4 o = oacc[f] * inv;
+            const int d0 = 16 * f + 4 * jg;
+            if (p.out_f32) {
+              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + row * D + d0) = o;
+            } else {
+              uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + row * D + d0;
+              const uint32_t w0 = (uint32_t)Elem<T>::from_f32(o[0]) |
+                                  ((uint32_t)Elem<T>::from_f32(o[1]) << 16);
+              const uint32_t w1 = (uint32_t)Elem<T>::from_f32(o[2]) |
+                                  ((uint32_t)Elem<T>::from_f32(o[3]) << 16);
+              *reinterpret_cast<uint2*>(op) = make_uint2(w0, w1);
+            }
+          }
+        } else {
+          const size_t slot = 2 * (size_t)w + (piece_first != 0 ? 1 : 0);
+          const size_t pr_idx = slot * G + r16;
+          if (jg == 0) {
+            p.ws_m[pr_idx] = m_run;
+            p.ws_l[pr_idx] = l_tot;
+          }
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+            *reinterpret_cast<f32x4*>(p.ws_acc + pr_idx * D + 16 * f + 4 * jg) = oacc[f];
+        }
+      }
+    }
   };
 
-  // Software pipeline: the next step's loads are in flight while the current one computes.
-  // Past the last step the "next" load repeats the current step's addresses (cache hits),
-  // which keeps every load unconditional.
-  {
-    StepRegs<D> R0, R1;
-    int st = wave;
-    if (st < n_steps) {
-      load_step(R0, st);
-      while (true) {
-        int nx = st + W < n_steps ? st + W : st;
-        load_step(R1, nx);
-        compute_step(R0, st);
-        st += W;
-        if (st >= n_steps) break;
-        nx = st + W < n_steps ? st + W : st;
-        load_step(R0, nx);
-        compute_step(R1, st);
-        st += W;
-        if (st >= n_steps) break;
-      }
+  // Software pipeline: the next step's loads (and the next piece's query rows) are in flight
+  // while the current step computes. Past the last step the lookahead load repeats the last
+  // step's addresses (cache hits), which keeps every load unconditional.
+  StepRegs<D> BA, BB;
+  StepInfo sa = load_step(BA, 0), sb;
+  int i = 0;
+  while (true) {
+    begin_step(sa, i);
+    if (i + 1 < nsteps) {
+      cursor_next(cur, sm_prefix, sm_len, Hkv);
+      sb = load_step(BB, i + 1);
+    } else {
+      load_step(BB, i);
     }
-  }
-
-  // l over the four lane groups that hold the same head
-  l_run = cross_sum<16>(l_run);
-  if (poisoned) {
-    l_run = __builtin_nanf("");
-  }
-
-  // ---- merge the W wavefronts of this workgroup (wave 0 keeps the result) --------------
-  constexpr int DP = D + 4;   // padded row: spreads heads over LDS banks
-  __shared__ float sm_m[W][16];
-  __shared__ float sm_l[W][16];
-  __shared__ float sm_acc[W > 1 ? W - 1 : 1][16][DP];
-  if constexpr (W > 1) {
-    if (wave > 0) {
-      if (jg == 0) {
-        sm_m[wave][r16] = m_run;
-        sm_l[wave][r16] = l_run;
-      }
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-        *reinterpret_cast<f32x4*>(&sm_acc[wave - 1][r16][16 * f + 4 * jg]) = oacc[f];
+    compute_step(BA, sa, i);
+    if (++i >= nsteps) break;
+    begin_step(sb, i);
+    if (i + 1 < nsteps) {
+      cursor_next(cur, sm_prefix, sm_len, Hkv);
+      sa = load_step(BA, i + 1);
+    } else {
+      load_step(BA, i);
     }
-    __syncthreads();
-    if (wave > 0) return;
-    float mw[W];
-    mw[0] = m_run;
-    float m_star = m_run;
-#pragma unroll
-    for (int w = 1; w < W; ++w) {
-      mw[w] = sm_m[w][r16];
-      m_star = fmaxf(m_star, mw[w]);
-    }
-    const bool empty = m_star == kNegInf;
-    float c0 = empty ? 0.f : fast_exp2(m_run - m_star);
-    l_run *= c0;
-#pragma unroll
-    for (int f = 0; f < NF; ++f) oacc[f] *= c0;
-#pragma unroll
-    for (int w = 1; w < W; ++w) {
-      const float cw = empty ? 0.f : fast_exp2(mw[w] - m_star);
-      l_run += cw * sm_l[w][r16];
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-        oacc[f] += cw * *reinterpret_cast<const f32x4*>(&sm_acc[w - 1][r16][16 * f + 4 * jg]);
-    }
-    m_run = m_star;
-  }
-
-  if (r16 >= G) return;
-  const int h = g * G + r16;
-  const size_t row = (size_t)s * p.num_q_heads + h;
-  if (n_part == 1) {
-    const float inv_ok = l_run;
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      f32x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = inv_ok == 0.f ? 0.f : oacc[f][e] / inv_ok;
-      const int d0 = 16 * f + 4 * jg;
-      if (p.out_f32) {
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + row * D + d0) = o;
-      } else {
-        uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + row * D + d0;
-        uint32_t w0 = (uint32_t)Elem<T>::from_f32(o[0]) | ((uint32_t)Elem<T>::from_f32(o[1]) << 16);
-        uint32_t w1 = (uint32_t)Elem<T>::from_f32(o[2]) | ((uint32_t)Elem<T>::from_f32(o[3]) << 16);
-        *reinterpret_cast<uint2*>(op) = make_uint2(w0, w1);
-      }
-    }
-  } else {
-    const size_t pr = row * p.n_part_max + part;
-    if (jg == 0) {
-      p.ws_m[pr] = m_run;
-      p.ws_l[pr] = l_run;
-    }
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-      *reinterpret_cast<f32x4*>(p.ws_acc + pr * D + 16 * f + 4 * jg) = oacc[f];
+    compute_step(BB, sb, i);
+    if (++i >= nsteps) break;
   }
 }
 
 template <typename T, int D, int B>
-static hipError_t launch_t(const DecodeParams& p, int waves, hipStream_t st) {
-  const int64_t grid = (int64_t)p.num_kv_heads * p.num_seqs * p.n_part_max;
-  if (grid <= 0) return hipSuccess;
+static int resident_t(int waves, size_t lds) {
+  int blocks = 0;
+  hipError_t e = hipErrorInvalidValue;
   switch (waves) {
-    case 1: hipLaunchKernelGGL((decode_partial_mfma<T, D, B, 1>), dim3((unsigned)grid), dim3(64), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((decode_partial_mfma<T, D, B, 2>), dim3((unsigned)grid), dim3(128), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((decode_partial_mfma<T, D, B, 4>), dim3((unsigned)grid), dim3(256), 0, st, p); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_mfma<T, D, B, 1>, 64, lds); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_mfma<T, D, B, 2>, 128, lds); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_mfma<T, D, B, 4>, 256, lds); break;
+    default: break;
+  }
+  return e == hipSuccess ? blocks * waves : 0;
+}
+
+int decode_mfma_resident_waves(int kv_dtype, int head_dim, int block_size, int waves,
+                               int num_seqs) {
+  const size_t lds = decode_lds_bytes(num_seqs);
+  const bool bf = kv_dtype == 2;
+#define PKV_CASE(D, B)                                                                   \
+  if (head_dim == D && block_size == B)                                                  \
+    return bf ? resident_t<bf16_t, D, B>(waves, lds) : resident_t<f16_t, D, B>(waves, lds);
+  PKV_CASE(64, 16)
+  PKV_CASE(64, 32)
+  PKV_CASE(128, 16)
+  PKV_CASE(128, 32)
+#undef PKV_CASE
+  return 0;
+}
+
+template <typename T, int D, int B>
+static hipError_t launch_t(const DecodeParams& p, int waves, hipStream_t st) {
+  const int grid = (p.num_workers + waves - 1) / waves;
+  if (grid <= 0) return hipSuccess;
+  const size_t lds = decode_lds_bytes(p.num_seqs);
+  switch (waves) {
+    case 1: hipLaunchKernelGGL((decode_mfma<T, D, B, 1>), dim3(grid), dim3(64), lds, st, p); break;
+    case 2: hipLaunchKernelGGL((decode_mfma<T, D, B, 2>), dim3(grid), dim3(128), lds, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_mfma<T, D, B, 4>), dim3(grid), dim3(256), lds, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -2,9 +2,9 @@
 // eight query heads per KV head. Used for multi-head caches (G = 1), where a matrix-core tile
 // would be 1/16 full, and for fp32 caches.
 //
-// Same contract and work decomposition as the matrix-core kernel (one workgroup per
-// (sequence, KV head, partition); W wavefronts share the partition's 32-token steps), same
-// partial-state output ("Paged Attention and vLLM", section "Paged Attention CUDA Kernel").
+// Same contract and balanced step schedule as the matrix-core kernel (schedule.h), same
+// output: normalised rows for whole segments, partial states (m, l, acc) for split pieces
+// ("Paged Attention and vLLM", section "Paged Attention CUDA Kernel").
 //
 // Scores. A key row of d elements is LPR = d*esize/16 sixteen-byte chunks; lane l covers
 // chunk l%LPR of row l/LPR, so one load instruction reads TPI = 64/LPR whole rows and a step
@@ -16,11 +16,12 @@
 // four tokens) and each lane accumulates its own output rows -- no cross-lane reduction.
 #include "device_common.h"
 #include "kernels.h"
+#include "schedule.h"
 
 namespace pkv {
 
 template <typename T, int D, int B, int G, int W>
-__global__ __launch_bounds__(64 * W) void decode_partial_valu(DecodeParams p) {
+__global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
   constexpr int ES = Elem<T>::kBytes;
   constexpr int EPC = 16 / ES;        // elements per 16-byte chunk
   constexpr int LPR = D / EPC;        // lanes per key row
@@ -31,90 +32,63 @@ __global__ __launch_bounds__(64 * W) void decode_partial_valu(DecodeParams p) {
   constexpr int VCH = B * ES / 16;    // 16-byte chunks in one value row of a block
   constexpr int VE = 16 / ES;         // elements per value chunk
 
+  extern __shared__ int64_t smem[];
+  const int S = p.num_seqs;
+  int64_t* sm_prefix = smem;
+  int64_t* sm_wave = smem + S + 1;
+  const int cap = p.max_blocks * B;
+  build_step_prefix(p.lens, S, cap, sm_prefix, sm_wave);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= S; i += blockDim.x) p.prefix[i] = sm_prefix[i];
+
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int row = lane / LPR;
   const int ch = lane % LPR;
-
-  int wg = blockIdx.x;
   const int Hkv = p.num_kv_heads;
-  const int g = wg % Hkv;
-  wg /= Hkv;
-  const int s = wg % p.num_seqs;
-  const int part = wg / p.num_seqs;
-
-  // lengths beyond the table or the launch are clamped: never read past either
-  const int cap = min(p.max_blocks * B, p.n_part_max * p.partition);
-  int L = p.lens[s];
-  L = L < 0 ? 0 : (L > cap ? cap : L);
-  const int n_part = L > 0 ? ceil_div(L, p.partition) : 1;
-  if (part >= n_part) return;
-  const int t0 = part * p.partition;
-  const int t1 = min(t0 + p.partition, L);
-  const int n_steps = t1 > t0 ? ceil_div(t1 - t0, 32) : 0;
-
-  // this lane's slice of the G query rows, widened to fp32
-  float qf[G][EPC];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const char* qp = reinterpret_cast<const char*>(p.q) +
-                     (((size_t)s * p.num_q_heads + (size_t)g * G + h) * D + (size_t)ch * EPC) * ES;
-    u32x4 w = load16(qp);
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      if constexpr (ES == 4) qf[h][e] = __uint_as_float(w[e]);
-      else qf[h][e] = (e & 1) ? hi16<T>(w[e >> 1]) : lo16<T>(w[e >> 1]);
-    }
-  }
-
-  const int jb0 = t0 / B;
-  const int nbp = t1 > t0 ? ceil_div(t1 - t0, B) : 0;
-  int tbl = 0;
-  bool bad = false;
-  if (lane < nbp) {
-    tbl = p.tables[(size_t)s * p.max_blocks + jb0 + lane];
-    bad = (unsigned)tbl >= (unsigned)p.num_blocks;
-    if (bad) tbl = 0;
-  }
-  const bool poisoned = __builtin_amdgcn_ballot_w64(bad) != 0;
+  const int n = p.num_workers;
+  const int w = blockIdx.x * W + wave;
+  if (w >= n) return;
+  const int64_t N = (int64_t)Hkv * sm_prefix[S];
+  const int64_t R0 = range_begin(N, n, w);
+  const int nsteps = (int)(range_begin(N, n, w + 1) - R0);
+  if (nsteps <= 0) return;
+  const int64_t R1 = R0 + nsteps;
 
   const char* kbase = reinterpret_cast<const char*>(p.k_pool);
   const char* vbase = reinterpret_cast<const char*>(p.v_pool);
+  const char* qbase = reinterpret_cast<const char*>(p.q);
   const size_t blk_stride = (size_t)B * D * ES;
+
+  int cur_chunk = 0;
+  ChunkMeta cm = make_chunk_meta<B>(sm_prefix, p.lens, p.tables, S, Hkv, cap, p.max_blocks,
+                                    p.num_blocks, R0, R1, lane);
+  ChunkMeta nm = make_chunk_meta<B>(sm_prefix, p.lens, p.tables, S, Hkv, cap, p.max_blocks,
+                                    p.num_blocks, R0 + 32, R1, lane);
+  auto info = [&](int i) {
+    const bool cur = (i >> 5) == cur_chunk;
+    const int j = i & 31;
+    StepInfo si;
+    si.s = __builtin_amdgcn_readlane(cur ? cm.s : nm.s, j);
+    si.g = __builtin_amdgcn_readlane(cur ? cm.g : nm.g, j);
+    si.k = __builtin_amdgcn_readlane(cur ? cm.k : nm.k, j);
+    si.ns = __builtin_amdgcn_readlane(cur ? cm.ns : nm.ns, j);
+    si.L = __builtin_amdgcn_readlane(cur ? cm.L : nm.L, j);
+    si.b0 = __builtin_amdgcn_readlane(cur ? cm.blk : nm.blk, j);
+    si.b1 = B == 16 ? __builtin_amdgcn_readlane(cur ? cm.blk : nm.blk, j + 32) : si.b0;
+    return si;
+  };
 
   struct Regs {
     u32x4 k[NI];
     u32x4 v[DU][BPS][VCH];
   };
 
-  auto load_step = [&](Regs& r, int step) {
-    const int rel = (step * 32) / B;
-    int b0 = __builtin_amdgcn_readlane(tbl, rel);
-    int b1 = b0;
-    if constexpr (B == 16) {
-      if (t0 + step * 32 + 16 < t1) b1 = __builtin_amdgcn_readlane(tbl, rel + 1);
-    }
-#pragma unroll
-    for (int c = 0; c < NI; ++c) {
-      const int tt = TPI * c + row;
-      const int blk = (B == 16 && tt >= 16) ? b1 : b0;
-      const int off = tt & (B - 1);
-      r.k[c] = load16(kbase + ((size_t)blk * Hkv + g) * blk_stride + (size_t)off * D * ES +
-                      (size_t)ch * 16);
-    }
-#pragma unroll
-    for (int u = 0; u < DU; ++u)
-#pragma unroll
-      for (int bb = 0; bb < BPS; ++bb) {
-        const int blk = bb ? b1 : b0;
-        const char* vp = vbase + ((size_t)blk * Hkv + g) * blk_stride +
-                         (size_t)(lane + 64 * u) * B * ES;
-#pragma unroll
-        for (int x = 0; x < VCH; ++x) r.v[u][bb][x] = load16(vp + 16 * x);
-      }
-  };
-
+  u32x4 qnext[G];
+  float qf[G][EPC];
   float m_run[G], l_run[G], acc[G][DU];
+  bool poison = false;
+  int piece_first = 0, piece_k0 = 0;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m_run[h] = kNegInf;
@@ -125,17 +99,75 @@ __global__ __launch_bounds__(64 * W) void decode_partial_valu(DecodeParams p) {
 
   __shared__ float sp[W][G][32];
 
+  auto load_step = [&](Regs& r, int i) {
+    const StepInfo si = info(i);
+    if (i == 0 || si.k == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        qnext[h] = load16(qbase + (((size_t)si.s * p.num_q_heads + (size_t)si.g * G + h) * D +
+                                   (size_t)ch * EPC) * ES);
+    }
+    const int b0 = si.b0 < 0 ? 0 : si.b0;
+    const int b1 = si.b1 < 0 ? 0 : si.b1;
+#pragma unroll
+    for (int c = 0; c < NI; ++c) {
+      const int tt = TPI * c + row;
+      const int blk = (B == 16 && tt >= 16) ? b1 : b0;
+      const int off = tt & (B - 1);
+      r.k[c] = load16(kbase + ((size_t)blk * Hkv + si.g) * blk_stride + (size_t)off * D * ES +
+                      (size_t)ch * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < DU; ++u)
+#pragma unroll
+      for (int bb = 0; bb < BPS; ++bb) {
+        const int blk = bb ? b1 : b0;
+        const char* vp = vbase + ((size_t)blk * Hkv + si.g) * blk_stride +
+                         (size_t)(lane + 64 * u) * B * ES;
+#pragma unroll
+        for (int x = 0; x < VCH; ++x) r.v[u][bb][x] = load16(vp + 16 * x);
+      }
+  };
+
+  auto begin_step = [&](int i) {
+    if ((i >> 5) != cur_chunk) {
+      cur_chunk = i >> 5;
+      cm = nm;
+      nm = make_chunk_meta<B>(sm_prefix, p.lens, p.tables, S, Hkv, cap, p.max_blocks,
+                              p.num_blocks, R0 + 32 * (int64_t)(cur_chunk + 1), R1, lane);
+    }
+    const StepInfo si = info(i);
+    if (i == 0 || si.k == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          if constexpr (ES == 4) qf[h][e] = __uint_as_float(qnext[h][e]);
+          else qf[h][e] = (e & 1) ? hi16<T>(qnext[h][e >> 1]) : lo16<T>(qnext[h][e >> 1]);
+        }
+        m_run[h] = kNegInf;
+        l_run[h] = 0.f;
+#pragma unroll
+        for (int u = 0; u < DU; ++u) acc[h][u] = 0.f;
+      }
+      poison = false;
+      piece_first = i;
+      piece_k0 = si.k;
+    }
+  };
+
   auto value_at = [&](const Regs& r, int u, int t) -> float {
     const int bb = t / B;
     const int tt = t % B;
-    const uint32_t w = r.v[u][bb][tt / VE][(tt % VE) / (4 / ES)];
-    if constexpr (ES == 4) return __uint_as_float(w);
-    else return (tt & 1) ? hi16<T>(w) : lo16<T>(w);
+    const uint32_t wd = r.v[u][bb][tt / VE][(tt % VE) / (4 / ES)];
+    if constexpr (ES == 4) return __uint_as_float(wd);
+    else return (tt & 1) ? hi16<T>(wd) : lo16<T>(wd);
   };
 
-  auto compute_step = [&](Regs& r, int step) {
-    const int tb = t0 + step * 32;
-    const int nvalid = t1 - tb;
+  auto compute_step = [&](Regs& r, int i) {
+    const StepInfo si = info(i);
+    const int nvalid = si.L - 32 * si.k;
+    poison = poison || si.b0 < 0 || (B == 16 && nvalid > 16 && si.b1 < 0);
     float z[NI][G];
 #pragma unroll
     for (int c = 0; c < NI; ++c) {
@@ -201,109 +233,106 @@ __global__ __launch_bounds__(64 * W) void decode_partial_valu(DecodeParams p) {
       }
     }
     __builtin_amdgcn_wave_barrier();
+
+    if (si.k == si.ns - 1 || i == nsteps - 1) {
+      const bool whole = piece_k0 == 0 && si.k == si.ns - 1;
+      const size_t slot = 2 * (size_t)w + (piece_first != 0 ? 1 : 0);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float l_tot = cross_sum<LPR>(l_run[h]);
+        if (poison) l_tot = __builtin_nanf("");
+        if (whole) {
+          const size_t orow = (size_t)si.s * p.num_q_heads + (size_t)si.g * G + h;
+#pragma unroll
+          for (int u = 0; u < DU; ++u) {
+            const float o = l_tot == 0.f ? 0.f : acc[h][u] / l_tot;
+            const int d = lane + 64 * u;
+            if (p.out_f32) {
+              reinterpret_cast<float*>(p.out)[orow * D + d] = o;
+            } else {
+              if constexpr (ES == 2)
+                reinterpret_cast<uint16_t*>(p.out)[orow * D + d] = Elem<T>::from_f32(o);
+            }
+          }
+        } else {
+          const size_t pr = slot * G + h;
+          if (lane == 0) {
+            p.ws_m[pr] = m_run[h];
+            p.ws_l[pr] = l_tot;
+          }
+#pragma unroll
+          for (int u = 0; u < DU; ++u) p.ws_acc[pr * D + lane + 64 * u] = acc[h][u];
+        }
+      }
+    }
   };
 
-  {
-    Regs R0, R1;
-    int st = wave;
-    if (st < n_steps) {
-      load_step(R0, st);
-      while (true) {
-        int nx = st + W < n_steps ? st + W : st;
-        load_step(R1, nx);
-        compute_step(R0, st);
-        st += W;
-        if (st >= n_steps) break;
-        nx = st + W < n_steps ? st + W : st;
-        load_step(R0, nx);
-        compute_step(R1, st);
-        st += W;
-        if (st >= n_steps) break;
-      }
-    }
-  }
-
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    l_run[h] = cross_sum<LPR>(l_run[h]);
-    if (poisoned) l_run[h] = __builtin_nanf("");
-  }
-
-  __shared__ float sm_m[W][G];
-  __shared__ float sm_l[W][G];
-  __shared__ float sm_acc[W > 1 ? W - 1 : 1][G][D];
-  if constexpr (W > 1) {
-    if (wave > 0) {
-      if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          sm_m[wave][h] = m_run[h];
-          sm_l[wave][h] = l_run[h];
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int u = 0; u < DU; ++u) sm_acc[wave - 1][h][lane + 64 * u] = acc[h][u];
-    }
-    __syncthreads();
-    if (wave > 0) return;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float m_star = m_run[h];
-#pragma unroll
-      for (int w = 1; w < W; ++w) m_star = fmaxf(m_star, sm_m[w][h]);
-      const bool empty = m_star == kNegInf;
-      const float c0 = empty ? 0.f : fast_exp2(m_run[h] - m_star);
-      l_run[h] *= c0;
-#pragma unroll
-      for (int u = 0; u < DU; ++u) acc[h][u] *= c0;
-#pragma unroll
-      for (int w = 1; w < W; ++w) {
-        const float cw = empty ? 0.f : fast_exp2(sm_m[w][h] - m_star);
-        l_run[h] += cw * sm_l[w][h];
-#pragma unroll
-        for (int u = 0; u < DU; ++u) acc[h][u] += cw * sm_acc[w - 1][h][lane + 64 * u];
-      }
-      m_run[h] = m_star;
-    }
-  }
-
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const size_t orow = (size_t)s * p.num_q_heads + (size_t)g * G + h;
-    if (n_part == 1) {
-#pragma unroll
-      for (int u = 0; u < DU; ++u) {
-        const float o = l_run[h] == 0.f ? 0.f : acc[h][u] / l_run[h];
-        const int d = lane + 64 * u;
-        if (p.out_f32) {
-          reinterpret_cast<float*>(p.out)[orow * D + d] = o;
-        } else {
-          if constexpr (ES == 2)
-            reinterpret_cast<uint16_t*>(p.out)[orow * D + d] = Elem<T>::from_f32(o);
-        }
-      }
-    } else {
-      const size_t pr = orow * p.n_part_max + part;
-      if (lane == 0) {
-        p.ws_m[pr] = m_run[h];
-        p.ws_l[pr] = l_run[h];
-      }
-#pragma unroll
-      for (int u = 0; u < DU; ++u) p.ws_acc[pr * D + lane + 64 * u] = acc[h][u];
-    }
+  Regs RA, RB;
+  load_step(RA, 0);
+  int i = 0;
+  while (true) {
+    begin_step(i);
+    load_step(RB, i + 1 < nsteps ? i + 1 : i);
+    compute_step(RA, i);
+    if (++i >= nsteps) break;
+    begin_step(i);
+    load_step(RA, i + 1 < nsteps ? i + 1 : i);
+    compute_step(RB, i);
+    if (++i >= nsteps) break;
   }
 }
 
 template <typename T, int D, int B, int G>
-static hipError_t launch_g(const DecodeParams& p, int waves, hipStream_t st) {
-  const int64_t grid = (int64_t)p.num_kv_heads * p.num_seqs * p.n_part_max;
-  if (grid <= 0) return hipSuccess;
+static int resident_g(int waves, size_t lds) {
+  int blocks = 0;
+  hipError_t e = hipErrorInvalidValue;
   switch (waves) {
-    case 1: hipLaunchKernelGGL((decode_partial_valu<T, D, B, G, 1>), dim3((unsigned)grid), dim3(64), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((decode_partial_valu<T, D, B, G, 2>), dim3((unsigned)grid), dim3(128), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((decode_partial_valu<T, D, B, G, 4>), dim3((unsigned)grid), dim3(256), 0, st, p); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_valu<T, D, B, G, 1>, 64, lds); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_valu<T, D, B, G, 2>, 128, lds); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_valu<T, D, B, G, 4>, 256, lds); break;
+    default: break;
+  }
+  return e == hipSuccess ? blocks * waves : 0;
+}
+
+template <typename T, int D, int B>
+static int resident_t(int group, int waves, size_t lds) {
+  switch (group) {
+    case 1: return resident_g<T, D, B, 1>(waves, lds);
+    case 2: if constexpr (sizeof(T) == 4) return resident_g<T, D, B, 2>(waves, lds); break;
+    case 4: if constexpr (sizeof(T) == 4) return resident_g<T, D, B, 4>(waves, lds); break;
+    case 8: if constexpr (sizeof(T) == 4) return resident_g<T, D, B, 8>(waves, lds); break;
+    default: break;
+  }
+  return 0;
+}
+
+int decode_valu_resident_waves(int kv_dtype, int head_dim, int block_size, int group,
+                               int waves, int num_seqs) {
+  const size_t lds = decode_lds_bytes(num_seqs);
+#define PKV_CASE(D, B)                                                                    \
+  if (head_dim == D && block_size == B) {                                                 \
+    if (kv_dtype == 0) return resident_t<float, D, B>(group, waves, lds);                 \
+    if (kv_dtype == 1) return resident_t<f16_t, D, B>(group, waves, lds);                 \
+    if (kv_dtype == 2) return resident_t<bf16_t, D, B>(group, waves, lds);                \
+  }
+  PKV_CASE(64, 16)
+  PKV_CASE(64, 32)
+  PKV_CASE(128, 16)
+  PKV_CASE(128, 32)
+#undef PKV_CASE
+  return 0;
+}
+
+template <typename T, int D, int B, int G>
+static hipError_t launch_g(const DecodeParams& p, int waves, hipStream_t st) {
+  const int grid = (p.num_workers + waves - 1) / waves;
+  if (grid <= 0) return hipSuccess;
+  const size_t lds = decode_lds_bytes(p.num_seqs);
+  switch (waves) {
+    case 1: hipLaunchKernelGGL((decode_valu<T, D, B, G, 1>), dim3(grid), dim3(64), lds, st, p); break;
+    case 2: hipLaunchKernelGGL((decode_valu<T, D, B, G, 2>), dim3(grid), dim3(128), lds, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_valu<T, D, B, G, 4>), dim3(grid), dim3(256), lds, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

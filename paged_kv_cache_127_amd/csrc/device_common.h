@@ -112,19 +112,19 @@ struct DecodeParams {
   const void* v_pool;
   const int32_t* tables;
   const int32_t* lens;
-  float* ws_acc;   // [S][Hq][n_part_max][D]
-  float* ws_m;     // [S][Hq][n_part_max]
-  float* ws_l;     // [S][Hq][n_part_max]
-  int out_f32;     // 1: fp32 output, 0: output in the cache's 16-bit type
+  float* ws_acc;       // [2 * num_workers][G][D] partial accumulators
+  float* ws_m;         // [2 * num_workers][G]    partial running max (log2 domain)
+  float* ws_l;         // [2 * num_workers][G]    partial running sum
+  int64_t* prefix;     // [S + 1] exclusive prefix of steps per sequence
+  int out_f32;         // 1: fp32 output, 0: output in the cache's 16-bit type
   int max_blocks;
   int num_seqs;
   int num_q_heads;
   int num_kv_heads;
   int num_blocks;
   int block_size;
-  int partition;   // tokens per partition, multiple of 32, <= 64 * block_size
-  int n_part_max;  // ceil(max_context_len / partition)
-  float scale_log2;  // softmax scale * log2(e)
+  int num_workers;     // wavefronts that split the step line
+  float scale_log2;    // softmax scale * log2(e)
 };
 
 }  // namespace pkv

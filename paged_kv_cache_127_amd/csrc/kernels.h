@@ -8,11 +8,16 @@
 
 namespace pkv {
 
-// Decode, one partial state per (sequence, KV head, partition). kv_dtype: 0 f32, 1 f16, 2 bf16.
+// Decode over the balanced step schedule (schedule.h). kv_dtype: 0 f32, 1 f16, 2 bf16.
 hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, int head_dim, int block_size,
                               int waves, hipStream_t st);
 hipError_t launch_decode_valu(const DecodeParams& p, int kv_dtype, int head_dim, int block_size,
                               int group, int waves, hipStream_t st);
+// Wavefronts of the decode kernel that fit on one compute unit at once (0 if unknown).
+int decode_mfma_resident_waves(int kv_dtype, int head_dim, int block_size, int waves,
+                               int num_seqs);
+int decode_valu_resident_waves(int kv_dtype, int head_dim, int block_size, int group, int waves,
+                               int num_seqs);
 hipError_t launch_splitk_reduce(const DecodeParams& p, int kv_dtype, int head_dim,
                                 hipStream_t st);
 

@@ -22,15 +22,20 @@ class DeviceBatch:
     def max_ctx(self):
         return max(1, int(self.b.lengths.max())) if self.b.num_seqs else 1
 
-    def decode(self, q=None, out_dtype=torch.float32, partition=0, lens=None, max_ctx=None,
+    def decode(self, q=None, out_dtype=torch.float32, workers=0, lens=None, max_ctx=None,
                tables=None):
         q = self.q if q is None else q
-        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+        out = torch.full(q.shape, float("nan"), dtype=out_dtype, device=q.device)
+        # workspace and output start as NaN: a read of a slot nobody wrote, or a row nobody
+        # wrote, shows up in the result
+        S, Hq, d = q.shape
+        ws = torch.full((pkv.pkv_decode_workspace_size(S, Hq, self.k_pool.shape[1], d, workers),),
+                        255, dtype=torch.uint8, device=q.device)
         pkv.paged_attn_decode(out, q, self.k_pool, self.v_pool,
                               self.tables if tables is None else tables,
                               self.lens if lens is None else lens,
                               self.max_ctx if max_ctx is None else max_ctx,
-                              partition_tokens=partition)
+                              num_workers=workers, workspace=ws)
         torch.cuda.synchronize()
         return out.cpu()
 

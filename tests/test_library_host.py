@@ -110,20 +110,28 @@ def test_decode_argument_checks():
     assert _decode_call(kv_dtype=0, Hq=3, Hkv=1)[0] == -2      # fp32 with G = 3
     assert _decode_call(Hq=17 * 2, Hkv=2)[0] == -2             # G = 17
     assert _decode_call(max_ctx=129)[0] == -1                  # > 8 blocks of 16
-    assert _decode_call(part=48)[0] == -2
-    assert _decode_call(part=64 * 16 + 32, max_blocks=128, max_ctx=2048)[0] == -2
+    assert _decode_call(part=-1)[0] == -1                      # negative worker count
+    assert _decode_call(S=5000)[0] == -2                       # more sequences than one call takes
     rc, msg = _decode_call(max_ctx=128, part=32)
     assert rc == -3 and "workspace" in msg
+    rc, msg = _decode_call(ws=0x1000, ws_bytes=100, part=32)
+    assert rc == -3
     assert _decode_call(out_dtype=1)[0] == -2                  # f16 out for a bf16 cache
 
 
 def test_workspace_size():
+    """Two partial slots per worker (G heads x (d accumulators + max + sum)) and the step prefix
+    of S+1 int64, each region padded to 256 bytes."""
     f = pkv.pkv_decode_workspace_size
-    assert f(4, 8, 2, 128, 512, 512) == 0                      # one partition: no workspace
-    assert f(4, 8, 2, 128, 513, 512) == 4 * 8 * 2 * 130 * 4
-    assert f(8, 64, 8, 128, 32768, 512) == 8 * 64 * 64 * 130 * 4
-    P = pkv.pkv_decode_auto_partition(256, 8, 4096)
-    assert P % 32 == 0 and P > 0
+    up = lambda x: (x + 255) // 256 * 256
+    for S, hq, hkv, d, n in ((4, 8, 2, 128, 7), (256, 64, 8, 128, 1024), (3, 4, 4, 64, 1)):
+        G = hq // hkv
+        slots = 2 * n * G
+        want = up(slots * d * 4) + 2 * up(slots * 4) + up((S + 1) * 8)
+        assert f(S, hq, hkv, d, n) == want
+    assert f(4, 8, 3, 128, 7) == 0                             # not a multiple: no size
+    auto = pkv.pkv_decode_auto_workers()
+    assert auto > 0 and f(256, 64, 8, 128, 0) == f(256, 64, 8, 128, auto)
 
 
 def test_append_and_cow_argument_checks():
