@@ -116,8 +116,7 @@ def main():
     lens = torch.from_numpy(b.lengths).to(dev)
     max_ctx = int(b.lengths.max())
     out = torch.empty(S, Hq, d, dtype=torch.float32, device=dev)
-    ws_bytes = pkv.pkv_decode_workspace_size(S, Hq, Hkv, d, args.workers)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = pkv.decode_workspace(S, Hq, Hkv, d, args.workers, dev)
     k_new, v_new = (x.to(dev) for x in W.new_tokens(b.seed, 1, S, Hkv, d, b.dtype))
     seq_ids = torch.arange(S, dtype=torch.int32, device=dev)
     positions = (lens - 1).to(torch.int32)

@@ -79,11 +79,13 @@ const char* pkv_last_error(void);
  * for a_t, with V applied) -- the gather is fused, no contiguous copy is made. Keys and values
  * of KV head g serve the G query heads g*G .. g*G+G-1 (grouped-query attention, [P1] "Where
  * contiguous allocation wastes space" notes that GQA stores fewer KV heads).
- * Work split: the 32-token steps of all (sequence, KV head) pairs form one line that
- * `num_workers` wavefronts cut into equal contiguous ranges, so each reads the same number of
- * K/V bytes whatever the length mix. A pair finished inside one range is written directly; a
- * pair split across ranges leaves one partial (m, l, acc) per range and a second kernel merges
- * them with the log-sum-exp rule of [P2] "Paged Attention CUDA Kernel" (exact up to rounding).
+ * Work split: the 32-token steps of all (sequence, KV head) pairs form one line, cut into one
+ * contiguous range per wavefront ("worker") of equal weight, where a step weighs one unit and
+ * the start of a pair about one more; so all workers finish close together whatever the
+ * length mix. A pair finished inside one range is written directly; a pair split across
+ * ranges leaves one partial (m, l, acc) per range and a second kernel merges them with the
+ * log-sum-exp rule of [P2] "Paged Attention CUDA Kernel" (exact up to rounding). The split
+ * depends only on the lengths and num_workers, so a call is deterministic.
  * context_lens[s] == 0 gives a zero row.
  *
  *   out           device [num_seqs][num_q_heads][head_dim], element type out_dtype
@@ -92,7 +94,8 @@ const char* pkv_last_error(void);
  *   k_pool,v_pool device, layout above
  *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries past
  *                 ceil(context_lens[s] / block_size) are never read
- *   context_lens  device int32 [num_seqs], each in [0, max_context_len]
+ *   context_lens  device int32 [num_seqs], each in [0, max_context_len] (values outside are
+ *                 clamped to that range)
  *   max_context_len  host int, an upper bound of context_lens, at most
  *                 max_blocks_per_seq * block_size
  *   num_seqs      at most 4096 per call
@@ -101,8 +104,9 @@ const char* pkv_last_error(void);
  *                 resident at once), else 1 .. 2^20 (any count gives the same result up to
  *                 rounding)
  *   workspace     device scratch, 256-byte aligned, of at least
- *                 pkv_decode_workspace_size(...) bytes for the same num_workers; contents need
- *                 no initialisation. Two decode calls in flight at once need two workspaces.
+ *                 pkv_decode_workspace_size(...) bytes for the same num_workers; no contents
+ *                 are assumed between calls. Calls that overlap in time need separate
+ *                 workspaces.
  * --------------------------------------------------------------------------------------- */
 size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                  int num_workers);

@@ -15,7 +15,8 @@ import torch  # loaded first: the library then binds to the HIP runtime torch al
 
 __all__ = [
     "PagedKVError", "paged_attn_decode", "kv_cache_append", "cow_block_copy",
-    "pkv_decode_workspace_size", "pkv_decode_auto_workers", "BlockPool", "timing_enable",
+    "pkv_decode_workspace_size", "decode_workspace",
+    "pkv_decode_auto_workers", "BlockPool", "timing_enable",
     "timing_query", "set_validate", "library_path", "load_library", "PKV_F32", "PKV_F16", "PKV_BF16",
 ]
 
@@ -132,6 +133,13 @@ def pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                          head_dim, num_workers))
 
 
+def decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, num_workers=0,
+                     device="cuda") -> torch.Tensor:
+    """Allocate a decode workspace for these sizes."""
+    n = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, num_workers)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
 def pkv_decode_auto_workers() -> int:
     return int(load_library().pkv_decode_auto_workers())
 
@@ -156,9 +164,8 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
         raise ValueError("block_tables must be [S][max_blocks] and context_lens [S]")
     if out.dtype not in (torch.float32, k_pool.dtype):
         raise TypeError("out must be float32 or the cache dtype")
-    ws_need = pkv_decode_workspace_size(S, Hq, Hkv, d, num_workers)
-    if workspace is None and ws_need > 0:
-        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = decode_workspace(S, Hq, Hkv, d, num_workers, q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(L.paged_attn_decode(

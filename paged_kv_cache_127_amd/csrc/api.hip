@@ -123,18 +123,27 @@ int choose_workers(int num_workers) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Schedule weight of a segment start relative to a step's 4 (a piece start costs about one
+// step of streaming time on gfx950); PAGEDKV_PIECE_WEIGHT overrides it for measurements.
+int piece_weight() {
+  const int v = env_int("PAGEDKV_PIECE_WEIGHT", 4);
+  return v < 0 ? 0 : (v > 64 ? 64 : v);
+}
+
 struct WsLayout {
-  size_t acc, m, l, prefix, total;
+  size_t prefix, wprefix, m, l, acc, total;
 };
 
+// Two partial slots per worker, and the two per-sequence prefixes the merge reads.
 WsLayout ws_layout(int num_seqs, int G, int head_dim, int n) {
+  const size_t slots = 2 * (size_t)n;
   WsLayout L;
-  const size_t slots = 2 * (size_t)n * G;
-  L.acc = 0;
-  L.m = align256(slots * head_dim * sizeof(float));
-  L.l = L.m + align256(slots * sizeof(float));
-  L.prefix = L.l + align256(slots * sizeof(float));
-  L.total = L.prefix + align256(((size_t)num_seqs + 1) * sizeof(int64_t));
+  L.prefix = 0;
+  L.wprefix = align256(((size_t)num_seqs + 1) * sizeof(int64_t));
+  L.m = L.wprefix + align256(((size_t)num_seqs + 1) * sizeof(int64_t));
+  L.l = L.m + align256(slots * G * sizeof(float));
+  L.acc = L.l + align256(slots * G * sizeof(float));
+  L.total = L.acc + align256(slots * G * head_dim * sizeof(float));
   return L;
 }
 
@@ -217,11 +226,12 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
     const int cus = cu_count();
     n = (cus > 0 ? cus : 256) * per_cu;
   }
+  const int pw = piece_weight();
   {
-    // the step line must fit the 64-bit worker arithmetic: N * n < 2^62
-    const double steps_max = (double)num_kv_heads * num_seqs *
-                             ((double)max_blocks_per_seq * block_size / 32.0 + 1.0);
-    if (steps_max * (double)n >= 4.0e18)
+    // the weighted step line must fit the 64-bit worker arithmetic: N_w * n < 2^62
+    const double weight_max = (double)num_kv_heads * num_seqs *
+                              (4.0 * ((double)max_context_len / 32.0 + 1.0) + pw);
+    if (weight_max * (double)n >= 4.0e18)
       return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: problem too large for one call");
   }
   const WsLayout wl = ws_layout(num_seqs, G, head_dim, n);
@@ -258,6 +268,7 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
   p.lens = context_lens;
   p.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
   p.max_blocks = max_blocks_per_seq;
+  p.max_context_len = max_context_len;
   p.num_seqs = num_seqs;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
@@ -266,7 +277,9 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
   p.num_workers = n;
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim);
   p.scale_log2 = sc * 1.4426950408889634f;
+  p.piece_weight = pw;
   char* ws = reinterpret_cast<char*>(workspace);
+  p.wprefix = reinterpret_cast<int64_t*>(ws + wl.wprefix);
   p.ws_acc = reinterpret_cast<float*>(ws + wl.acc);
   p.ws_m = reinterpret_cast<float*>(ws + wl.m);
   p.ws_l = reinterpret_cast<float*>(ws + wl.l);
@@ -285,7 +298,8 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
   if (e != hipSuccess) return launch_error(e, "paged_attn_decode: decode kernel");
   e = timed("splitk_reduce", st,
             [&] { return pkv::launch_splitk_reduce(p, kv_dtype, head_dim, st); });
-  if (e != hipSuccess) return launch_error(e, "paged_attn_decode: merge kernel");
+  if (e != hipSuccess)
+    return launch_error(e, "paged_attn_decode: merge kernel");
   return ok();
 }
 

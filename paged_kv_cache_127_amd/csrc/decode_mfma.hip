@@ -72,13 +72,17 @@ void decode_mfma(DecodeParams p) {
   extern __shared__ int64_t smem[];
   const int S = p.num_seqs;
   int64_t* sm_prefix = smem;
-  int64_t* sm_wave = smem + S + 1;
-  int32_t* sm_len = reinterpret_cast<int32_t*>(smem + S + 1 + 16);
-  const int cap = p.max_blocks * B;
+  int64_t* sm_wts = smem + S + 1;
+  int64_t* sm_wave = smem + 2 * (S + 1);
+  int32_t* sm_len = reinterpret_cast<int32_t*>(smem + 2 * (S + 1) + 16);
+  const int cap = min(p.max_context_len, p.max_blocks * B);   // the workspace is sized for it
   stage_lengths(p.lens, S, cap, sm_len);
-  build_step_prefix(p.lens, S, cap, sm_prefix, sm_wave);
+  build_prefixes(p.lens, S, cap, p.piece_weight, sm_prefix, sm_wts, sm_wave);
   if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i <= S; i += blockDim.x) p.prefix[i] = sm_prefix[i];
+    for (int i = threadIdx.x; i <= S; i += blockDim.x) {
+      p.prefix[i] = sm_prefix[i];
+      p.wprefix[i] = sm_wts[i];
+    }
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -86,14 +90,21 @@ void decode_mfma(DecodeParams p) {
   const int jg = lane >> 4;
   const int Hkv = p.num_kv_heads;
   const int G = p.num_q_heads / Hkv;
-  const int n = p.num_workers;
   const int w = blockIdx.x * W + wave;
-  if (w >= n) return;
-  const int64_t N = (int64_t)Hkv * sm_prefix[S];
-  const int64_t R0 = range_begin(N, n, w);
-  const int nsteps = (int)(range_begin(N, n, w + 1) - R0);
-  if (nsteps <= 0) return;
-  const int64_t R1 = R0 + nsteps;
+  if (w >= p.num_workers) return;
+
+  Walker<B> wk;
+  wk.sm_prefix = sm_prefix;
+  wk.sm_len = sm_len;
+  wk.tables = p.tables;
+  wk.S = S;
+  wk.Hkv = Hkv;
+  wk.max_blocks = p.max_blocks;
+  wk.num_blocks = p.num_blocks;
+  wk.lane = lane;
+  wk.w = w;
+  const Line line = Line::make(sm_prefix, sm_wts, S, Hkv, p.piece_weight, p.num_workers);
+  if (!wk.init(line.steps_before(line.wbegin(w)), line.steps_before(line.wbegin(w + 1)))) return;
 
   const char* kbase = reinterpret_cast<const char*>(p.k_pool);
   const char* vbase = reinterpret_cast<const char*>(p.v_pool);
@@ -106,40 +117,18 @@ void decode_mfma(DecodeParams p) {
   const int kofs1 = (((tokA0 + 4) & (B - 1)) * D + 8 * jg) * ES;
   const int vofs = (r16 * B + (vtok & (B - 1))) * ES;
 
-  // block ids of the current and the next 32-step chunk; the walk itself is a scalar cursor
-  int cur_chunk = 0;
-  int tcur = chunk_blocks<B>(sm_prefix, sm_len, p.tables, S, Hkv, p.max_blocks, p.num_blocks,
-                             R0, R1, lane);
-  int tnext = chunk_blocks<B>(sm_prefix, sm_len, p.tables, S, Hkv, p.max_blocks, p.num_blocks,
-                              R0 + 32, R1, lane);
-  Cursor cur = cursor_at(sm_prefix, sm_len, S, Hkv, R0);   // next step to load
-
   u32x4 qcur[NC];
   float m_run = kNegInf, l_run = 0.f;
-  bool poison = false;
-  int piece_first = 0, piece_k0 = 0;
+  bool poison = false, piece_rfirst = true;
+  int piece_k0 = 0;
   f32x4 oacc[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) oacc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Loads of step i (the cursor's position); returns the step's description.
-  auto load_step = [&](StepRegs<D>& r, int i) {
-    StepInfo si;
-    si.s = cur.s;
-    si.g = cur.g;
-    si.k = cur.k;
-    si.ns = cur.ns;
-    si.L = cur.L;
-    // read the next chunk's block ids only when the step is in it: a select would make every
-    // step wait for that chunk's table load
-    if ((i >> 5) == cur_chunk) {
-      si.b0 = __builtin_amdgcn_readlane(tcur, i & 31);
-      si.b1 = B == 16 ? __builtin_amdgcn_readlane(tcur, (i & 31) + 32) : si.b0;
-    } else {
-      si.b0 = __builtin_amdgcn_readlane(tnext, i & 31);
-      si.b1 = B == 16 ? __builtin_amdgcn_readlane(tnext, (i & 31) + 32) : si.b0;
-    }
-    if (i == 0 || si.k == 0) {   // first step of a piece: its query rows
+  auto starts_piece = [](const StepInfo& si) { return si.rfirst || si.k == 0; };
+
+  auto load_step = [&](StepRegs<D>& r, const StepInfo& si) {
+    if (starts_piece(si)) {   // first step of a piece: its query rows
       const char* qp = qbase + (((size_t)si.s * p.num_q_heads + (size_t)si.g * G + r16) * D +
                                 8 * jg) * ES;
 #pragma unroll
@@ -161,32 +150,25 @@ void decode_mfma(DecodeParams p) {
                                  kv_block_stride + vofs;
 #pragma unroll
     for (int f = 0; f < NF; ++f) r.v[f] = load16(vt + (size_t)16 * f * B * ES);
-    return si;
   };
 
-  // Start of step i: move the block window, and open a new piece.
-  auto begin_step = [&](const StepInfo& si, int i) {
-    if ((i >> 5) != cur_chunk) {
-      cur_chunk = i >> 5;
-      tcur = tnext;
-      tnext = chunk_blocks<B>(sm_prefix, sm_len, p.tables, S, Hkv, p.max_blocks, p.num_blocks,
-                              R0 + 32 * (int64_t)(cur_chunk + 1), R1, lane);
-    }
-    if (i == 0 || si.k == 0) {
+  // Start of a step: open a new piece.
+  auto begin_step = [&](const StepInfo& si) {
+    if (starts_piece(si)) {
       m_run = kNegInf;
       l_run = 0.f;
       poison = false;
-      piece_first = i;
+      piece_rfirst = si.rfirst;
       piece_k0 = si.k;
 #pragma unroll
       for (int f = 0; f < NF; ++f) oacc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
 
-  auto compute_step = [&](StepRegs<D>& r, const StepInfo& si, int i) {
+  auto compute_step = [&](StepRegs<D>& r, const StepInfo& si) {
     // a new piece takes its query rows here, after the next step's loads were issued, so the
     // wait for them never drains the load pipeline
-    if (i == 0 || si.k == 0) {
+    if (starts_piece(si)) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) qcur[c] = r.q[c];
     }
@@ -250,7 +232,7 @@ void decode_mfma(DecodeParams p) {
     }
 
     // end of a piece: write the output (whole segment) or a partial state
-    if (si.k == si.ns - 1 || i == nsteps - 1) {
+    if (si.rlast || si.k == si.ns - 1) {
       float l_tot = cross_sum<16>(l_run);
       if (poison) l_tot = __builtin_nanf("");
       const bool whole = piece_k0 == 0 && si.k == si.ns - 1;
@@ -275,8 +257,7 @@ void decode_mfma(DecodeParams p) {
             }
           }
         } else {
-          const size_t slot = 2 * (size_t)w + (piece_first != 0 ? 1 : 0);
-          const size_t pr_idx = slot * G + r16;
+          const size_t pr_idx = piece_slot(si.range, piece_rfirst) * G + r16;
           if (jg == 0) {
             p.ws_m[pr_idx] = m_run;
             p.ws_l[pr_idx] = l_tot;
@@ -289,31 +270,34 @@ void decode_mfma(DecodeParams p) {
     }
   };
 
-  // Software pipeline: the next step's loads (and the next piece's query rows) are in flight
+  // Software pipeline: the next step's loads (with the next piece's query rows) are in flight
   // while the current step computes. Past the last step the lookahead load repeats the last
   // step's addresses (cache hits), which keeps every load unconditional.
   StepRegs<D> BA, BB;
-  StepInfo sa = load_step(BA, 0), sb;
+  StepInfo sa = wk.load_info(0), sb;
+  load_step(BA, sa);
   int i = 0;
   while (true) {
-    begin_step(sa, i);
-    if (i + 1 < nsteps) {
-      cursor_next(cur, sm_prefix, sm_len, Hkv);
-      sb = load_step(BB, i + 1);
+    wk.advance(i);
+    begin_step(sa);
+    if (wk.has(i + 1)) {
+      sb = wk.load_info(i + 1);
+      load_step(BB, sb);
     } else {
-      load_step(BB, i);
+      load_step(BB, sa);
     }
-    compute_step(BA, sa, i);
-    if (++i >= nsteps) break;
-    begin_step(sb, i);
-    if (i + 1 < nsteps) {
-      cursor_next(cur, sm_prefix, sm_len, Hkv);
-      sa = load_step(BA, i + 1);
+    compute_step(BA, sa);
+    if (!wk.has(++i)) break;
+    wk.advance(i);
+    begin_step(sb);
+    if (wk.has(i + 1)) {
+      sa = wk.load_info(i + 1);
+      load_step(BA, sa);
     } else {
-      load_step(BA, i);
+      load_step(BA, sb);
     }
-    compute_step(BB, sb, i);
-    if (++i >= nsteps) break;
+    compute_step(BB, sb);
+    if (!wk.has(++i)) break;
   }
 }
 

@@ -35,60 +35,54 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
   extern __shared__ int64_t smem[];
   const int S = p.num_seqs;
   int64_t* sm_prefix = smem;
-  int64_t* sm_wave = smem + S + 1;
-  const int cap = p.max_blocks * B;
-  build_step_prefix(p.lens, S, cap, sm_prefix, sm_wave);
+  int64_t* sm_wts = smem + S + 1;
+  int64_t* sm_wave = smem + 2 * (S + 1);
+  int32_t* sm_len = reinterpret_cast<int32_t*>(smem + 2 * (S + 1) + 16);
+  const int cap = min(p.max_context_len, p.max_blocks * B);   // the workspace is sized for it
+  stage_lengths(p.lens, S, cap, sm_len);
+  build_prefixes(p.lens, S, cap, p.piece_weight, sm_prefix, sm_wts, sm_wave);
   if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i <= S; i += blockDim.x) p.prefix[i] = sm_prefix[i];
+    for (int i = threadIdx.x; i <= S; i += blockDim.x) {
+      p.prefix[i] = sm_prefix[i];
+      p.wprefix[i] = sm_wts[i];
+    }
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int row = lane / LPR;
   const int ch = lane % LPR;
   const int Hkv = p.num_kv_heads;
-  const int n = p.num_workers;
   const int w = blockIdx.x * W + wave;
-  if (w >= n) return;
-  const int64_t N = (int64_t)Hkv * sm_prefix[S];
-  const int64_t R0 = range_begin(N, n, w);
-  const int nsteps = (int)(range_begin(N, n, w + 1) - R0);
-  if (nsteps <= 0) return;
-  const int64_t R1 = R0 + nsteps;
+  if (w >= p.num_workers) return;
+
+  Walker<B> wk;
+  wk.sm_prefix = sm_prefix;
+  wk.sm_len = sm_len;
+  wk.tables = p.tables;
+  wk.S = S;
+  wk.Hkv = Hkv;
+  wk.max_blocks = p.max_blocks;
+  wk.num_blocks = p.num_blocks;
+  wk.lane = lane;
+  wk.w = w;
+  const Line line = Line::make(sm_prefix, sm_wts, S, Hkv, p.piece_weight, p.num_workers);
+  if (!wk.init(line.steps_before(line.wbegin(w)), line.steps_before(line.wbegin(w + 1)))) return;
 
   const char* kbase = reinterpret_cast<const char*>(p.k_pool);
   const char* vbase = reinterpret_cast<const char*>(p.v_pool);
   const char* qbase = reinterpret_cast<const char*>(p.q);
   const size_t blk_stride = (size_t)B * D * ES;
 
-  int cur_chunk = 0;
-  ChunkMeta cm = make_chunk_meta<B>(sm_prefix, p.lens, p.tables, S, Hkv, cap, p.max_blocks,
-                                    p.num_blocks, R0, R1, lane);
-  ChunkMeta nm = make_chunk_meta<B>(sm_prefix, p.lens, p.tables, S, Hkv, cap, p.max_blocks,
-                                    p.num_blocks, R0 + 32, R1, lane);
-  auto info = [&](int i) {
-    const bool cur = (i >> 5) == cur_chunk;
-    const int j = i & 31;
-    StepInfo si;
-    si.s = __builtin_amdgcn_readlane(cur ? cm.s : nm.s, j);
-    si.g = __builtin_amdgcn_readlane(cur ? cm.g : nm.g, j);
-    si.k = __builtin_amdgcn_readlane(cur ? cm.k : nm.k, j);
-    si.ns = __builtin_amdgcn_readlane(cur ? cm.ns : nm.ns, j);
-    si.L = __builtin_amdgcn_readlane(cur ? cm.L : nm.L, j);
-    si.b0 = __builtin_amdgcn_readlane(cur ? cm.blk : nm.blk, j);
-    si.b1 = B == 16 ? __builtin_amdgcn_readlane(cur ? cm.blk : nm.blk, j + 32) : si.b0;
-    return si;
-  };
-
   struct Regs {
     u32x4 k[NI];
     u32x4 v[DU][BPS][VCH];
+    u32x4 q[G];   // this lane's slice of the G query rows, for the first step of a piece
   };
 
-  u32x4 qnext[G];
   float qf[G][EPC];
   float m_run[G], l_run[G], acc[G][DU];
-  bool poison = false;
-  int piece_first = 0, piece_k0 = 0;
+  bool poison = false, piece_rfirst = true;
+  int piece_k0 = 0;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m_run[h] = kNegInf;
@@ -99,13 +93,14 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
 
   __shared__ float sp[W][G][32];
 
-  auto load_step = [&](Regs& r, int i) {
-    const StepInfo si = info(i);
-    if (i == 0 || si.k == 0) {
+  auto starts_piece = [](const StepInfo& si) { return si.rfirst || si.k == 0; };
+
+  auto load_step = [&](Regs& r, const StepInfo& si) {
+    if (starts_piece(si)) {
 #pragma unroll
       for (int h = 0; h < G; ++h)
-        qnext[h] = load16(qbase + (((size_t)si.s * p.num_q_heads + (size_t)si.g * G + h) * D +
-                                   (size_t)ch * EPC) * ES);
+        r.q[h] = load16(qbase + (((size_t)si.s * p.num_q_heads + (size_t)si.g * G + h) * D +
+                                 (size_t)ch * EPC) * ES);
     }
     const int b0 = si.b0 < 0 ? 0 : si.b0;
     const int b1 = si.b1 < 0 ? 0 : si.b1;
@@ -129,29 +124,17 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
       }
   };
 
-  auto begin_step = [&](int i) {
-    if ((i >> 5) != cur_chunk) {
-      cur_chunk = i >> 5;
-      cm = nm;
-      nm = make_chunk_meta<B>(sm_prefix, p.lens, p.tables, S, Hkv, cap, p.max_blocks,
-                              p.num_blocks, R0 + 32 * (int64_t)(cur_chunk + 1), R1, lane);
-    }
-    const StepInfo si = info(i);
-    if (i == 0 || si.k == 0) {
+  auto begin_step = [&](const StepInfo& si) {
+    if (starts_piece(si)) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          if constexpr (ES == 4) qf[h][e] = __uint_as_float(qnext[h][e]);
-          else qf[h][e] = (e & 1) ? hi16<T>(qnext[h][e >> 1]) : lo16<T>(qnext[h][e >> 1]);
-        }
         m_run[h] = kNegInf;
         l_run[h] = 0.f;
 #pragma unroll
         for (int u = 0; u < DU; ++u) acc[h][u] = 0.f;
       }
       poison = false;
-      piece_first = i;
+      piece_rfirst = si.rfirst;
       piece_k0 = si.k;
     }
   };
@@ -164,8 +147,16 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
     else return (tt & 1) ? hi16<T>(wd) : lo16<T>(wd);
   };
 
-  auto compute_step = [&](Regs& r, int i) {
-    const StepInfo si = info(i);
+  auto compute_step = [&](Regs& r, const StepInfo& si) {
+    if (starts_piece(si)) {   // after the next step's loads were issued: no pipeline drain
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          if constexpr (ES == 4) qf[h][e] = __uint_as_float(r.q[h][e]);
+          else qf[h][e] = (e & 1) ? hi16<T>(r.q[h][e >> 1]) : lo16<T>(r.q[h][e >> 1]);
+        }
+    }
     const int nvalid = si.L - 32 * si.k;
     poison = poison || si.b0 < 0 || (B == 16 && nvalid > 16 && si.b1 < 0);
     float z[NI][G];
@@ -234,18 +225,19 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
     }
     __builtin_amdgcn_wave_barrier();
 
-    if (si.k == si.ns - 1 || i == nsteps - 1) {
+    if (si.rlast || si.k == si.ns - 1) {
       const bool whole = piece_k0 == 0 && si.k == si.ns - 1;
-      const size_t slot = 2 * (size_t)w + (piece_first != 0 ? 1 : 0);
+      const size_t slot = piece_slot(si.range, piece_rfirst);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float l_tot = cross_sum<LPR>(l_run[h]);
         if (poison) l_tot = __builtin_nanf("");
         if (whole) {
           const size_t orow = (size_t)si.s * p.num_q_heads + (size_t)si.g * G + h;
+          const float inv = l_tot == 0.f ? 0.f : 1.0f / l_tot;
 #pragma unroll
           for (int u = 0; u < DU; ++u) {
-            const float o = l_tot == 0.f ? 0.f : acc[h][u] / l_tot;
+            const float o = acc[h][u] * inv;
             const int d = lane + 64 * u;
             if (p.out_f32) {
               reinterpret_cast<float*>(p.out)[orow * D + d] = o;
@@ -268,17 +260,30 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
   };
 
   Regs RA, RB;
-  load_step(RA, 0);
+  StepInfo sa = wk.load_info(0), sb;
+  load_step(RA, sa);
   int i = 0;
   while (true) {
-    begin_step(i);
-    load_step(RB, i + 1 < nsteps ? i + 1 : i);
-    compute_step(RA, i);
-    if (++i >= nsteps) break;
-    begin_step(i);
-    load_step(RA, i + 1 < nsteps ? i + 1 : i);
-    compute_step(RB, i);
-    if (++i >= nsteps) break;
+    wk.advance(i);
+    begin_step(sa);
+    if (wk.has(i + 1)) {
+      sb = wk.load_info(i + 1);
+      load_step(RB, sb);
+    } else {
+      load_step(RB, sa);
+    }
+    compute_step(RA, sa);
+    if (!wk.has(++i)) break;
+    wk.advance(i);
+    begin_step(sb);
+    if (wk.has(i + 1)) {
+      sa = wk.load_info(i + 1);
+      load_step(RA, sa);
+    } else {
+      load_step(RA, sb);
+    }
+    compute_step(RB, sb);
+    if (!wk.has(++i)) break;
   }
 }
 

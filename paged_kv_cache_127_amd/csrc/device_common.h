@@ -112,18 +112,21 @@ struct DecodeParams {
   const void* v_pool;
   const int32_t* tables;
   const int32_t* lens;
-  float* ws_acc;       // [2 * num_workers][G][D] partial accumulators
-  float* ws_m;         // [2 * num_workers][G]    partial running max (log2 domain)
-  float* ws_l;         // [2 * num_workers][G]    partial running sum
+  float* ws_acc;       // [slots][G][D] partial accumulators
+  float* ws_m;         // [slots][G]    partial running max (log2 domain)
+  float* ws_l;         // [slots][G]    partial running sum
   int64_t* prefix;     // [S + 1] exclusive prefix of steps per sequence
+  int64_t* wprefix;    // [S + 1] exclusive prefix of schedule weights per sequence
   int out_f32;         // 1: fp32 output, 0: output in the cache's 16-bit type
   int max_blocks;
+  int max_context_len;   // lengths are clamped to [0, max_context_len]
   int num_seqs;
   int num_q_heads;
   int num_kv_heads;
   int num_blocks;
   int block_size;
-  int num_workers;     // wavefronts that split the step line
+  int num_workers;     // wavefronts of the decode kernel
+  int piece_weight;    // schedule weight of a segment start (a step weighs 4)
   float scale_log2;    // softmax scale * log2(e)
 };
 

@@ -1,21 +1,31 @@
-// Balanced streaming schedule for the decode kernels.
+// Balanced static streaming schedule for the decode kernels.
 //
 // The decode work is the set of 32-token "steps" of every (sequence, KV head) segment: segment
-// (s, g) holds ns(s) = ceil(L_s / 32) steps, and segments are ordered (s, g). All steps are laid
-// out in one line of N = H_kv * sum_s ns(s) steps, and worker w (one wavefront) streams the
-// contiguous range [w*N/n, (w+1)*N/n) -- every worker reads the same number of K/V bytes to
-// within one step, whatever the length mix. A worker's range crosses segment boundaries; each
-// maximal run of one segment inside a range is a "piece". A piece that is a whole segment
-// writes the normalised output directly. Only a worker's first and last piece can be part of a
-// longer segment; those write a partial softmax state (m, l, acc) -- per-block partials of
-// "Paged Attention and vLLM", section "Paged Attention CUDA Kernel" -- to slot 2w (first
-// piece) or 2w+1 (last piece, when it is not also the first), and the merge kernel combines the
-// partials of each split segment with the log-sum-exp rule of the same section.
+// (s, g) holds ns(s) = ceil(L_s / 32) steps, and segments are ordered (s, g), so all steps form
+// one line of N = H_kv * sum_s ns(s) steps. Each worker (one wavefront) takes one contiguous
+// range of that line, so every worker reads about the same number of K/V bytes whatever the
+// length mix.
 //
-// A worker computes its whole step schedule up front, 32 steps at a time: lane j of a chunk
-// holds segment, step-in-segment and the physical block ids of step j (lane j + 32 holds the
-// second block at block size 16), and the next chunk is prepared while the current one
-// streams, so no dependent table load sits between two steps.
+// A range crosses segment boundaries; each maximal run of one segment inside a range is a
+// "piece". Starting a piece costs time of its own (its query rows, the end-of-piece reduction
+// and output write), so the ranges are cut on a weighted line, not on the step count: every
+// step weighs kStepWeight and every segment start weighs piece_weight more (a weightless mark
+// placed before its first step). A worker owns the steps whose weighted start falls in its
+// equal share [N_w * w / n, N_w * (w + 1) / n) of the weighted total N_w; those are still a
+// contiguous run of steps, so nothing downstream changes. A range full of short sequences thus
+// holds fewer steps than one inside a long sequence, and both take about the same time.
+//
+// A piece that is a whole segment writes the normalised output directly. Only the first and
+// the last piece of a range can be part of a longer segment; those write a partial softmax
+// state (m, l, acc) -- the per-block partials of "Paged Attention and vLLM", section "Paged
+// Attention CUDA Kernel" -- to slot 2w (first piece) or 2w+1 (last piece, when it is not also
+// the first) of worker w, and the merge kernel combines the partials of each split segment with
+// the log-sum-exp rule of the same section.
+//
+// A worker resolves its range a window of up to 32 steps at a time: lane j of a window holds
+// the physical block of step j (lane j + 32 the second block at block size 16), and the next
+// window is prepared while the current one streams, so no dependent table load sits between
+// two steps.
 #pragma once
 
 #include "device_common.h"
@@ -23,21 +33,34 @@
 namespace pkv {
 
 constexpr int kStepTokens = 32;
-constexpr int kMaxSeqsPerCall = 4096;   // LDS holds the per-sequence step prefix
+constexpr int kStepWeight = 4;          // weight of one step on the cut line
+constexpr int kMaxSeqsPerCall = 4096;   // LDS holds the per-sequence prefixes
+constexpr int kNonEmptyBits = 13;       // packs (steps, non-empty count <= 4096) into one int64
 
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
-// Workgroup-wide exclusive prefix of ns(s) over s into sm_prefix[0..S] (sm_prefix[S] = total).
-// All threads of the workgroup must call it.
-__device__ inline void build_step_prefix(const int32_t* lens, int S, int cap, int64_t* sm_prefix,
-                                         int64_t* sm_wave) {
+// Workgroup-wide exclusive prefixes over s of the steps ns(s) (into steps[0..S]) and of the
+// weights kStepWeight * ns(s) + piece_weight * [ns(s) > 0] (into wts[0..S]). All threads of the
+// workgroup must call it; sm_wave holds 16 int64.
+__device__ inline void build_prefixes(const int32_t* lens, int S, int cap, int piece_weight,
+                                      int64_t* steps, int64_t* wts, int64_t* sm_wave) {
   const int nthr = blockDim.x;
   const int t = threadIdx.x;
   const int per = (S + nthr - 1) / nthr;
   const int lo = t * per;
   const int hi = min(lo + per, S);
+  auto packed = [&](int i) -> int64_t {
+    const int ns = ceil_div(clamp_len(lens[i], cap), kStepTokens);
+    return ((int64_t)ns << kNonEmptyBits) + (ns > 0 ? 1 : 0);
+  };
+  auto store = [&](int i, int64_t v) {
+    const int64_t st = v >> kNonEmptyBits;
+    const int64_t ne = v & ((1 << kNonEmptyBits) - 1);
+    steps[i] = st;
+    wts[i] = kStepWeight * st + (int64_t)piece_weight * ne;
+  };
   int64_t sum = 0;
-  for (int i = lo; i < hi; ++i) sum += ceil_div(clamp_len(lens[i], cap), kStepTokens);
+  for (int i = lo; i < hi; ++i) sum += packed(i);
   // inclusive scan of the per-thread sums inside the wavefront
   const int lane = t & 63;
   int64_t inc = sum;
@@ -53,45 +76,98 @@ __device__ inline void build_step_prefix(const int32_t* lens, int S, int cap, in
   for (int w = 0; w < wave; ++w) base += sm_wave[w];
   int64_t run = base + inc - sum;   // exclusive prefix of this thread's first element
   for (int i = lo; i < hi; ++i) {
-    sm_prefix[i] = run;
-    run += ceil_div(clamp_len(lens[i], cap), kStepTokens);
+    store(i, run);
+    run += packed(i);
   }
-  if (t == nthr - 1) sm_prefix[S] = base + inc;
+  if (t == nthr - 1) store(S, base + inc);
   __syncthreads();
 }
 
-// Largest s in [0, S) with Hkv * prefix[s] <= r (r < Hkv * prefix[S]).
-__device__ __forceinline__ int find_seq(const int64_t* sm_prefix, int S, int Hkv, int64_t r) {
+// Largest s in [0, S) with Hkv * prefix[s] <= r (r < Hkv * prefix[S]); for a prefix that is
+// constant over empty sequences this is a sequence with work.
+__device__ __forceinline__ int find_seq(const int64_t* prefix, int S, int Hkv, int64_t r) {
   int lo = 0, hi = S;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if ((int64_t)Hkv * sm_prefix[mid] <= r) lo = mid;
+    if ((int64_t)Hkv * prefix[mid] <= r) lo = mid;
     else hi = mid;
   }
   return lo;
 }
 
-// First step of worker w's range. The host guarantees N * n < 2^62.
+// Start of share w of a line of N units cut into n shares. The host guarantees N * n < 2^62.
 __device__ __forceinline__ int64_t range_begin(int64_t N, int n, int w) {
   return (int64_t)(((uint64_t)N * (uint64_t)w) / (uint64_t)n);
 }
 
-// Worker that owns global step r < N: the largest w with range_begin(w) <= r.
+// Share that holds unit r < N: the largest w with range_begin(w) <= r.
 __device__ __forceinline__ int worker_of(int64_t N, int n, int64_t r) {
   return (int)((((uint64_t)r + 1) * (uint64_t)n - 1) / (uint64_t)N);
 }
 
-// Dynamic LDS of a decode workgroup: the step prefix (S+1 int64), the per-wavefront partial
-// sums (16 int64) and the clamped lengths (S int32).
+// The weighted cut of the step line (prefix arrays in LDS or global memory).
+struct Line {
+  const int64_t* steps;   // [S + 1] step prefix
+  const int64_t* wts;     // [S + 1] weight prefix
+  int S, Hkv, pw, n;
+  int64_t N, Nw;          // steps, total weight
+
+  __device__ static Line make(const int64_t* steps, const int64_t* wts, int S, int Hkv, int pw,
+                              int n) {
+    Line l;
+    l.steps = steps;
+    l.wts = wts;
+    l.S = S;
+    l.Hkv = Hkv;
+    l.pw = pw;
+    l.n = n;
+    l.N = (int64_t)Hkv * steps[S];
+    l.Nw = (int64_t)Hkv * wts[S];
+    return l;
+  }
+  __device__ int64_t wbegin(int w) const { return range_begin(Nw, n, w); }
+  __device__ int owner(int64_t x) const { return worker_of(Nw, n, x); }
+
+  // Steps of one segment (ns steps, weighted start ws0) whose weighted start is below x.
+  __device__ int64_t in_segment_before(int64_t x, int64_t ws0, int64_t ns) const {
+    const int64_t off = x - ws0 - pw;   // steps start at ws0 + pw + kStepWeight * k
+    if (off <= 0) return 0;
+    const int64_t c = (off + kStepWeight - 1) / kStepWeight;
+    return c < ns ? c : ns;
+  }
+
+  // Steps of the whole line whose weighted start is below x (0 <= x <= Nw).
+  __device__ int64_t steps_before(int64_t x) const {
+    if (x >= Nw) return N;
+    const int s = find_seq(wts, S, Hkv, x);
+    const int64_t ns = steps[s + 1] - steps[s];
+    const int64_t seg_w = kStepWeight * ns + pw;
+    const int64_t rem = x - (int64_t)Hkv * wts[s];
+    const int64_t g = rem / seg_w;
+    return (int64_t)Hkv * steps[s] + g * ns +
+           in_segment_before(x, (int64_t)Hkv * wts[s] + g * seg_w, ns);
+  }
+};
+
+// Dynamic LDS of a decode workgroup: the step and weight prefixes (2 x (S+1) int64), the
+// per-wavefront partial sums (16 int64) and the clamped lengths (S int32).
 inline size_t decode_lds_bytes(int num_seqs) {
-  return ((size_t)num_seqs + 1 + 16) * sizeof(int64_t) + (size_t)num_seqs * sizeof(int32_t);
+  return (2 * ((size_t)num_seqs + 1) + 16) * sizeof(int64_t) + (size_t)num_seqs * sizeof(int32_t);
 }
 
-// Store the clamped lengths next to the prefix (all threads of the workgroup call it; a
-// barrier follows in build_step_prefix's caller before use).
+// Store the clamped lengths (all threads of the workgroup call it; build_prefixes' barriers
+// order it before any use).
 __device__ inline void stage_lengths(const int32_t* lens, int S, int cap, int32_t* sm_len) {
   for (int i = threadIdx.x; i < S; i += blockDim.x) sm_len[i] = clamp_len(lens[i], cap);
 }
+
+// Uniform description of one step of a worker's stream.
+struct StepInfo {
+  int s, g, k, ns, L, b0, b1;
+  int range;        // the worker (its partial slots are 2*range, 2*range+1)
+  bool rfirst;      // first step of the worker's range
+  bool rlast;       // last step of the worker's range
+};
 
 // Wave-uniform position in the step line: segment (s, g), step k of ns, sequence length L.
 struct Cursor {
@@ -110,9 +186,10 @@ __device__ inline Cursor cursor_at(const int64_t* sm_prefix, const int32_t* sm_l
   return c;
 }
 
-// Next step of the line (the caller knows one exists).
+// Next step of the line (the caller knows one exists; the walk stops at the last sequence
+// regardless, so that a broken caller cannot loop or leave the prefix array).
 __device__ inline void cursor_next(Cursor& c, const int64_t* sm_prefix, const int32_t* sm_len,
-                                   int Hkv) {
+                                   int S, int Hkv) {
   if (++c.k < c.ns) return;
   c.k = 0;
   if (++c.g < Hkv) return;
@@ -120,66 +197,112 @@ __device__ inline void cursor_next(Cursor& c, const int64_t* sm_prefix, const in
   do {
     ++c.s;
     c.ns = (int)(sm_prefix[c.s + 1] - sm_prefix[c.s]);
-  } while (c.ns == 0);
+  } while (c.ns == 0 && c.s < S - 1);
   c.L = sm_len[c.s];
 }
 
-// Physical block of this lane's slot in a 32-step chunk starting at step r0 of the line: lane j
-// holds the first block of step r0 + (j & 31), lane j + 32 the second (block size 16). -1 marks an
-// out-of-range table entry, 0 a slot past the sequence (never used).
+// Physical block of this lane's slot for the window of steps [r0, r1) (at most 32): lane j
+// holds the first block of step r0 + (j & 31), lane j + 32 the second (block size 16). A step
+// whose tokens all sit in its first block gets that block for its second too: the masked
+// second-half loads then re-read lines the first half fetches, instead of all converging on
+// one fixed block. -1 marks an out-of-range table entry, 0 a lane past the window (unused).
 template <int B>
-__device__ inline int chunk_blocks(const int64_t* sm_prefix, const int32_t* sm_len,
-                                   const int32_t* tables, int S, int Hkv, int max_blocks,
-                                   int num_blocks, int64_t r0, int64_t r1, int lane) {
+__device__ inline int window_blocks(const int64_t* sm_prefix, const int32_t* sm_len,
+                                    const int32_t* tables, int S, int Hkv, int max_blocks,
+                                    int num_blocks, int64_t r0, int64_t r1, int lane) {
   const int64_t r = r0 + (lane & 31);
   if (r >= r1) return 0;
   const Cursor c = cursor_at(sm_prefix, sm_len, S, Hkv, r);
-  const int jb = (B == 16) ? 2 * c.k + (lane >> 5) : c.k;
-  if (jb >= ceil_div(c.L, B)) return 0;
+  int jb = (B == 16) ? 2 * c.k + (lane >> 5) : c.k;
+  if (jb >= ceil_div(c.L, B)) jb -= 1;   // only the second block of a step can be past the end
   const int b = tables[(size_t)c.s * max_blocks + jb];
   return ((unsigned)b < (unsigned)num_blocks) ? b : -1;
 }
 
-// Uniform description of one step of a worker's range.
-struct StepInfo {
-  int s, g, k, ns, L, b0, b1;
-};
-
-// Per-lane schedule of one 32-step chunk of a worker's range.
-struct ChunkMeta {
-  int s;      // sequence
-  int g;      // KV head
-  int k;      // step inside the segment
-  int ns;     // steps in the segment
-  int L;      // tokens of the sequence (clamped)
-  int blk;    // physical block of this lane's block slot, -1 = out-of-range table entry
-};
-
+// Walks one worker's range [b0, end) of the step line in windows of up to 32 steps. Keeps the
+// current and the next window (block ids in one VGPR each); the next one is made as soon as
+// the current one starts, so its table load has a whole window of time.
 template <int B>
-__device__ inline ChunkMeta make_chunk_meta(const int64_t* sm_prefix, const int32_t* lens,
-                                            const int32_t* tables, int S, int Hkv, int cap,
-                                            int max_blocks, int num_blocks, int64_t r0,
-                                            int64_t r1, int lane) {
-  ChunkMeta m{0, 0, 0, 1, 0, 0};
-  const int64_t r = r0 + (lane & 31);
-  if (r < r1) {
-    const int s = find_seq(sm_prefix, S, Hkv, r);
-    const int64_t base = (int64_t)Hkv * sm_prefix[s];
-    const int ns = (int)(sm_prefix[s + 1] - sm_prefix[s]);
-    const int64_t rem = r - base;
-    m.s = s;
-    m.ns = ns;
-    m.g = (int)(rem / ns);
-    m.k = (int)(rem - (int64_t)m.g * ns);
-    m.L = clamp_len(lens[s], cap);
-    const int jb = (B == 16) ? 2 * m.k + (lane >> 5) : m.k;
-    const int nb = ceil_div(m.L, B);
-    if (jb < nb) {
-      const int b = tables[(size_t)s * max_blocks + jb];
-      m.blk = ((unsigned)b < (unsigned)num_blocks) ? b : -1;
+struct Walker {
+  struct Win {
+    int64_t start;   // first line step
+    int len;         // steps (1..32)
+    int i0;          // stream index of the first step
+    int tbl;         // per-lane block ids
+    __device__ int end() const { return i0 + len; }
+  };
+
+  const int64_t* sm_prefix;
+  const int32_t* sm_len;
+  const int32_t* tables;
+  int S, Hkv, max_blocks, num_blocks, lane, w;
+  int64_t b0, next, end;   // the range and the first step not yet in a window
+  Win cw, nw;
+  bool nw_valid;
+  Cursor cur;              // load-side position
+
+  __device__ bool make_window(Win& x, int i0) {
+    if (next >= end) return false;
+    x.start = next;
+    x.len = (int)min((int64_t)32, end - next);
+    next += x.len;
+    x.i0 = i0;
+    x.tbl = window_blocks<B>(sm_prefix, sm_len, tables, S, Hkv, max_blocks, num_blocks,
+                             x.start, x.start + x.len, lane);
+    return true;
+  }
+
+  // Returns false when the range is empty.
+  __device__ bool init(int64_t range_b0, int64_t range_end) {
+    b0 = range_b0;
+    end = range_end;
+    next = b0;
+    if (!make_window(cw, 0)) return false;
+    nw_valid = make_window(nw, cw.end());
+    cur = cursor_at(sm_prefix, sm_len, S, Hkv, b0);
+    return true;
+  }
+
+  __device__ bool has(int i) const { return i < cw.end() || (nw_valid && i < nw.end()); }
+
+  // Compute side reached stream step i (has(i) is true): retire the current window when i
+  // leaves it and start the table load of the one after.
+  __device__ void advance(int i) {
+    if (i >= cw.end()) {
+      cw = nw;
+      nw_valid = make_window(nw, cw.end());
     }
   }
-  return m;
+
+  // Description of stream step i for its loads; steps must be requested in order 0, 1, 2, ...
+  __device__ StepInfo load_info(int i) {
+    if (i != 0) cursor_next(cur, sm_prefix, sm_len, S, Hkv);
+    StepInfo si;
+    si.s = cur.s;
+    si.g = cur.g;
+    si.k = cur.k;
+    si.ns = cur.ns;
+    si.L = cur.L;
+    if (i < cw.end()) {
+      const int j = i - cw.i0;
+      si.b0 = __builtin_amdgcn_readlane(cw.tbl, j);
+      si.b1 = B == 16 ? __builtin_amdgcn_readlane(cw.tbl, j + 32) : si.b0;
+    } else {
+      const int j = i - nw.i0;
+      si.b0 = __builtin_amdgcn_readlane(nw.tbl, j);
+      si.b1 = B == 16 ? __builtin_amdgcn_readlane(nw.tbl, j + 32) : si.b0;
+    }
+    si.range = w;
+    si.rfirst = i == 0;
+    si.rlast = b0 + i == end - 1;
+    return si;
+  }
+};
+
+// Partial slot of the piece that starts at this step: the first piece of a worker's range uses
+// slot 2*w, the last one (when it is not also the first) 2*w + 1.
+__device__ __forceinline__ size_t piece_slot(int w, bool starts_range) {
+  return 2 * (size_t)w + (starts_range ? 0 : 1);
 }
 
 }  // namespace pkv

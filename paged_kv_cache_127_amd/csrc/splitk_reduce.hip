@@ -1,16 +1,21 @@
-// Merge of split segments. A (sequence, KV head) segment whose steps span the ranges of
-// several workers left one partial state (m, l, acc) per worker (schedule.h gives the slot of
-// each); they combine with the log-sum-exp rule of "Paged Attention and vLLM", section
-// "Paged Attention CUDA Kernel":
+// Merge of split segments. A (sequence, KV head) segment whose steps span several worker ranges
+// of the decode schedule (schedule.h) left one partial state (m, l, acc) per range; they combine
+// with the log-sum-exp rule of "Paged Attention and vLLM", section "Paged Attention CUDA Kernel":
 //   m* = max_k m_k,  o = sum_k 2^(m_k - m*) acc_k / sum_k 2^(m_k - m*) l_k
 // (m is kept in the log2 domain). Segments of empty sequences get a zero row here; segments
-// that one worker finished were written by the decode kernel and are skipped.
-// One workgroup per segment; threads cover the G x D outputs of its query heads (G <= 16).
+// that one range finished were written by the decode kernel and are skipped.
+//
+// One workgroup per segment, one thread per few output elements. The slots of the segment
+// follow from the schedule arithmetic alone; each thread loads (m, l, acc) of four slots at a
+// time with independent loads and folds them into a running (max, numerator, denominator), so
+// a segment costs one round trip for the prefixes and one per four partials.
 #include "device_common.h"
 #include "kernels.h"
 #include "schedule.h"
 
 namespace pkv {
+
+constexpr int kMergeBatch = 4;
 
 template <int D, typename T>
 __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
@@ -19,12 +24,13 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
   const int s = seg / Hkv;
   const int g = seg - s * Hkv;
   const int G = p.num_q_heads / Hkv;
-  const int64_t ps = p.prefix[s];
-  const int64_t ns = p.prefix[s + 1] - ps;
+  const int64_t ns = p.prefix[s + 1] - p.prefix[s];
   const size_t row0 = (size_t)s * p.num_q_heads + (size_t)g * G;
+  const int t = threadIdx.x;
+  constexpr int kPer = (16 * D + 255) / 256;   // elements per thread at the largest group (16)
 
-  auto store = [&](int h, int d, float o) {
-    const size_t idx = (row0 + h) * D + d;
+  auto store = [&](int e, float o) {
+    const size_t idx = row0 * D + e;
     if (p.out_f32) {
       reinterpret_cast<float*>(p.out)[idx] = o;
     } else {
@@ -33,73 +39,79 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
   };
 
   if (ns == 0) {
-    for (int e = threadIdx.x; e < G * D; e += blockDim.x) store(e / D, e % D, 0.f);
+    for (int e = t; e < G * D; e += blockDim.x) store(e, 0.f);
     return;
   }
-  const int n = p.num_workers;
-  const int64_t N = (int64_t)Hkv * p.prefix[p.num_seqs];
-  const int64_t G0 = (int64_t)Hkv * ps + (int64_t)g * ns;
-  const int wf = worker_of(N, n, G0);
-  const int wl = worker_of(N, n, G0 + ns - 1);
-  if (wf == wl) return;
-  // the first worker's piece is its last piece (slot 2w+1) unless it also starts its range
-  const int first_slot = 2 * wf + (G0 != range_begin(N, n, wf) ? 1 : 0);
-  constexpr int kChunk = 256;
-  __shared__ int sm_slot[kChunk];
-  __shared__ int sm_cnt;
-  // per-thread online merge state for its (head, dim) outputs
-  constexpr int kPer = (16 * D + 255) / 256;
-  float mrun[kPer], num[kPer], den[kPer];
+  const Line line = Line::make(p.prefix, p.wprefix, p.num_seqs, Hkv, p.piece_weight,
+                               p.num_workers);
+  const int64_t seg_w = kStepWeight * ns + line.pw;
+  const int64_t ws0 = (int64_t)Hkv * p.wprefix[s] + g * seg_w;   // weighted segment start
+  const int64_t first = ws0 + line.pw;                            // weighted start of step 0
+  const int rf = line.owner(first);
+  const int rl = line.owner(first + kStepWeight * (ns - 1));
+  if (rf == rl) return;   // one worker wrote the whole segment
+  // rf's piece is its first one (slot 2 rf) unless rf also holds the previous segment's last
+  // step, which starts at ws0 - kStepWeight
+  const int64_t first_slot = 2 * (int64_t)rf + (line.wbegin(rf) > ws0 - kStepWeight ? 0 : 1);
+
+  float M[kPer], num[kPer], den[kPer];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    mrun[j] = kNegInf;
-    num[j] = 0.f;
-    den[j] = 0.f;
+  for (int q = 0; q < kPer; ++q) {
+    M[q] = kNegInf;
+    num[q] = 0.f;
+    den[q] = 0.f;
   }
-  for (int c0 = wf; c0 <= wl; c0 += kChunk) {
-    // wavefront 0 lists the slots of the non-empty workers in [c0, c0 + kChunk): workers whose
-    // range is empty (more workers than steps) wrote nothing
-    if (threadIdx.x < 64) {
-      const int lane = threadIdx.x;
-      int cnt = 0;
-      for (int b = c0; b < c0 + kChunk && b <= wl; b += 64) {
-        const int w = b + lane;
-        const bool ok = w <= wl && range_begin(N, n, w + 1) != range_begin(N, n, w);
-        const uint64_t mask = __builtin_amdgcn_ballot_w64(ok);
-        if (ok) {
-          const int pos = cnt + __popcll(mask & ((1ull << lane) - 1));
-          sm_slot[pos] = w == wf ? first_slot : 2 * w;
+  // Workers rf+1 .. rl start inside the segment: their first piece (slot 2r) belongs to it if
+  // they hold any of its steps.
+  int64_t before_r = line.in_segment_before(line.wbegin(rf + 1), ws0, ns);
+  for (int r0 = rf; r0 <= rl; r0 += kMergeBatch) {
+    int64_t slot[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int r = r0 + j;
+      slot[j] = -1;
+      if (r == rf) {
+        slot[j] = first_slot;
+      } else if (r <= rl) {
+        const int64_t after_r = r == rl ? ns : line.in_segment_before(line.wbegin(r + 1), ws0, ns);
+        if (after_r > before_r) slot[j] = 2 * (int64_t)r;
+        before_r = after_r;
+      }
+    }
+    float mj[kMergeBatch][kPer], lj[kMergeBatch][kPer], aj[kMergeBatch][kPer];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j)
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int e = t + 256 * q;
+        mj[j][q] = kNegInf;
+        lj[j][q] = 0.f;
+        aj[j][q] = 0.f;
+        if (slot[j] >= 0 && e < G * D) {
+          const int64_t pr = slot[j] * G + e / D;
+          mj[j][q] = p.ws_m[pr];
+          lj[j][q] = p.ws_l[pr];
+          aj[j][q] = p.ws_acc[pr * D + (e % D)];
         }
-        cnt += __popcll(mask);
       }
-      if (lane == 0) sm_cnt = cnt;
-    }
-    __syncthreads();
-    const int cnt = sm_cnt;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int e = threadIdx.x + 256 * j;
-      if (e >= G * D) break;
-      const int h = e / D, d = e - h * D;
-      for (int t = 0; t < cnt; ++t) {
-        const size_t r = (size_t)sm_slot[t] * G + h;
-        const float m = p.ws_m[r];
-        if (m == kNegInf) continue;
-        const float m_new = fmaxf(mrun[j], m);
-        const float a = fast_exp2(mrun[j] - m_new);   // 0 while mrun is still -inf
-        const float c = fast_exp2(m - m_new);
-        num[j] = num[j] * a + c * p.ws_acc[r * D + d];
-        den[j] = den[j] * a + c * p.ws_l[r];
-        mrun[j] = m_new;
+    for (int j = 0; j < kMergeBatch; ++j)
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        if (slot[j] < 0) continue;
+        const float m_new = fmaxf(M[q], mj[j][q]);
+        if (m_new == kNegInf) continue;
+        const float a_old = fast_exp2(M[q] - m_new);
+        const float a_new = fast_exp2(mj[j][q] - m_new);
+        num[q] = num[q] * a_old + a_new * aj[j][q];
+        den[q] = den[q] * a_old + a_new * lj[j][q];
+        M[q] = m_new;
       }
-    }
-    __syncthreads();
   }
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int e = threadIdx.x + 256 * j;
-    if (e >= G * D) break;
-    store(e / D, e % D, den[j] == 0.f ? 0.f : num[j] / den[j]);
+  for (int q = 0; q < kPer; ++q) {
+    const int e = t + 256 * q;
+    if (e < G * D) store(e, den[q] == 0.f ? 0.f : num[q] / den[q]);
   }
 }
 

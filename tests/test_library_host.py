@@ -120,16 +120,16 @@ def test_decode_argument_checks():
 
 
 def test_workspace_size():
-    """Two partial slots per worker (G heads x (d accumulators + max + sum)) and the step prefix
-    of S+1 int64, each region padded to 256 bytes."""
+    """The step and weight prefixes (S+1 int64 each), then m, l and acc for two partial slots per
+    worker -- each region padded to 256 bytes."""
     f = pkv.pkv_decode_workspace_size
     up = lambda x: (x + 255) // 256 * 256
     for S, hq, hkv, d, n in ((4, 8, 2, 128, 7), (256, 64, 8, 128, 1024), (3, 4, 4, 64, 1)):
         G = hq // hkv
-        slots = 2 * n * G
-        want = up(slots * d * 4) + 2 * up(slots * 4) + up((S + 1) * 8)
+        slots = 2 * n
+        want = 2 * up((S + 1) * 8) + 2 * up(slots * G * 4) + up(slots * G * d * 4)
         assert f(S, hq, hkv, d, n) == want
-    assert f(4, 8, 3, 128, 7) == 0                             # not a multiple: no size
+    assert f(4, 8, 3, 128, 7) == 0                        # not a multiple: no size
     auto = pkv.pkv_decode_auto_workers()
     assert auto > 0 and f(256, 64, 8, 128, 0) == f(256, 64, 8, 128, auto)
 
