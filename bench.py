@@ -31,7 +31,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode attention KV GB/s (fraction of HBM peak) and seq-steps/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_mfma_gqa256_b16_traffic.json")
 KERNEL_SOURCES = ["paged_kv_cache_127_amd/csrc/decode_mfma.hip",
-                  "paged_kv_cache_127_amd/csrc/device_common.h"]
+                  "paged_kv_cache_127_amd/csrc/device_common.h",
+                  "paged_kv_cache_127_amd/csrc/schedule.h"]
 
 
 def kernel_source_sha() -> str:
@@ -88,7 +89,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--block-size", type=int, default=16, choices=(16, 32))
     ap.add_argument("--workers", type=int, default=0, help="decode wavefronts (0 = automatic)")
-    ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--cpu-steps", type=int, default=15,
+                    help="decode steps of the CPU oracle (about 0.7 s each on one core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain device copy of this size (counter calibration)")

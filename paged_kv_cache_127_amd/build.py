@@ -25,8 +25,6 @@ HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
     # no packed fp32 instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # a fetch-add stays one lane's plain atomic: its result is read a step later, not at once
-    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", INCLUDE, "-I", CSRC,
 ]
 CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-I", INCLUDE]
