@@ -218,7 +218,7 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
   if (n == 0) {
     // every worker resident at once: the resident wavefronts per CU of the chosen kernel,
     // capped by the per-CU count the automatic workspace size assumes
-    int per_cu = use_mfma ? pkv::decode_mfma_resident_waves(kv_dtype, head_dim, block_size,
+    int per_cu = use_mfma ? pkv::decode_mfma_resident_waves(kv_dtype, head_dim, block_size, G,
                                                             waves, num_seqs)
                           : pkv::decode_valu_resident_waves(kv_dtype, head_dim, block_size, G,
                                                             waves, num_seqs);
@@ -278,6 +278,7 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim);
   p.scale_log2 = sc * 1.4426950408889634f;
   p.piece_weight = pw;
+  p.ring_cap = pkv::ring_capacity(G, head_dim);
   char* ws = reinterpret_cast<char*>(workspace);
   p.wprefix = reinterpret_cast<int64_t*>(ws + wl.wprefix);
   p.ws_acc = reinterpret_cast<float*>(ws + wl.acc);

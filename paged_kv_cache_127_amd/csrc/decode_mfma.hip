@@ -20,7 +20,7 @@
 // Probabilities are split into a 16-bit high part and a 16-bit remainder (two MFMAs), which
 // keeps P.V at close to fp32 accuracy. Scores and the online softmax stay in fp32; the scale
 // (times log2 e) is applied to the fp32 scores and exp2 is used throughout.
-// The next step's loads (with the next piece's query rows) are in flight while a step computes.
+// The next step's loads (with its query rows) are in flight while a step computes.
 #include "device_common.h"
 #include "kernels.h"
 #include "schedule.h"
@@ -42,7 +42,7 @@ template <int D>
 struct StepRegs {
   u32x4 k[2][D / 32];   // K operand per sub-tile and d-chunk
   u32x4 v[D / 16];      // V operand per d-chunk
-  u32x4 q[D / 32];      // Q operand, loaded only for the first step of a piece
+  u32x4 q[D / 32];      // Q operand (the step's query rows)
 };
 
 // Split two fp32 probabilities into packed 16-bit high parts and remainders.
@@ -85,7 +85,7 @@ void decode_mfma(DecodeParams p) {
     }
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = uni((int)(threadIdx.x >> 6));
   const int r16 = lane & 15;
   const int jg = lane >> 4;
   const int Hkv = p.num_kv_heads;
@@ -93,18 +93,21 @@ void decode_mfma(DecodeParams p) {
   const int w = blockIdx.x * W + wave;
   if (w >= p.num_workers) return;
 
-  Walker<B> wk;
-  wk.sm_prefix = sm_prefix;
-  wk.sm_len = sm_len;
-  wk.tables = p.tables;
-  wk.S = S;
-  wk.Hkv = Hkv;
-  wk.max_blocks = p.max_blocks;
-  wk.num_blocks = p.num_blocks;
-  wk.lane = lane;
-  wk.w = w;
-  const Line line = Line::make(sm_prefix, sm_wts, S, Hkv, p.piece_weight, p.num_workers);
-  if (!wk.init(line.steps_before(line.wbegin(w)), line.steps_before(line.wbegin(w + 1)))) return;
+  StepStream<B> ss;
+  ss.sm_prefix = sm_prefix;
+  ss.sm_len = sm_len;
+  ss.tables = (ctable_t)p.tables;
+  ss.S = S;
+  ss.Hkv = Hkv;
+  ss.max_blocks = p.max_blocks;
+  ss.num_blocks = p.num_blocks;
+  ss.w = w;
+  {
+    const Line line = Line::make(sm_prefix, sm_wts, S, Hkv, p.piece_weight, p.num_workers);
+    ss.init(line.steps_before(line.wbegin(w)), line.steps_before(line.wbegin(w + 1)));
+  }
+  const int64_t nsteps = ss.end - ss.b0;
+  if (nsteps <= 0) return;
 
   const char* kbase = reinterpret_cast<const char*>(p.k_pool);
   const char* vbase = reinterpret_cast<const char*>(p.v_pool);
@@ -117,7 +120,19 @@ void decode_mfma(DecodeParams p) {
   const int kofs1 = (((tokA0 + 4) & (B - 1)) * D + 8 * jg) * ES;
   const int vofs = (r16 * B + (vtok & (B - 1))) * ES;
 
-  u32x4 qcur[NC];
+  // Output ring (dynamic LDS after the schedule arrays): piece results are staged here and
+  // written to memory only when the ring is full or the range is done. A vector store that is
+  // still in flight makes every later wait for a vector load a full drain (loads and stores
+  // share one counter and stores complete out of order), so stores stay out of the streaming
+  // loop. Entry: G rows of D floats, then the G running maxima and sums (partials); header:
+  // destination element offset and (slot << 2 | kind).
+  const int R = p.ring_cap;
+  const int EF = G * D + 2 * G;
+  char* ring = reinterpret_cast<char*>(smem) + ring_offset(S) +
+               (size_t)wave * R * (16 + (size_t)EF * 4);
+  int64_t* rhdr = reinterpret_cast<int64_t*>(ring);
+  float* rdat = reinterpret_cast<float*>(ring + (size_t)R * 16);
+  int ring_n = 0;
   float m_run = kNegInf, l_run = 0.f;
   bool poison = false, piece_rfirst = true;
   int piece_k0 = 0;
@@ -127,16 +142,20 @@ void decode_mfma(DecodeParams p) {
 
   auto starts_piece = [](const StepInfo& si) { return si.rfirst || si.k == 0; };
 
+  // All loads of a step are unconditional and branch-free, so the compiler's wait counts stay
+  // exact across the pipelined loop. The query rows are loaded every step (cache hits after a
+  // piece's first step); the padding columns of the 16-wide tile repeat head G-1 and are never
+  // stored.
+  const int qrow = r16 < G ? r16 : G - 1;
   auto load_step = [&](StepRegs<D>& r, const StepInfo& si) {
-    if (starts_piece(si)) {   // first step of a piece: its query rows
-      const char* qp = qbase + (((size_t)si.s * p.num_q_heads + (size_t)si.g * G + r16) * D +
+    {
+      const char* qp = qbase + (((size_t)si.s * p.num_q_heads + (size_t)si.g * G + qrow) * D +
                                 8 * jg) * ES;
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        r.q[c] = r16 < G ? load16(qp + 32 * c * ES) : u32x4{0, 0, 0, 0};
+      for (int c = 0; c < NC; ++c) r.q[c] = load16(qp + 32 * c * ES);
     }
-    const int b0 = si.b0 < 0 ? 0 : si.b0;     // out-of-range entries read block 0, then poison
-    const int b1 = si.b1 < 0 ? 0 : si.b1;
+    const int b0 = valid_block(si.b0, p.num_blocks) ? si.b0 : 0;   // out-of-range: block 0,
+    const int b1 = valid_block(si.b1, p.num_blocks) ? si.b1 : 0;   // then poison
     const char* t0 = kbase + ((size_t)b0 * Hkv + si.g) * kv_block_stride;
     const char* t1 = kbase + ((size_t)b1 * Hkv + si.g) * kv_block_stride;
     const char* ka = (B == 16 && tokA0 >= 16) ? t1 : t0;
@@ -150,6 +169,53 @@ void decode_mfma(DecodeParams p) {
                                  kv_block_stride + vofs;
 #pragma unroll
     for (int f = 0; f < NF; ++f) r.v[f] = load16(vt + (size_t)16 * f * B * ES);
+  };
+
+  // Write the staged piece results: every store instruction covers 1 KB of contiguous memory
+  // (the G rows of one (sequence, KV head) are adjacent in the output and in a partial slot).
+  auto flush = [&](bool drain) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int n4 = G * D / 4;
+    for (int e = 0; e < ring_n; ++e) {
+      const float* so = rdat + (size_t)e * EF;
+      const int64_t dst = uni(rhdr[2 * e]);
+      const int64_t tag = uni(rhdr[2 * e + 1]);
+      const int kind = (int)(tag & 3);
+      if (kind == 2 && lane < G) {
+        const int64_t slot = tag >> 2;
+        p.ws_m[slot * G + lane] = so[G * D + lane];
+        p.ws_l[slot * G + lane] = so[G * D + G + lane];
+      }
+#pragma unroll
+      for (int k = 0; k < (16 * D / 4) / 64; ++k) {
+        const int e4 = lane + 64 * k;
+        if (e4 < n4) {
+          const f32x4 o = *reinterpret_cast<const f32x4*>(so + 4 * e4);
+          if (kind == 0) {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + dst + 4 * e4) = o;
+          } else if (kind == 1) {
+            const uint32_t w0 = (uint32_t)Elem<T>::from_f32(o[0]) |
+                                ((uint32_t)Elem<T>::from_f32(o[1]) << 16);
+            const uint32_t w1 = (uint32_t)Elem<T>::from_f32(o[2]) |
+                                ((uint32_t)Elem<T>::from_f32(o[3]) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + dst + 4 * e4) =
+                make_uint2(w0, w1);
+          } else {
+            *reinterpret_cast<f32x4*>(p.ws_acc + dst + 4 * e4) = o;
+          }
+        }
+      }
+    }
+    ring_n = 0;
+    // Inside the loop (ring full, rare) wait for the stores right here, so that no store is
+    // pending when the next vector-load wait comes; the s_waitcnt immediate is vmcnt(0) with
+    // the other counters left free.
+    if (drain) __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
   // Start of a step: open a new piece.
@@ -166,20 +232,15 @@ void decode_mfma(DecodeParams p) {
   };
 
   auto compute_step = [&](StepRegs<D>& r, const StepInfo& si) {
-    // a new piece takes its query rows here, after the next step's loads were issued, so the
-    // wait for them never drains the load pipeline
-    if (starts_piece(si)) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) qcur[c] = r.q[c];
-    }
     const int nvalid = si.L - 32 * si.k;             // valid tokens in this step (>= 1)
-    poison = poison || si.b0 < 0 || (B == 16 && nvalid > 16 && si.b1 < 0);
+    poison = poison || !valid_block(si.b0, p.num_blocks) ||
+             (B == 16 && nvalid > 16 && !valid_block(si.b1, p.num_blocks));
     f32x4 sacc[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       sacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) sacc[a] = mfma16x16x32<T>(r.k[a][c], qcur[c], sacc[a]);
+      for (int c = 0; c < NC; ++c) sacc[a] = mfma16x16x32<T>(r.k[a][c], r.q[c], sacc[a]);
     }
     float z[8];
 #pragma unroll
@@ -231,78 +292,70 @@ void decode_mfma(DecodeParams p) {
       oacc[f] = mfma16x16x32<T>(r.v[f], plo, oacc[f]);
     }
 
-    // end of a piece: write the output (whole segment) or a partial state
+    // End of a piece: stage the output (whole segment, normalised) or the partial state.
     if (si.rlast || si.k == si.ns - 1) {
       float l_tot = cross_sum<16>(l_run);
       if (poison) l_tot = __builtin_nanf("");
       const bool whole = piece_k0 == 0 && si.k == si.ns - 1;
+      const float so_scale = whole ? (l_tot == 0.f ? 0.f : 1.0f / l_tot) : 1.f;
+      float* so = rdat + (size_t)ring_n * EF;
       if (r16 < G) {
-        const int h = si.g * G + r16;
-        if (whole) {
-          const size_t row = (size_t)si.s * p.num_q_heads + h;
-          const float inv = l_tot == 0.f ? 0.f : 1.0f / l_tot;
 #pragma unroll
-          for (int f = 0; f < NF; ++f) {
-            const f32x4 o = oacc[f] * inv;
-            const int d0 = 16 * f + 4 * jg;
-            if (p.out_f32) {
-              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + row * D + d0) = o;
-            } else {
-              uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + row * D + d0;
-              const uint32_t w0 = (uint32_t)Elem<T>::from_f32(o[0]) |
-                                  ((uint32_t)Elem<T>::from_f32(o[1]) << 16);
-              const uint32_t w1 = (uint32_t)Elem<T>::from_f32(o[2]) |
-                                  ((uint32_t)Elem<T>::from_f32(o[3]) << 16);
-              *reinterpret_cast<uint2*>(op) = make_uint2(w0, w1);
-            }
-          }
-        } else {
-          const size_t pr_idx = piece_slot(si.range, piece_rfirst) * G + r16;
-          if (jg == 0) {
-            p.ws_m[pr_idx] = m_run;
-            p.ws_l[pr_idx] = l_tot;
-          }
-#pragma unroll
-          for (int f = 0; f < NF; ++f)
-            *reinterpret_cast<f32x4*>(p.ws_acc + pr_idx * D + 16 * f + 4 * jg) = oacc[f];
+        for (int f = 0; f < NF; ++f)
+          *reinterpret_cast<f32x4*>(so + r16 * D + 16 * f + 4 * jg) = oacc[f] * so_scale;
+        if (!whole && jg == 0) {
+          so[G * D + r16] = m_run;
+          so[G * D + G + r16] = l_tot;
         }
       }
+      if (lane == 0) {
+        if (whole) {
+          rhdr[2 * ring_n] = ((int64_t)si.s * p.num_q_heads + (int64_t)si.g * G) * D;
+          rhdr[2 * ring_n + 1] = p.out_f32 ? 0 : 1;
+        } else {
+          const int64_t slot = (int64_t)piece_slot(si.range, piece_rfirst);
+          rhdr[2 * ring_n] = slot * G * D;
+          rhdr[2 * ring_n + 1] = (slot << 2) | 2;
+        }
+      }
+      if (++ring_n == R) flush(true);
     }
   };
 
-  // Software pipeline: the next step's loads (with the next piece's query rows) are in flight
-  // while the current step computes. Past the last step the lookahead load repeats the last
-  // step's addresses (cache hits), which keeps every load unconditional.
+  // Software pipeline over two register buffers: while step i computes, the loads of step
+  // i + 1 are in flight; the loads of step i + 2 are issued into the buffer step i has just
+  // consumed, and the block ids of the step after that are being fetched (scalar loads). Past
+  // the last step the stream repeats it (cache hits), which keeps every vector load
+  // unconditional. The loop runs over pairs of steps with its only exit at the bottom, so the
+  // compiler's wait counts stay exact; an odd last step is finished after it.
   StepRegs<D> BA, BB;
-  StepInfo sa = wk.load_info(0), sb;
+  StepInfo sa = ss.next();
+  StepInfo sb = ss.next();
   load_step(BA, sa);
-  int i = 0;
-  while (true) {
-    wk.advance(i);
+  load_step(BB, sb);
+  StepInfo sc = ss.next();
+  for (int64_t i = 0; i + 2 <= nsteps; i += 2) {
+    // BA: step i (sa); BB: step i + 1 (sb); sc describes step i + 2
     begin_step(sa);
-    if (wk.has(i + 1)) {
-      sb = wk.load_info(i + 1);
-      load_step(BB, sb);
-    } else {
-      load_step(BB, sa);
-    }
     compute_step(BA, sa);
-    if (!wk.has(++i)) break;
-    wk.advance(i);
+    load_step(BA, sc);
+    const StepInfo sd = ss.next();
     begin_step(sb);
-    if (wk.has(i + 1)) {
-      sa = wk.load_info(i + 1);
-      load_step(BA, sa);
-    } else {
-      load_step(BA, sb);
-    }
     compute_step(BB, sb);
-    if (!wk.has(++i)) break;
+    load_step(BB, sd);
+    sa = sc;
+    sb = sd;
+    sc = ss.next();
   }
+  if (nsteps & 1) {
+    begin_step(sa);
+    compute_step(BA, sa);
+  }
+  flush(false);
 }
 
 template <typename T, int D, int B>
-static int resident_t(int waves, size_t lds) {
+static int resident_t(int waves, size_t lds) {   // lds: dynamic bytes for this many waves
   int blocks = 0;
   hipError_t e = hipErrorInvalidValue;
   switch (waves) {
@@ -314,9 +367,9 @@ static int resident_t(int waves, size_t lds) {
   return e == hipSuccess ? blocks * waves : 0;
 }
 
-int decode_mfma_resident_waves(int kv_dtype, int head_dim, int block_size, int waves,
+int decode_mfma_resident_waves(int kv_dtype, int head_dim, int block_size, int group, int waves,
                                int num_seqs) {
-  const size_t lds = decode_lds_bytes(num_seqs);
+  const size_t lds = mfma_lds_bytes(num_seqs, group, head_dim, waves);
   const bool bf = kv_dtype == 2;
 #define PKV_CASE(D, B)                                                                   \
   if (head_dim == D && block_size == B)                                                  \
@@ -333,7 +386,7 @@ template <typename T, int D, int B>
 static hipError_t launch_t(const DecodeParams& p, int waves, hipStream_t st) {
   const int grid = (p.num_workers + waves - 1) / waves;
   if (grid <= 0) return hipSuccess;
-  const size_t lds = decode_lds_bytes(p.num_seqs);
+  const size_t lds = mfma_lds_bytes(p.num_seqs, p.num_q_heads / p.num_kv_heads, D, waves);
   switch (waves) {
     case 1: hipLaunchKernelGGL((decode_mfma<T, D, B, 1>), dim3(grid), dim3(64), lds, st, p); break;
     case 2: hipLaunchKernelGGL((decode_mfma<T, D, B, 2>), dim3(grid), dim3(128), lds, st, p); break;

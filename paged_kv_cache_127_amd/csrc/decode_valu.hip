@@ -48,25 +48,28 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
     }
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = uni((int)(threadIdx.x >> 6));
   const int row = lane / LPR;
   const int ch = lane % LPR;
   const int Hkv = p.num_kv_heads;
   const int w = blockIdx.x * W + wave;
   if (w >= p.num_workers) return;
 
-  Walker<B> wk;
-  wk.sm_prefix = sm_prefix;
-  wk.sm_len = sm_len;
-  wk.tables = p.tables;
-  wk.S = S;
-  wk.Hkv = Hkv;
-  wk.max_blocks = p.max_blocks;
-  wk.num_blocks = p.num_blocks;
-  wk.lane = lane;
-  wk.w = w;
-  const Line line = Line::make(sm_prefix, sm_wts, S, Hkv, p.piece_weight, p.num_workers);
-  if (!wk.init(line.steps_before(line.wbegin(w)), line.steps_before(line.wbegin(w + 1)))) return;
+  StepStream<B> ss;
+  ss.sm_prefix = sm_prefix;
+  ss.sm_len = sm_len;
+  ss.tables = (ctable_t)p.tables;
+  ss.S = S;
+  ss.Hkv = Hkv;
+  ss.max_blocks = p.max_blocks;
+  ss.num_blocks = p.num_blocks;
+  ss.w = w;
+  {
+    const Line line = Line::make(sm_prefix, sm_wts, S, Hkv, p.piece_weight, p.num_workers);
+    ss.init(line.steps_before(line.wbegin(w)), line.steps_before(line.wbegin(w + 1)));
+  }
+  const int64_t nsteps = ss.end - ss.b0;
+  if (nsteps <= 0) return;
 
   const char* kbase = reinterpret_cast<const char*>(p.k_pool);
   const char* vbase = reinterpret_cast<const char*>(p.v_pool);
@@ -76,10 +79,9 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
   struct Regs {
     u32x4 k[NI];
     u32x4 v[DU][BPS][VCH];
-    u32x4 q[G];   // this lane's slice of the G query rows, for the first step of a piece
+    u32x4 q[G];   // this lane's slice of the G query rows of the step's KV head
   };
 
-  float qf[G][EPC];
   float m_run[G], l_run[G], acc[G][DU];
   bool poison = false, piece_rfirst = true;
   int piece_k0 = 0;
@@ -96,14 +98,13 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
   auto starts_piece = [](const StepInfo& si) { return si.rfirst || si.k == 0; };
 
   auto load_step = [&](Regs& r, const StepInfo& si) {
-    if (starts_piece(si)) {
+    // the query rows every step, so that no load is conditional (cache hits after the first)
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-        r.q[h] = load16(qbase + (((size_t)si.s * p.num_q_heads + (size_t)si.g * G + h) * D +
-                                 (size_t)ch * EPC) * ES);
-    }
-    const int b0 = si.b0 < 0 ? 0 : si.b0;
-    const int b1 = si.b1 < 0 ? 0 : si.b1;
+    for (int h = 0; h < G; ++h)
+      r.q[h] = load16(qbase + (((size_t)si.s * p.num_q_heads + (size_t)si.g * G + h) * D +
+                               (size_t)ch * EPC) * ES);
+    const int b0 = valid_block(si.b0, p.num_blocks) ? si.b0 : 0;   // out-of-range: block 0,
+    const int b1 = valid_block(si.b1, p.num_blocks) ? si.b1 : 0;   // then poison
 #pragma unroll
     for (int c = 0; c < NI; ++c) {
       const int tt = TPI * c + row;
@@ -148,17 +149,17 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
   };
 
   auto compute_step = [&](Regs& r, const StepInfo& si) {
-    if (starts_piece(si)) {   // after the next step's loads were issued: no pipeline drain
+    float qf[G][EPC];
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          if constexpr (ES == 4) qf[h][e] = __uint_as_float(r.q[h][e]);
-          else qf[h][e] = (e & 1) ? hi16<T>(r.q[h][e >> 1]) : lo16<T>(r.q[h][e >> 1]);
-        }
-    }
+      for (int e = 0; e < EPC; ++e) {
+        if constexpr (ES == 4) qf[h][e] = __uint_as_float(r.q[h][e]);
+        else qf[h][e] = (e & 1) ? hi16<T>(r.q[h][e >> 1]) : lo16<T>(r.q[h][e >> 1]);
+      }
     const int nvalid = si.L - 32 * si.k;
-    poison = poison || si.b0 < 0 || (B == 16 && nvalid > 16 && si.b1 < 0);
+    poison = poison || !valid_block(si.b0, p.num_blocks) ||
+             (B == 16 && nvalid > 16 && !valid_block(si.b1, p.num_blocks));
     float z[NI][G];
 #pragma unroll
     for (int c = 0; c < NI; ++c) {
@@ -259,31 +260,34 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
     }
   };
 
+  // Software pipeline over two register buffers: while step i computes, the loads of step
+  // i + 1 are in flight; the loads of step i + 2 are issued into the buffer step i has just
+  // consumed, and the block ids of the step after that are being fetched (scalar loads). Past
+  // the last step the stream repeats it (cache hits), which keeps every vector load
+  // unconditional. The loop runs over pairs of steps with its only exit at the bottom, so the
+  // compiler's wait counts stay exact; an odd last step is finished after it.
   Regs RA, RB;
-  StepInfo sa = wk.load_info(0), sb;
+  StepInfo sa = ss.next();
+  StepInfo sb = ss.next();
   load_step(RA, sa);
-  int i = 0;
-  while (true) {
-    wk.advance(i);
+  load_step(RB, sb);
+  StepInfo sc = ss.next();
+  for (int64_t i = 0; i + 2 <= nsteps; i += 2) {
+    // RA: step i (sa); RB: step i + 1 (sb); sc describes step i + 2
     begin_step(sa);
-    if (wk.has(i + 1)) {
-      sb = wk.load_info(i + 1);
-      load_step(RB, sb);
-    } else {
-      load_step(RB, sa);
-    }
     compute_step(RA, sa);
-    if (!wk.has(++i)) break;
-    wk.advance(i);
+    load_step(RA, sc);
+    const StepInfo sd = ss.next();
     begin_step(sb);
-    if (wk.has(i + 1)) {
-      sa = wk.load_info(i + 1);
-      load_step(RA, sa);
-    } else {
-      load_step(RA, sb);
-    }
     compute_step(RB, sb);
-    if (!wk.has(++i)) break;
+    load_step(RB, sd);
+    sa = sc;
+    sb = sd;
+    sc = ss.next();
+  }
+  if (nsteps & 1) {
+    begin_step(sa);
+    compute_step(RA, sa);
   }
 }
 

@@ -127,6 +127,7 @@ struct DecodeParams {
   int block_size;
   int num_workers;     // wavefronts of the decode kernel
   int piece_weight;    // schedule weight of a segment start (a step weighs 4)
+  int ring_cap;        // staged piece results per wavefront (matrix-core kernel)
   float scale_log2;    // softmax scale * log2(e)
 };
 

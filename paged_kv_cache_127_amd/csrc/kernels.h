@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "device_common.h"
+#include "schedule.h"
 
 namespace pkv {
 
@@ -14,8 +15,22 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, int head_dim,
 hipError_t launch_decode_valu(const DecodeParams& p, int kv_dtype, int head_dim, int block_size,
                               int group, int waves, hipStream_t st);
 // Wavefronts of the decode kernel that fit on one compute unit at once (0 if unknown).
-int decode_mfma_resident_waves(int kv_dtype, int head_dim, int block_size, int waves,
+int decode_mfma_resident_waves(int kv_dtype, int head_dim, int block_size, int group, int waves,
                                int num_seqs);
+
+// Output ring of the matrix-core decode kernel: per wavefront, ring_capacity staged piece
+// results of G rows x D floats plus 2 G floats, each with a 16-byte header, in dynamic LDS
+// after the schedule arrays.
+constexpr size_t kRingBudgetBytes = 32 * 1024;   // per wavefront
+inline int ring_capacity(int group, int head_dim) {
+  const size_t per = 16 + 4 * ((size_t)group * head_dim + 2 * (size_t)group);
+  const size_t r = kRingBudgetBytes / per;
+  return r < 1 ? 1 : (r > 16 ? 16 : (int)r);
+}
+inline size_t mfma_lds_bytes(int num_seqs, int group, int head_dim, int waves) {
+  const size_t per = 16 + 4 * ((size_t)group * head_dim + 2 * (size_t)group);
+  return ring_offset(num_seqs) + (size_t)waves * ring_capacity(group, head_dim) * per;
+}
 int decode_valu_resident_waves(int kv_dtype, int head_dim, int block_size, int group, int waves,
                                int num_seqs);
 hipError_t launch_splitk_reduce(const DecodeParams& p, int kv_dtype, int head_dim,

@@ -22,10 +22,10 @@
 // the first) of worker w, and the merge kernel combines the partials of each split segment with
 // the log-sum-exp rule of the same section.
 //
-// A worker resolves its range a window of up to 32 steps at a time: lane j of a window holds
-// the physical block of step j (lane j + 32 the second block at block size 16), and the next
-// window is prepared while the current one streams, so no dependent table load sits between
-// two steps.
+// A worker walks its range with a wave-uniform cursor held in scalar registers. The physical
+// block ids of a step come from scalar loads of the block table, issued two steps before the
+// step's K/V loads, so no dependent table load sits between two steps and no vector-memory
+// wait is ever spent on the schedule.
 #pragma once
 
 #include "device_common.h"
@@ -38,6 +38,19 @@ constexpr int kMaxSeqsPerCall = 4096;   // LDS holds the per-sequence prefixes
 constexpr int kNonEmptyBits = 13;       // packs (steps, non-empty count <= 4096) into one int64
 
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
+
+// Wave-uniform copies (scalar registers) of values every lane holds alike, e.g. LDS reads at a
+// uniform address: branches on them are scalar branches, not exec-mask regions.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The block table seen through the constant address space: loads at uniform addresses become
+// scalar loads (the table is read-only during a call).
+typedef const __attribute__((address_space(4))) int32_t* ctable_t;
 
 // Workgroup-wide exclusive prefixes over s of the steps ns(s) (into steps[0..S]) and of the
 // weights kStepWeight * ns(s) + piece_weight * [ns(s) > 0] (into wts[0..S]). All threads of the
@@ -89,7 +102,7 @@ __device__ __forceinline__ int find_seq(const int64_t* prefix, int S, int Hkv, i
   int lo = 0, hi = S;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if ((int64_t)Hkv * prefix[mid] <= r) lo = mid;
+    if ((int64_t)Hkv * uni(prefix[mid]) <= r) lo = mid;
     else hi = mid;
   }
   return lo;
@@ -121,8 +134,8 @@ struct Line {
     l.Hkv = Hkv;
     l.pw = pw;
     l.n = n;
-    l.N = (int64_t)Hkv * steps[S];
-    l.Nw = (int64_t)Hkv * wts[S];
+    l.N = (int64_t)Hkv * uni(steps[S]);
+    l.Nw = (int64_t)Hkv * uni(wts[S]);
     return l;
   }
   __device__ int64_t wbegin(int w) const { return range_begin(Nw, n, w); }
@@ -140,19 +153,24 @@ struct Line {
   __device__ int64_t steps_before(int64_t x) const {
     if (x >= Nw) return N;
     const int s = find_seq(wts, S, Hkv, x);
-    const int64_t ns = steps[s + 1] - steps[s];
+    const int64_t st0 = uni(steps[s]);
+    const int64_t ns = uni(steps[s + 1]) - st0;
     const int64_t seg_w = kStepWeight * ns + pw;
-    const int64_t rem = x - (int64_t)Hkv * wts[s];
-    const int64_t g = rem / seg_w;
-    return (int64_t)Hkv * steps[s] + g * ns +
-           in_segment_before(x, (int64_t)Hkv * wts[s] + g * seg_w, ns);
+    const int64_t w0 = (int64_t)Hkv * uni(wts[s]);
+    const int64_t g = (x - w0) / seg_w;
+    return (int64_t)Hkv * st0 + g * ns + in_segment_before(x, w0 + g * seg_w, ns);
   }
 };
 
 // Dynamic LDS of a decode workgroup: the step and weight prefixes (2 x (S+1) int64), the
 // per-wavefront partial sums (16 int64) and the clamped lengths (S int32).
-inline size_t decode_lds_bytes(int num_seqs) {
+__host__ __device__ inline size_t decode_lds_bytes(int num_seqs) {
   return (2 * ((size_t)num_seqs + 1) + 16) * sizeof(int64_t) + (size_t)num_seqs * sizeof(int32_t);
+}
+
+// Start of whatever a kernel keeps in dynamic LDS after the schedule arrays (16-byte aligned).
+__host__ __device__ inline size_t ring_offset(int num_seqs) {
+  return (decode_lds_bytes(num_seqs) + 15) & ~(size_t)15;
 }
 
 // Store the clamped lengths (all threads of the workgroup call it; build_prefixes' barriers
@@ -178,11 +196,12 @@ __device__ inline Cursor cursor_at(const int64_t* sm_prefix, const int32_t* sm_l
                                    int Hkv, int64_t r) {
   Cursor c;
   c.s = find_seq(sm_prefix, S, Hkv, r);
-  const int64_t rem = r - (int64_t)Hkv * sm_prefix[c.s];
-  c.ns = (int)(sm_prefix[c.s + 1] - sm_prefix[c.s]);
+  const int64_t p0 = uni(sm_prefix[c.s]);
+  const int64_t rem = r - (int64_t)Hkv * p0;
+  c.ns = (int)(uni(sm_prefix[c.s + 1]) - p0);
   c.g = (int)(rem / c.ns);
   c.k = (int)(rem - (int64_t)c.g * c.ns);
-  c.L = sm_len[c.s];
+  c.L = uni(sm_len[c.s]);
   return c;
 }
 
@@ -196,105 +215,60 @@ __device__ inline void cursor_next(Cursor& c, const int64_t* sm_prefix, const in
   c.g = 0;
   do {
     ++c.s;
-    c.ns = (int)(sm_prefix[c.s + 1] - sm_prefix[c.s]);
+    c.ns = (int)(uni(sm_prefix[c.s + 1]) - uni(sm_prefix[c.s]));
   } while (c.ns == 0 && c.s < S - 1);
-  c.L = sm_len[c.s];
+  c.L = uni(sm_len[c.s]);
 }
 
-// Physical block of this lane's slot for the window of steps [r0, r1) (at most 32): lane j
-// holds the first block of step r0 + (j & 31), lane j + 32 the second (block size 16). A step
-// whose tokens all sit in its first block gets that block for its second too: the masked
-// second-half loads then re-read lines the first half fetches, instead of all converging on
-// one fixed block. -1 marks an out-of-range table entry, 0 a lane past the window (unused).
-template <int B>
-__device__ inline int window_blocks(const int64_t* sm_prefix, const int32_t* sm_len,
-                                    const int32_t* tables, int S, int Hkv, int max_blocks,
-                                    int num_blocks, int64_t r0, int64_t r1, int lane) {
-  const int64_t r = r0 + (lane & 31);
-  if (r >= r1) return 0;
-  const Cursor c = cursor_at(sm_prefix, sm_len, S, Hkv, r);
-  int jb = (B == 16) ? 2 * c.k + (lane >> 5) : c.k;
-  if (jb >= ceil_div(c.L, B)) jb -= 1;   // only the second block of a step can be past the end
-  const int b = tables[(size_t)c.s * max_blocks + jb];
-  return ((unsigned)b < (unsigned)num_blocks) ? b : -1;
+// Physical block ids come from the caller's table; anything outside [0, num_blocks) is read as
+// block 0 and poisons the row.
+__device__ __forceinline__ bool valid_block(int b, int num_blocks) {
+  return (unsigned)b < (unsigned)num_blocks;
 }
 
-// Walks one worker's range [b0, end) of the step line in windows of up to 32 steps. Keeps the
-// current and the next window (block ids in one VGPR each); the next one is made as soon as
-// the current one starts, so its table load has a whole window of time.
+// Describes the steps of one worker's range [b0, end) in order. next() returns the current
+// step's description -- with its physical block ids fetched by scalar loads from the table row
+// (raw: they are checked where they are used, so the loads' latency is hidden) -- and moves the
+// cursor on; past the end of the range it keeps describing the last step. A step whose tokens
+// all sit in its first block (block size 16) gets that block for its second half too: the
+// masked loads then re-read lines the first half fetches.
 template <int B>
-struct Walker {
-  struct Win {
-    int64_t start;   // first line step
-    int len;         // steps (1..32)
-    int i0;          // stream index of the first step
-    int tbl;         // per-lane block ids
-    __device__ int end() const { return i0 + len; }
-  };
-
+struct StepStream {
   const int64_t* sm_prefix;
   const int32_t* sm_len;
-  const int32_t* tables;
-  int S, Hkv, max_blocks, num_blocks, lane, w;
-  int64_t b0, next, end;   // the range and the first step not yet in a window
-  Win cw, nw;
-  bool nw_valid;
-  Cursor cur;              // load-side position
+  ctable_t tables;
+  int S, Hkv, max_blocks, num_blocks, w;
+  int64_t b0, end, j;   // the range and the line index of the next step to describe
+  Cursor c;             // position of step j
 
-  __device__ bool make_window(Win& x, int i0) {
-    if (next >= end) return false;
-    x.start = next;
-    x.len = (int)min((int64_t)32, end - next);
-    next += x.len;
-    x.i0 = i0;
-    x.tbl = window_blocks<B>(sm_prefix, sm_len, tables, S, Hkv, max_blocks, num_blocks,
-                             x.start, x.start + x.len, lane);
-    return true;
-  }
-
-  // Returns false when the range is empty.
-  __device__ bool init(int64_t range_b0, int64_t range_end) {
+  __device__ void init(int64_t range_b0, int64_t range_end) {
     b0 = range_b0;
     end = range_end;
-    next = b0;
-    if (!make_window(cw, 0)) return false;
-    nw_valid = make_window(nw, cw.end());
-    cur = cursor_at(sm_prefix, sm_len, S, Hkv, b0);
-    return true;
+    j = b0;
+    if (j < end) c = cursor_at(sm_prefix, sm_len, S, Hkv, j);
   }
 
-  __device__ bool has(int i) const { return i < cw.end() || (nw_valid && i < nw.end()); }
-
-  // Compute side reached stream step i (has(i) is true): retire the current window when i
-  // leaves it and start the table load of the one after.
-  __device__ void advance(int i) {
-    if (i >= cw.end()) {
-      cw = nw;
-      nw_valid = make_window(nw, cw.end());
-    }
-  }
-
-  // Description of stream step i for its loads; steps must be requested in order 0, 1, 2, ...
-  __device__ StepInfo load_info(int i) {
-    if (i != 0) cursor_next(cur, sm_prefix, sm_len, S, Hkv);
+  __device__ StepInfo next() {
     StepInfo si;
-    si.s = cur.s;
-    si.g = cur.g;
-    si.k = cur.k;
-    si.ns = cur.ns;
-    si.L = cur.L;
-    if (i < cw.end()) {
-      const int j = i - cw.i0;
-      si.b0 = __builtin_amdgcn_readlane(cw.tbl, j);
-      si.b1 = B == 16 ? __builtin_amdgcn_readlane(cw.tbl, j + 32) : si.b0;
+    si.s = c.s;
+    si.g = c.g;
+    si.k = c.k;
+    si.ns = c.ns;
+    si.L = c.L;
+    const ctable_t row = tables + (size_t)c.s * max_blocks;
+    const int jb0 = B == 16 ? 2 * c.k : c.k;
+    si.b0 = row[jb0];
+    if (B == 16) {
+      const int jb1 = jb0 + 1 < ceil_div(c.L, B) ? jb0 + 1 : jb0;
+      si.b1 = row[jb1];
     } else {
-      const int j = i - nw.i0;
-      si.b0 = __builtin_amdgcn_readlane(nw.tbl, j);
-      si.b1 = B == 16 ? __builtin_amdgcn_readlane(nw.tbl, j + 32) : si.b0;
+      si.b1 = si.b0;
     }
     si.range = w;
-    si.rfirst = i == 0;
-    si.rlast = b0 + i == end - 1;
+    si.rfirst = j == b0;
+    si.rlast = j == end - 1;
+    ++j;
+    if (j < end) cursor_next(c, sm_prefix, sm_len, S, Hkv);
     return si;
   }
 };
