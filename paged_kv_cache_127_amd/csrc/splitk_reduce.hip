@@ -5,48 +5,59 @@
 // (m is kept in the log2 domain). Segments of empty sequences get a zero row here; segments
 // that one range finished were written by the decode kernel and are skipped.
 //
-// One workgroup per segment, one thread per few output elements. The slots of the segment
-// follow from the schedule arithmetic alone; each thread loads (m, l, acc) of four slots at a
-// time with independent loads and folds them into a running (max, numerator, denominator), so
-// a segment costs one round trip for the prefixes and one per four partials.
+// One wavefront per segment, four per workgroup. The slots of a segment follow from the
+// schedule arithmetic alone; lane l holds f32x4 chunks l, l + 64, ... of the segment's G rows
+// (contiguous in a slot and in the output), loads (m, l, acc) of two slots at a time with
+// independent loads and folds them into a running (max, numerator, denominator): a segment
+// costs one round trip for the prefixes and one per two partials.
 #include "device_common.h"
 #include "kernels.h"
 #include "schedule.h"
 
 namespace pkv {
 
-constexpr int kMergeBatch = 4;
+constexpr int kMergeBatch = 2;
 
-template <int D, typename T>
+// KMAX = ceil(G * D / 256): f32x4 chunks per lane (G rows of D floats over 64 lanes).
+template <int D, typename T, int KMAX>
 __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
+  const int lane = threadIdx.x & 63;
   const int Hkv = p.num_kv_heads;
-  const int seg = blockIdx.x;
+  const int seg = blockIdx.x * 4 + uni((int)(threadIdx.x >> 6));
+  if (seg >= p.num_seqs * Hkv) return;
   const int s = seg / Hkv;
   const int g = seg - s * Hkv;
   const int G = p.num_q_heads / Hkv;
-  const int64_t ns = p.prefix[s + 1] - p.prefix[s];
-  const size_t row0 = (size_t)s * p.num_q_heads + (size_t)g * G;
-  const int t = threadIdx.x;
-  constexpr int kPer = (16 * D + 255) / 256;   // elements per thread at the largest group (16)
+  const int n4 = G * D / 4;                          // f32x4 chunks of the segment's rows
+  const int64_t ns = uni(p.prefix[s + 1]) - uni(p.prefix[s]);
+  const size_t base = ((size_t)s * p.num_q_heads + (size_t)g * G) * D;
 
-  auto store = [&](int e, float o) {
-    const size_t idx = row0 * D + e;
+  auto store = [&](int e4, f32x4 o) {
     if (p.out_f32) {
-      reinterpret_cast<float*>(p.out)[idx] = o;
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + base + 4 * e4) = o;
     } else {
-      if constexpr (sizeof(T) == 2) reinterpret_cast<uint16_t*>(p.out)[idx] = Elem<T>::from_f32(o);
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t w0 = (uint32_t)Elem<T>::from_f32(o[0]) |
+                            ((uint32_t)Elem<T>::from_f32(o[1]) << 16);
+        const uint32_t w1 = (uint32_t)Elem<T>::from_f32(o[2]) |
+                            ((uint32_t)Elem<T>::from_f32(o[3]) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + base + 4 * e4) =
+            make_uint2(w0, w1);
+      }
     }
   };
 
   if (ns == 0) {
-    for (int e = t; e < G * D; e += blockDim.x) store(e, 0.f);
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+      if (lane + 64 * k < n4) store(lane + 64 * k, f32x4{0.f, 0.f, 0.f, 0.f});
     return;
   }
   const Line line = Line::make(p.prefix, p.wprefix, p.num_seqs, Hkv, p.piece_weight,
                                p.num_workers);
   const int64_t seg_w = kStepWeight * ns + line.pw;
-  const int64_t ws0 = (int64_t)Hkv * p.wprefix[s] + g * seg_w;   // weighted segment start
-  const int64_t first = ws0 + line.pw;                            // weighted start of step 0
+  const int64_t ws0 = (int64_t)Hkv * uni(p.wprefix[s]) + g * seg_w;   // weighted segment start
+  const int64_t first = ws0 + line.pw;                                 // weighted start of step 0
   const int rf = line.owner(first);
   const int rl = line.owner(first + kStepWeight * (ns - 1));
   if (rf == rl) return;   // one worker wrote the whole segment
@@ -54,16 +65,19 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
   // step, which starts at ws0 - kStepWeight
   const int64_t first_slot = 2 * (int64_t)rf + (line.wbegin(rf) > ws0 - kStepWeight ? 0 : 1);
 
-  float M[kPer], num[kPer], den[kPer];
+  float M[KMAX], den[KMAX];
+  f32x4 num[KMAX];
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    M[q] = kNegInf;
-    num[q] = 0.f;
-    den[q] = 0.f;
+  for (int k = 0; k < KMAX; ++k) {
+    M[k] = kNegInf;
+    den[k] = 0.f;
+    num[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const f32x4* acc4 = reinterpret_cast<const f32x4*>(p.ws_acc);
   // Workers rf+1 .. rl start inside the segment: their first piece (slot 2r) belongs to it if
   // they hold any of its steps.
   int64_t before_r = line.in_segment_before(line.wbegin(rf + 1), ws0, ns);
+#pragma unroll 1
   for (int r0 = rf; r0 <= rl; r0 += kMergeBatch) {
     int64_t slot[kMergeBatch];
 #pragma unroll
@@ -78,57 +92,76 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
         before_r = after_r;
       }
     }
-    float mj[kMergeBatch][kPer], lj[kMergeBatch][kPer], aj[kMergeBatch][kPer];
+    float mj[kMergeBatch][KMAX], lj[kMergeBatch][KMAX];
+    f32x4 aj[kMergeBatch][KMAX];
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j)
 #pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const int e = t + 256 * q;
-        mj[j][q] = kNegInf;
-        lj[j][q] = 0.f;
-        aj[j][q] = 0.f;
-        if (slot[j] >= 0 && e < G * D) {
-          const int64_t pr = slot[j] * G + e / D;
-          mj[j][q] = p.ws_m[pr];
-          lj[j][q] = p.ws_l[pr];
-          aj[j][q] = p.ws_acc[pr * D + (e % D)];
+      for (int k = 0; k < KMAX; ++k) {
+        const int e4 = lane + 64 * k;
+        mj[j][k] = kNegInf;
+        lj[j][k] = 0.f;
+        aj[j][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (slot[j] >= 0 && e4 < n4) {
+          const int64_t pr = slot[j] * G + (4 * e4) / D;
+          mj[j][k] = p.ws_m[pr];
+          lj[j][k] = p.ws_l[pr];
+          aj[j][k] = acc4[slot[j] * n4 + e4];
         }
       }
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j)
 #pragma unroll
-      for (int q = 0; q < kPer; ++q) {
+      for (int k = 0; k < KMAX; ++k) {
         if (slot[j] < 0) continue;
-        const float m_new = fmaxf(M[q], mj[j][q]);
+        const float m_new = fmaxf(M[k], mj[j][k]);
         if (m_new == kNegInf) continue;
-        const float a_old = fast_exp2(M[q] - m_new);
-        const float a_new = fast_exp2(mj[j][q] - m_new);
-        num[q] = num[q] * a_old + a_new * aj[j][q];
-        den[q] = den[q] * a_old + a_new * lj[j][q];
-        M[q] = m_new;
+        const float a_old = fast_exp2(M[k] - m_new);
+        const float a_new = fast_exp2(mj[j][k] - m_new);
+        num[k] = num[k] * a_old + aj[j][k] * a_new;
+        den[k] = den[k] * a_old + lj[j][k] * a_new;
+        M[k] = m_new;
       }
   }
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    const int e = t + 256 * q;
-    if (e < G * D) store(e, den[q] == 0.f ? 0.f : num[q] / den[q]);
+  for (int k = 0; k < KMAX; ++k) {
+    const int e4 = lane + 64 * k;
+    if (e4 < n4) {
+      const float inv = den[k] == 0.f ? 0.f : 1.0f / den[k];
+      store(e4, num[k] * inv);
+    }
   }
+}
+
+template <int D, typename T>
+static void launch_merge_t(const DecodeParams& p, unsigned grid, hipStream_t st) {
+  const int chunks = (p.num_q_heads / p.num_kv_heads * D / 4 + 63) / 64;
+  if (chunks <= 1)
+    hipLaunchKernelGGL((splitk_merge<D, T, 1>), dim3(grid), dim3(256), 0, st, p);
+  else if (chunks <= 2)
+    hipLaunchKernelGGL((splitk_merge<D, T, 2>), dim3(grid), dim3(256), 0, st, p);
+  else if (chunks <= 4)
+    hipLaunchKernelGGL((splitk_merge<D, T, 4>), dim3(grid), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((splitk_merge<D, T, 8>), dim3(grid), dim3(256), 0, st, p);
 }
 
 hipError_t launch_splitk_reduce(const DecodeParams& p, int kv_dtype, int head_dim,
                                 hipStream_t st) {
-  const int64_t grid = (int64_t)p.num_seqs * p.num_kv_heads;
-  if (grid <= 0) return hipSuccess;
-#define PKV_RED(D, T) \
-  hipLaunchKernelGGL((splitk_merge<D, T>), dim3((unsigned)grid), dim3(256), 0, st, p)
+  const int64_t segs = (int64_t)p.num_seqs * p.num_kv_heads;
+  if (segs <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)((segs + 3) / 4);
   if (head_dim == 64) {
-    if (kv_dtype == 1) PKV_RED(64, f16_t); else if (kv_dtype == 2) PKV_RED(64, bf16_t); else PKV_RED(64, float);
+    if (kv_dtype == 1) launch_merge_t<64, f16_t>(p, grid, st);
+    else if (kv_dtype == 2) launch_merge_t<64, bf16_t>(p, grid, st);
+    else launch_merge_t<64, float>(p, grid, st);
   } else if (head_dim == 128) {
-    if (kv_dtype == 1) PKV_RED(128, f16_t); else if (kv_dtype == 2) PKV_RED(128, bf16_t); else PKV_RED(128, float);
+    if (kv_dtype == 1) launch_merge_t<128, f16_t>(p, grid, st);
+    else if (kv_dtype == 2) launch_merge_t<128, bf16_t>(p, grid, st);
+    else launch_merge_t<128, float>(p, grid, st);
   } else {
     return hipErrorInvalidValue;
   }
-#undef PKV_RED
   return hipGetLastError();
 }
 

@@ -331,6 +331,29 @@ def test_append_scatter_bit_exact(dt, B):
     assert torch.equal(bits(db.v_pool.cpu()), bits(vr))
 
 
+@pytest.mark.parametrize("dt,d,B,n", [("bf16", 128, 16, 300), ("f32", 128, 32, 150),
+                                      ("f16", 64, 16, 1500)])
+def test_append_many_tokens_bit_exact(dt, d, B, n):
+    """Many tokens per call, several in the same blocks, up to 1500 in one call."""
+    b = W.small_batch([500, 700, 333, 480], 8, 2, d, B, DT[dt], seed=57, pool_factor=1.5)
+    db = DeviceBatch(b)
+    rng = np.random.default_rng(1)
+    cand = [(s, p) for s in range(4) for p in range(-(-int(b.lengths[s]) // B) * B)]
+    pick = [cand[i] for i in rng.choice(len(cand), size=n, replace=False)]
+    k_new, v_new = W.new_tokens(b.seed, 10, n, 2, d, DT[dt])
+    kr, vr = b.k_pool.clone(), b.v_pool.clone()
+    for i, (s, p) in enumerate(pick):
+        blk, off = oracle.token_address(p, b.tables[s], B)
+        kr[blk, :, off] = k_new[i]
+        vr[blk, :, :, off] = v_new[i]
+    as_dev = lambda x: torch.tensor(x, dtype=torch.int32, device="cuda")
+    pkv.kv_cache_append(db.k_pool, db.v_pool, k_new.cuda(), v_new.cuda(),
+                        as_dev([s for s, _ in pick]), as_dev([p for _, p in pick]), db.tables)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(db.k_pool.cpu()), bits(kr))
+    assert torch.equal(bits(db.v_pool.cpu()), bits(vr))
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("B", [16, 32])
 def test_cow_copy_bit_exact(dt, B):
