@@ -190,11 +190,13 @@ int pkv_seq_fork(pkv_pool* pool, const int32_t* src_row, int32_t* dst_row, int n
 int pkv_seq_release(pkv_pool* pool, const int32_t* table_row, int num_blocks_used);
 
 /* ---------------------------------------------------------------------------------------
- * Kernel timing (for tests and benchmarks). While enabled, every kernel this library
- * launches is bracketed by a pair of hipEvents recorded on its launch stream.
- * pkv_timing_query waits for the recorded events of kernels whose name contains `name`
- * ("decode_partial", "splitk_reduce", "append", "cow", or "" for all) and returns their
- * summed duration and launch count. Enabling clears earlier records.
+ * Kernel timing (for tests and benchmarks). pkv_timing_enable(k) with k > 0 brackets every
+ * k-th launch of each kernel this library launches by a pair of hipEvents recorded on its
+ * launch stream (k = 1: every launch; a larger k keeps the events' own cost out of most
+ * launches); k = 0 switches timing off. pkv_timing_query waits for the recorded events of
+ * kernels whose name contains `name` ("decode_partial", "splitk_reduce", "append", "cow", or
+ * "" for all) and returns their summed duration and the number of timed launches. Enabling
+ * clears earlier records.
  * --------------------------------------------------------------------------------------- */
 int pkv_timing_enable(int on);
 int pkv_timing_query(const char* name, double* total_ms, int64_t* launches);

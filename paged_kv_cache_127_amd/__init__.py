@@ -215,8 +215,10 @@ def set_validate(on: bool = True):
     _check(load_library().pkv_set_validate(1 if on else 0))
 
 
-def timing_enable(on: bool = True):
-    _check(load_library().pkv_timing_enable(1 if on else 0))
+def timing_enable(on=True, every: int = 1):
+    """Time every ``every``-th launch of each library kernel (C: ``pkv_timing_enable``);
+    ``on=False`` switches timing off."""
+    _check(load_library().pkv_timing_enable(max(1, int(every)) if on else 0))
 
 
 def timing_query(name: str = ""):

@@ -63,6 +63,8 @@ struct TimingRec {
 };
 std::mutex g_tmu;
 bool g_timing = false;
+int g_timing_every = 1;                       // time every k-th launch of each kernel
+std::vector<std::pair<const char*, int64_t>> g_seen;   // launches per kernel name
 std::vector<TimingRec> g_recs;
 std::vector<hipEvent_t> g_spare;
 
@@ -81,6 +83,17 @@ template <class F>
 hipError_t timed(const char* name, hipStream_t st, F&& launch) {
   std::unique_lock<std::mutex> lk(g_tmu);
   if (!g_timing) {
+    lk.unlock();
+    return launch();
+  }
+  int64_t* seen = nullptr;
+  for (auto& x : g_seen)
+    if (x.first == name) seen = &x.second;
+  if (!seen) {
+    g_seen.push_back({name, 0});
+    seen = &g_seen.back().second;
+  }
+  if ((*seen)++ % g_timing_every != 0) {
     lk.unlock();
     return launch();
   }
@@ -394,7 +407,9 @@ int pkv_timing_enable(int on) {
     g_spare.push_back(r.stop);
   }
   g_recs.clear();
-  g_timing = on != 0;
+  g_seen.clear();
+  g_timing = on > 0;
+  g_timing_every = on > 0 ? on : 1;
   return ok();
 }
 
