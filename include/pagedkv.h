@@ -33,7 +33,7 @@
  *
  * Cache layout (the pages leave it to the kernel, [P1] "Block size is a kernel choice too"):
  *   k_pool  [num_blocks][num_kv_heads][block_size][head_dim]   key rows of a block
- *   v_pool  [num_blocks][num_kv_heads][head_dim][block_size]   values, transposed in a block
+ *   v_pool  [num_blocks][num_kv_heads][block_size][head_dim]   value rows, same order
  *   Both pools hold one layer and share the element type `kv_dtype`.
  * Token p of sequence s sits in physical block block_tables[s][p / block_size] at offset
  * p % block_size ([P1] "A block table preserves token order"; [P2] "Block Table and
@@ -127,7 +127,7 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
  * head per generated token). For every i < num_tokens and KV head g:
  *   slot = (block_tables[seq_ids[i]][positions[i] / block_size], positions[i] % block_size)
  *   k_pool[slot.block][g][slot.offset][:] = k_new[i][g][:]
- *   v_pool[slot.block][g][:][slot.offset] = v_new[i][g][:]
+ *   v_pool[slot.block][g][slot.offset][:] = v_new[i][g][:]
  * The caller has already grown the table (and made shared blocks private, see
  * cow_block_copy). Slots must be distinct; a bitwise copy, no rounding.
  *   k_new, v_new  device [num_tokens][num_kv_heads][head_dim], element type kv_dtype

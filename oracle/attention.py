@@ -20,7 +20,7 @@ Readings where the pages leave a step open:
   * GQA head mapping: query head h reads KV head h div G, G = H_q / H_kv (contiguous groups).
   * scale defaults to 1/sqrt(head_dim).
   * An empty context (L = 0) yields a zero output.
-Layout (the pages leave it to the kernel): k_pool [N][H_kv][B][d], v_pool [N][H_kv][d][B].
+Layout (the pages leave it to the kernel): k_pool and v_pool both [N][H_kv][B][d].
 """
 from __future__ import annotations
 
@@ -72,14 +72,7 @@ def gather_kv(k_pool, v_pool, table_row, length: int, kv_head: int, block_size: 
     offset = pos % block_size
     phys = np.asarray(table_row, dtype=np.int64)[logical_block]
     K = _index(k_pool, phys, kv_head, offset)
-    # values sit transposed inside a block ([d][B]); viewed as [B][d] they index like keys
-    try:
-        import torch
-        v_rows = v_pool.transpose(2, 3) if isinstance(v_pool, torch.Tensor) \
-            else np.swapaxes(v_pool, 2, 3)
-    except ImportError:  # pragma: no cover
-        v_rows = np.swapaxes(v_pool, 2, 3)
-    V = _index(v_rows, phys, kv_head, offset)
+    V = _index(v_pool, phys, kv_head, offset)
     return K, V
 
 

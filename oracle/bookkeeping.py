@@ -112,7 +112,7 @@ class BlockPool:
 class PagedKVModel:
     """Pools of raw K/V values plus per-sequence tables and lengths.
 
-    ``k_pool`` is ``[N][H_kv][B][d]`` and ``v_pool`` ``[N][H_kv][d][B]`` (numpy arrays of any
+    ``k_pool`` and ``v_pool`` are ``[N][H_kv][B][d]`` (numpy arrays of any
     dtype; values are only copied, never combined).
     """
 
@@ -168,7 +168,7 @@ class PagedKVModel:
             if self.pool.refcount(old) > 1:
                 new = self.pool.claim(claim) if claim is not None else self.pool.alloc()
                 self.k[new, :, :r, :] = self.k[old, :, :r, :]
-                self.v[new, :, :, :r] = self.v[old, :, :, :r]
+                self.v[new, :, :r, :] = self.v[old, :, :r, :]
                 table[j] = new
                 self.pool.decref(old)
                 self.copies.append((old, new, r))
@@ -178,7 +178,7 @@ class PagedKVModel:
         """Store one token's K and V rows (``[H_kv][d]`` each) after the last stored token."""
         blk, r = self.prepare_write(s, claim)
         self.k[blk, :, r, :] = k_row
-        self.v[blk, :, :, r] = v_row
+        self.v[blk, :, r, :] = v_row
         self.lengths[s] += 1
         return blk, r
 

@@ -150,16 +150,16 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
                       num_workers: int = 0, workspace: Optional[torch.Tensor] = None,
                       stream=None) -> torch.Tensor:
     """out[s][h] = softmax(q[s][h] . K_s^T * scale) . V_s over the paged cache (C:
-    ``paged_attn_decode``). Shapes: q, out [S][H_q][d]; k_pool [N][H_kv][B][d];
-    v_pool [N][H_kv][d][B]; block_tables int32 [S][max_blocks]; context_lens int32 [S]."""
+    ``paged_attn_decode``). Shapes: q, out [S][H_q][d]; k_pool, v_pool [N][H_kv][B][d];
+    block_tables int32 [S][max_blocks]; context_lens int32 [S]."""
     L = load_library()
     kdt = _kv_dtype(k_pool)
     if q.dim() != 3 or k_pool.dim() != 4 or v_pool.dim() != 4 or out.shape != q.shape:
         raise ValueError("bad tensor ranks or out shape")
     S, Hq, d = q.shape
     N, Hkv, B, d2 = k_pool.shape
-    if d2 != d or tuple(v_pool.shape) != (N, Hkv, d, B):
-        raise ValueError("k_pool must be [N][H_kv][B][d] and v_pool [N][H_kv][d][B]")
+    if d2 != d or tuple(v_pool.shape) != (N, Hkv, B, d):
+        raise ValueError("k_pool and v_pool must both be [N][H_kv][B][d]")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
         raise ValueError("block_tables must be [S][max_blocks] and context_lens [S]")
     if out.dtype not in (torch.float32, k_pool.dtype):
@@ -182,6 +182,8 @@ def kv_cache_append(k_pool, v_pool, k_new, v_new, seq_ids, positions, block_tabl
     """Store K/V rows of new tokens ([n][H_kv][d]) at their slots (C: ``kv_cache_append``)."""
     L = load_library()
     N, Hkv, B, d = k_pool.shape
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool must both be [N][H_kv][B][d]")
     n = int(k_new.shape[0])
     if tuple(k_new.shape) != (n, Hkv, d) or tuple(v_new.shape) != (n, Hkv, d):
         raise ValueError("k_new/v_new must be [n][H_kv][d]")
@@ -200,6 +202,8 @@ def cow_block_copy(k_pool, v_pool, src_blocks, dst_blocks, num_tokens=None, stre
     ``cow_block_copy``). ``num_tokens`` None copies whole blocks."""
     L = load_library()
     N, Hkv, B, d = k_pool.shape
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool must both be [N][H_kv][B][d]")
     n = int(src_blocks.shape[0])
     if tuple(dst_blocks.shape) != (n,) or (num_tokens is not None and tuple(num_tokens.shape) != (n,)):
         raise ValueError("src/dst/num_tokens must be [num_pairs]")

@@ -291,7 +291,7 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim);
   p.scale_log2 = sc * 1.4426950408889634f;
   p.piece_weight = pw;
-  p.ring_cap = pkv::ring_capacity(G, head_dim);
+  p.ring_cap = pkv::ring_capacity(num_seqs, G, head_dim, waves);
   char* ws = reinterpret_cast<char*>(workspace);
   p.wprefix = reinterpret_cast<int64_t*>(ws + wl.wprefix);
   p.ws_acc = reinterpret_cast<float*>(ws + wl.acc);

@@ -13,18 +13,21 @@
 
 namespace pkv {
 
+// One thread per E-sized unit of a new row (E = 16 bytes when every pointer allows it, else
+// the element). Keys and values share the layout, so row (i, g) of k_new / v_new lands in one
+// contiguous row of its block: the writes of a token are whole cache lines.
 template <typename E>
-__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
-  const int D = p.head_dim, B = p.block_size, H = p.num_kv_heads;
-  const int64_t total = (int64_t)p.num_tokens * H * D;
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p, int units_per_row) {
+  const int U = units_per_row, B = p.block_size, H = p.num_kv_heads;
+  const int64_t total = (int64_t)p.num_tokens * H * U;
   E* kp = reinterpret_cast<E*>(p.k_pool);
   E* vp = reinterpret_cast<E*>(p.v_pool);
   const E* kn = reinterpret_cast<const E*>(p.k_new);
   const E* vn = reinterpret_cast<const E*>(p.v_new);
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
-    const int d = (int)(idx % D);
-    const int64_t t = idx / D;
+    const int u = (int)(idx % U);
+    const int64_t t = idx / U;
     const int g = (int)(t % H);
     const int i = (int)(t / H);
     const int s = p.seq_ids[i];
@@ -35,9 +38,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     const int blk = p.tables[(size_t)s * p.max_blocks + j];
     if ((unsigned)blk >= (unsigned)p.num_blocks) continue;
     const int off = pos - j * B;
-    const size_t hb = (size_t)blk * H + g;
-    kp[(hb * B + off) * D + d] = kn[idx];
-    vp[(hb * D + d) * B + off] = vn[idx];
+    const size_t row = ((size_t)blk * H + g) * B + off;
+    kp[row * U + u] = kn[idx];
+    vp[row * U + u] = vn[idx];
   }
 }
 
@@ -56,24 +59,30 @@ __global__ __launch_bounds__(256) void cow_kernel(CowParams p) {
   E* vp = reinterpret_cast<E*>(p.v_pool);
   const size_t sb = ((size_t)src * H + g) * B * D;
   const size_t db = ((size_t)dst * H + g) * B * D;
-  // keys: rows [0, n) are contiguous
-  for (int e = threadIdx.x; e < n * D; e += blockDim.x) kp[db + e] = kp[sb + e];
-  // values: head-dim row r holds its B slots contiguously; copy the first n of each row
+  // slots [0, n) are the first n rows of the (block, head) tile, keys and values alike
   for (int e = threadIdx.x; e < n * D; e += blockDim.x) {
-    const int r = e / n, t = e - r * n;
-    vp[db + (size_t)r * B + t] = vp[sb + (size_t)r * B + t];
+    kp[db + e] = kp[sb + e];
+    vp[db + e] = vp[sb + e];
   }
 }
 
 hipError_t launch_append(const AppendParams& p, int elem_bytes, hipStream_t st) {
-  const int64_t total = (int64_t)p.num_tokens * p.num_kv_heads * p.head_dim;
+  const int row_bytes = p.head_dim * elem_bytes;
+  const bool wide = row_bytes % 16 == 0 &&
+                    ((reinterpret_cast<uintptr_t>(p.k_pool) | reinterpret_cast<uintptr_t>(p.v_pool) |
+                      reinterpret_cast<uintptr_t>(p.k_new) | reinterpret_cast<uintptr_t>(p.v_new)) &
+                     15) == 0;
+  const int units = wide ? row_bytes / 16 : p.head_dim;
+  const int64_t total = (int64_t)p.num_tokens * p.num_kv_heads * units;
   if (total <= 0) return hipSuccess;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  if (elem_bytes == 4)
-    hipLaunchKernelGGL(append_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, st, p);
+  if (wide)
+    hipLaunchKernelGGL(append_kernel<u32x4>, dim3((unsigned)blocks), dim3(256), 0, st, p, units);
+  else if (elem_bytes == 4)
+    hipLaunchKernelGGL(append_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, st, p, units);
   else
-    hipLaunchKernelGGL(append_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(append_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st, p, units);
   return hipGetLastError();
 }
 

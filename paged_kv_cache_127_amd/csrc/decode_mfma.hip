@@ -8,15 +8,20 @@
 // contiguous copy). Whole segments are normalised and written to the output; split pieces
 // write partial states that the merge kernel combines.
 //
-// Per 32-token step a wavefront issues (per lane) 8 + 8 16-byte loads:
+// Per 32-token step (D = 128) a wavefront issues (per lane) 8 + 8 16-byte loads:
 //   K operand, sub-tile a (0/1), d-chunk c: key row tau(a, i) = 8*(i/4) + 4a + i%4 of the
 //     step, i = lane%16, head-dim slice [32c + 8*(lane/16), +8).
-//   V operand, d-chunk f: value row d = 16f + lane%16 (values are stored [d][B] inside a
-//     block), tokens 8*(lane/16) .. +8 of the step -- one contiguous 16-byte run.
+//   V rows, instruction f: value row 4f + lane/16 of the step, head-dim slice
+//     [8*(lane%16), +8) -- four whole 256-byte rows per instruction.
 // Scores S^T[token][head] = K . Q^T come out of v_mfma_f32_16x16x32 with lane l holding head
-// l%16 and tokens 8*(l/16) + 4a + e (e = 0..3) -- exactly the 8 consecutive tokens whose
-// values the same lane loaded, so the probabilities feed the P.V MFMA
-// (O^T[d][head] += V^T . P^T) as its B operand without any data exchange.
+// l%16 and tokens 8*(l/16) + 4a + e (e = 0..3), i.e. 8 consecutive tokens, which is the B
+// operand layout of the P.V MFMA (O^T[d][head] += V^T . P^T): the probabilities need no data
+// exchange. Its A operand wants, per lane, those 8 tokens of one head-dim column: the value
+// rows go through a per-wavefront LDS tile (32-byte pieces XOR-swizzled by row so that both
+// the row writes and the column reads spread over the banks) and come back transposed with
+// ds_read_b64_tr_b16 (in each 16-lane group, lane i receives element i%4 of the 4 x 16-bit
+// words that lanes 4k + i/4 address, k = 0..3: lanes 4k + c address token row k, head-dim
+// columns 4c .. 4c + 3 of the 16-column chunk).
 // Probabilities are split into a 16-bit high part and a 16-bit remainder (two MFMAs), which
 // keeps P.V at close to fp32 accuracy. Scores and the online softmax stay in fp32; the scale
 // (times log2 e) is applied to the fp32 scores and exp2 is used throughout.
@@ -41,9 +46,34 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 template <int D>
 struct StepRegs {
   u32x4 k[2][D / 32];   // K operand per sub-tile and d-chunk
-  u32x4 v[D / 16];      // V operand per d-chunk
+  u32x4 v[D / 16];      // value rows, 16 bytes per lane per instruction
   u32x4 q[D / 32];      // Q operand (the step's query rows)
 };
+
+// Swizzle of the 32-byte pieces of value row t in the LDS tile (D / 16 pieces per row): the 16
+// rows one transposed read touches (t = 8q + 4h + 0..3, q = 0..3) land on distinct piece
+// positions in every 256-byte bank window.
+template <int D>
+__device__ __forceinline__ int piece_swizzle(int t) {
+  if constexpr (D == 128) return (t & 3) | (((t >> 3) & 1) << 2);
+  else return ((t >> 1) & 1) | (((t >> 3) & 1) << 1);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Four 16-bit elements, transposed across each 16-lane group (ds_read_b64_tr_b16).
+__device__ __forceinline__ uint2 lds_read_tr16(const char* lds_byte_addr) {
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)(__attribute__((address_space(3))) char*)lds_byte_addr);
+  return __builtin_bit_cast(uint2, r);
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // Split two fp32 probabilities into packed 16-bit high parts and remainders.
 template <typename T>
@@ -118,7 +148,11 @@ void decode_mfma(DecodeParams p) {
   // per-lane byte offsets inside a (block, head) tile
   const int kofs0 = ((tokA0 & (B - 1)) * D + 8 * jg) * ES;
   const int kofs1 = (((tokA0 + 4) & (B - 1)) * D + 8 * jg) * ES;
-  const int vofs = (r16 * B + (vtok & (B - 1))) * ES;
+  constexpr int VLPR = D / 8;           // lanes per value row (16 bytes each)
+  constexpr int VTPI = 64 / VLPR;       // value rows per load instruction
+  constexpr int RB = D * ES;            // bytes per value row
+  const int vrow = lane / VLPR;
+  const int vch = lane % VLPR;
 
   // Output ring (dynamic LDS after the schedule arrays): piece results are staged here and
   // written to memory only when the ring is full or the range is done. A vector store that is
@@ -128,9 +162,24 @@ void decode_mfma(DecodeParams p) {
   // destination element offset and (slot << 2 | kind).
   const int R = p.ring_cap;
   const int EF = G * D + 2 * G;
-  char* ring = reinterpret_cast<char*>(smem) + ring_offset(S) +
+  char* ring = reinterpret_cast<char*>(smem) + ring_offset(S) + (size_t)W * 32 * RB +
                (size_t)wave * R * (16 + (size_t)EF * 4);
   int64_t* rhdr = reinterpret_cast<int64_t*>(ring);
+  // value staging tile of this wavefront (before the rings), and the per-lane byte offsets of
+  // its row writes (instruction f) and transposed reads (token half hh, piece f: XOR f << 5)
+  char* vstage = reinterpret_cast<char*>(smem) + ring_offset(S) + (size_t)wave * 32 * RB;
+  int vw_ofs[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int t = VTPI * f + vrow;
+    vw_ofs[f] = t * RB + (((vch >> 1) ^ piece_swizzle<D>(t)) << 5) + 16 * (vch & 1);
+  }
+  int vr_ofs[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int t = 8 * jg + 4 * hh + (r16 >> 2);
+    vr_ofs[hh] = t * RB + (piece_swizzle<D>(t) << 5) + 8 * (r16 & 3);
+  }
   float* rdat = reinterpret_cast<float*>(ring + (size_t)R * 16);
   int ring_n = 0;
   float m_run = kNegInf, l_run = 0.f;
@@ -165,18 +214,19 @@ void decode_mfma(DecodeParams p) {
       r.k[0][c] = load16(ka + kofs0 + 32 * c * ES);
       r.k[1][c] = load16(kb + kofs1 + 32 * c * ES);
     }
-    const char* vt = vbase + ((size_t)((B == 16 && vtok >= 16) ? b1 : b0) * Hkv + si.g) *
-                                 kv_block_stride + vofs;
 #pragma unroll
-    for (int f = 0; f < NF; ++f) r.v[f] = load16(vt + (size_t)16 * f * B * ES);
+    for (int f = 0; f < NF; ++f) {
+      const int t = VTPI * f + vrow;
+      const int blk = (B == 16 && t >= 16) ? b1 : b0;
+      r.v[f] = load16(vbase + ((size_t)blk * Hkv + si.g) * kv_block_stride +
+                      (size_t)(t & (B - 1)) * RB + 16 * vch);
+    }
   };
 
   // Write the staged piece results: every store instruction covers 1 KB of contiguous memory
   // (the G rows of one (sequence, KV head) are adjacent in the output and in a partial slot).
   auto flush = [&](bool drain) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_lds_sync();
     const int n4 = G * D / 4;
     for (int e = 0; e < ring_n; ++e) {
       const float* so = rdat + (size_t)e * EF;
@@ -213,9 +263,7 @@ void decode_mfma(DecodeParams p) {
     // pending when the next vector-load wait comes; the s_waitcnt immediate is vmcnt(0) with
     // the other counters left free.
     if (drain) __builtin_amdgcn_s_waitcnt(0x0F70);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_lds_sync();
   };
 
   // Start of a step: open a new piece.
@@ -241,6 +289,19 @@ void decode_mfma(DecodeParams p) {
       sacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) sacc[a] = mfma16x16x32<T>(r.k[a][c], r.q[c], sacc[a]);
+    }
+    // value rows into the LDS tile, then back as A operands (head-dim column 16f + lane%16,
+    // tokens 8*(lane/16) .. +8 of the step)
+    wave_lds_sync();   // the previous step's transposed reads come first
+#pragma unroll
+    for (int f = 0; f < NF; ++f) *reinterpret_cast<u32x4*>(vstage + vw_ofs[f]) = r.v[f];
+    wave_lds_sync();
+    u32x4 va[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const uint2 lo = lds_read_tr16(vstage + (vr_ofs[0] ^ (f << 5)));
+      const uint2 hi = lds_read_tr16(vstage + (vr_ofs[1] ^ (f << 5)));
+      va[f] = u32x4{lo.x, lo.y, hi.x, hi.y};
     }
     float z[8];
 #pragma unroll
@@ -284,12 +345,12 @@ void decode_mfma(DecodeParams p) {
       for (int u = 0; u < 4; ++u)
         msk[u] = (2 * u < nv ? 0xffffu : 0u) | (2 * u + 1 < nv ? 0xffff0000u : 0u);
 #pragma unroll
-      for (int f = 0; f < NF; ++f) r.v[f] &= msk;
+      for (int f = 0; f < NF; ++f) va[f] &= msk;
     }
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      oacc[f] = mfma16x16x32<T>(r.v[f], phi, oacc[f]);
-      oacc[f] = mfma16x16x32<T>(r.v[f], plo, oacc[f]);
+      oacc[f] = mfma16x16x32<T>(va[f], phi, oacc[f]);
+      oacc[f] = mfma16x16x32<T>(va[f], plo, oacc[f]);
     }
 
     // End of a piece: stage the output (whole segment, normalised) or the partial state.

@@ -11,9 +11,10 @@
 // reads its 32 key rows with NI = 32/TPI fully coalesced instructions. Each lane forms partial
 // dot products with its slice of the G query rows; DPP butterflies inside each group of LPR
 // lanes finish them.
-// Values. Stored [d][B] inside a block, so lane l owns head-dim rows l and l+64 and reads their
-// token runs contiguously; the step's probabilities go through LDS (one broadcast read per
-// four tokens) and each lane accumulates its own output rows -- no cross-lane reduction.
+// Values. Stored like the keys, so the value rows are read with the same instructions and each
+// lane already holds the probabilities of its own token rows: it accumulates p * v over them
+// into G x EPC partial sums of its head-dim slice; a piece's end sums them across the TPI
+// row groups (cross-lane swaps) before the output or partial state is written.
 #include "device_common.h"
 #include "kernels.h"
 #include "schedule.h"
@@ -27,10 +28,6 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
   constexpr int LPR = D / EPC;        // lanes per key row
   constexpr int TPI = 64 / LPR;       // key rows per load instruction
   constexpr int NI = 32 / TPI;        // key load instructions per step
-  constexpr int DU = D / 64;          // head-dim rows of V owned per lane
-  constexpr int BPS = 32 / B;         // blocks per step
-  constexpr int VCH = B * ES / 16;    // 16-byte chunks in one value row of a block
-  constexpr int VE = 16 / ES;         // elements per value chunk
 
   extern __shared__ int64_t smem[];
   const int S = p.num_seqs;
@@ -78,11 +75,11 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
 
   struct Regs {
     u32x4 k[NI];
-    u32x4 v[DU][BPS][VCH];
+    u32x4 v[NI];
     u32x4 q[G];   // this lane's slice of the G query rows of the step's KV head
   };
 
-  float m_run[G], l_run[G], acc[G][DU];
+  float m_run[G], l_run[G], acc[G][EPC];
   bool poison = false, piece_rfirst = true;
   int piece_k0 = 0;
 #pragma unroll
@@ -90,10 +87,8 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
     m_run[h] = kNegInf;
     l_run[h] = 0.f;
 #pragma unroll
-    for (int u = 0; u < DU; ++u) acc[h][u] = 0.f;
+    for (int e = 0; e < EPC; ++e) acc[h][e] = 0.f;
   }
-
-  __shared__ float sp[W][G][32];
 
   auto starts_piece = [](const StepInfo& si) { return si.rfirst || si.k == 0; };
 
@@ -109,20 +104,11 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
     for (int c = 0; c < NI; ++c) {
       const int tt = TPI * c + row;
       const int blk = (B == 16 && tt >= 16) ? b1 : b0;
-      const int off = tt & (B - 1);
-      r.k[c] = load16(kbase + ((size_t)blk * Hkv + si.g) * blk_stride + (size_t)off * D * ES +
-                      (size_t)ch * 16);
+      const size_t ofs = ((size_t)blk * Hkv + si.g) * blk_stride +
+                         (size_t)(tt & (B - 1)) * D * ES + (size_t)ch * 16;
+      r.k[c] = load16(kbase + ofs);
+      r.v[c] = load16(vbase + ofs);
     }
-#pragma unroll
-    for (int u = 0; u < DU; ++u)
-#pragma unroll
-      for (int bb = 0; bb < BPS; ++bb) {
-        const int blk = bb ? b1 : b0;
-        const char* vp = vbase + ((size_t)blk * Hkv + si.g) * blk_stride +
-                         (size_t)(lane + 64 * u) * B * ES;
-#pragma unroll
-        for (int x = 0; x < VCH; ++x) r.v[u][bb][x] = load16(vp + 16 * x);
-      }
   };
 
   auto begin_step = [&](const StepInfo& si) {
@@ -132,20 +118,12 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
         m_run[h] = kNegInf;
         l_run[h] = 0.f;
 #pragma unroll
-        for (int u = 0; u < DU; ++u) acc[h][u] = 0.f;
+        for (int e = 0; e < EPC; ++e) acc[h][e] = 0.f;
       }
       poison = false;
       piece_rfirst = si.rfirst;
       piece_k0 = si.k;
     }
-  };
-
-  auto value_at = [&](const Regs& r, int u, int t) -> float {
-    const int bb = t / B;
-    const int tt = t % B;
-    const uint32_t wd = r.v[u][bb][tt / VE][(tt % VE) / (4 / ES)];
-    if constexpr (ES == 4) return __uint_as_float(wd);
-    else return (tt & 1) ? hi16<T>(wd) : lo16<T>(wd);
   };
 
   auto compute_step = [&](Regs& r, const StepInfo& si) {
@@ -195,56 +173,56 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
       l_run[h] = l_run[h] * alpha + ps;
       m_run[h] = m_new;
 #pragma unroll
-      for (int u = 0; u < DU; ++u) acc[h][u] *= alpha;
+      for (int e = 0; e < EPC; ++e) acc[h][e] *= alpha;
     }
-    if (ch == 0) {
 #pragma unroll
-      for (int c = 0; c < NI; ++c)
+    for (int c = 0; c < NI; ++c) {
+      // slots past the context may hold anything (NaN included): their values count as zero
+      const bool live = TPI * c + row < nvalid;
+      float vx[EPC];
 #pragma unroll
-        for (int h = 0; h < G; ++h) sp[wave][h][TPI * c + row] = z[c][h];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const bool tail = nvalid < 32;
-#pragma unroll
-    for (int t4 = 0; t4 < 8; ++t4) {
-      f32x4 pw[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) pw[h] = *reinterpret_cast<const f32x4*>(&sp[wave][h][4 * t4]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 4 * t4 + e;
-#pragma unroll
-        for (int u = 0; u < DU; ++u) {
-          float v = value_at(r, u, t);
-          if (tail && t >= nvalid) v = 0.f;   // slots past the context may hold anything
-#pragma unroll
-          for (int h = 0; h < G; ++h) acc[h][u] = fmaf(pw[h][e], v, acc[h][u]);
-        }
+      for (int e = 0; e < EPC; ++e) {
+        float v;
+        if constexpr (ES == 4) v = __uint_as_float(r.v[c][e]);
+        else v = (e & 1) ? hi16<T>(r.v[c][e >> 1]) : lo16<T>(r.v[c][e >> 1]);
+        vx[e] = live ? v : 0.f;
       }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[h][e] = fmaf(z[c][h], vx[e], acc[h][e]);
     }
-    __builtin_amdgcn_wave_barrier();
 
     if (si.rlast || si.k == si.ns - 1) {
       const bool whole = piece_k0 == 0 && si.k == si.ns - 1;
       const size_t slot = piece_slot(si.range, piece_rfirst);
+      const int d0 = ch * EPC;   // this lane's head-dim slice; row group 0 stores it
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float l_tot = cross_sum<LPR>(l_run[h]);
         if (poison) l_tot = __builtin_nanf("");
+        float o[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) o[e] = cross_sum<LPR>(acc[h][e]);
         if (whole) {
           const size_t orow = (size_t)si.s * p.num_q_heads + (size_t)si.g * G + h;
           const float inv = l_tot == 0.f ? 0.f : 1.0f / l_tot;
-#pragma unroll
-          for (int u = 0; u < DU; ++u) {
-            const float o = acc[h][u] * inv;
-            const int d = lane + 64 * u;
+          if (row == 0) {
             if (p.out_f32) {
-              reinterpret_cast<float*>(p.out)[orow * D + d] = o;
+              float* op = reinterpret_cast<float*>(p.out) + orow * D + d0;
+#pragma unroll
+              for (int e4 = 0; e4 < EPC; e4 += 4)
+                *reinterpret_cast<f32x4*>(op + e4) =
+                    f32x4{o[e4] * inv, o[e4 + 1] * inv, o[e4 + 2] * inv, o[e4 + 3] * inv};
             } else {
-              if constexpr (ES == 2)
-                reinterpret_cast<uint16_t*>(p.out)[orow * D + d] = Elem<T>::from_f32(o);
+              if constexpr (ES == 2) {
+                u32x4 w;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                  w[u] = (uint32_t)scaled_to_16<T>(o[2 * u], inv) |
+                         ((uint32_t)scaled_to_16<T>(o[2 * u + 1], inv) << 16);
+                *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.out) + orow * D + d0) = w;
+              }
             }
           }
         } else {
@@ -253,8 +231,12 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
             p.ws_m[pr] = m_run[h];
             p.ws_l[pr] = l_tot;
           }
+          if (row == 0) {
 #pragma unroll
-          for (int u = 0; u < DU; ++u) p.ws_acc[pr * D + lane + 64 * u] = acc[h][u];
+            for (int e4 = 0; e4 < EPC; e4 += 4)
+              *reinterpret_cast<f32x4*>(p.ws_acc + pr * D + d0 + e4) =
+                  f32x4{o[e4], o[e4 + 1], o[e4 + 2], o[e4 + 3]};
+          }
         }
       }
     }

@@ -39,6 +39,16 @@ template <> struct Elem<bf16_t> {
   }
 };
 
+// x * s as an fp32 value, then rounded to the 16-bit type T. The empty asm makes the product
+// opaque, so the compiler cannot fuse multiply and narrowing into one mixed-precision FMA
+// (which rounds once, straight to 16 bits): a 16-bit output is exactly the fp32 output, rounded.
+template <typename T>
+__device__ __forceinline__ uint16_t scaled_to_16(float x, float s) {
+  float y = x * s;
+  asm("" : "+v"(y));
+  return Elem<T>::from_f32(y);
+}
+
 // 16-byte global load (global_load_dwordx4).
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);

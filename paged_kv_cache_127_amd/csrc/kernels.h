@@ -18,18 +18,30 @@ hipError_t launch_decode_valu(const DecodeParams& p, int kv_dtype, int head_dim,
 int decode_mfma_resident_waves(int kv_dtype, int head_dim, int block_size, int group, int waves,
                                int num_seqs);
 
-// Output ring of the matrix-core decode kernel: per wavefront, ring_capacity staged piece
-// results of G rows x D floats plus 2 G floats, each with a 16-byte header, in dynamic LDS
-// after the schedule arrays.
-constexpr size_t kRingBudgetBytes = 32 * 1024;   // per wavefront
-inline int ring_capacity(int group, int head_dim) {
-  const size_t per = 16 + 4 * ((size_t)group * head_dim + 2 * (size_t)group);
-  const size_t r = kRingBudgetBytes / per;
+// Dynamic LDS of the matrix-core decode kernel, after the schedule arrays: per wavefront a
+// value staging tile (32 token rows of D 16-bit elements, re-read transposed as MFMA operands)
+// and an output ring of ring_capacity staged piece results (G rows x D floats plus 2 G floats,
+// each with a 16-byte header). The ring takes what the workgroup's LDS has left, at most
+// kRingBudgetBytes and 16 entries per wavefront, at least one entry.
+constexpr size_t kLdsPerWorkgroup = 160 * 1024;   // gfx950
+constexpr size_t kRingBudgetBytes = 32 * 1024;    // per wavefront
+inline size_t value_stage_bytes(int head_dim) { return (size_t)32 * head_dim * 2; }
+inline size_t ring_entry_bytes(int group, int head_dim) {
+  return 16 + 4 * ((size_t)group * head_dim + 2 * (size_t)group);
+}
+inline int ring_capacity(int num_seqs, int group, int head_dim, int waves) {
+  const size_t per = ring_entry_bytes(group, head_dim);
+  const size_t fixed = ring_offset(num_seqs) + (size_t)waves * value_stage_bytes(head_dim);
+  size_t r = kRingBudgetBytes / per;
+  const size_t fit = fixed < kLdsPerWorkgroup ? (kLdsPerWorkgroup - fixed) / ((size_t)waves * per) : 0;
+  if (fit < r) r = fit;
   return r < 1 ? 1 : (r > 16 ? 16 : (int)r);
 }
 inline size_t mfma_lds_bytes(int num_seqs, int group, int head_dim, int waves) {
-  const size_t per = 16 + 4 * ((size_t)group * head_dim + 2 * (size_t)group);
-  return ring_offset(num_seqs) + (size_t)waves * ring_capacity(group, head_dim) * per;
+  return ring_offset(num_seqs) +
+         (size_t)waves * (value_stage_bytes(head_dim) +
+                          ring_capacity(num_seqs, group, head_dim, waves) *
+                              ring_entry_bytes(group, head_dim));
 }
 int decode_valu_resident_waves(int kv_dtype, int head_dim, int block_size, int group, int waves,
                                int num_seqs);

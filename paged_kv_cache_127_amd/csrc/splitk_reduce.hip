@@ -32,15 +32,16 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
   const int64_t ns = uni(p.prefix[s + 1]) - uni(p.prefix[s]);
   const size_t base = ((size_t)s * p.num_q_heads + (size_t)g * G) * D;
 
-  auto store = [&](int e4, f32x4 o) {
+  // o * s to the output (16-bit: the fp32 value rounded, see scaled_to_16)
+  auto store = [&](int e4, f32x4 o, float s) {
     if (p.out_f32) {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + base + 4 * e4) = o;
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + base + 4 * e4) = o * s;
     } else {
       if constexpr (sizeof(T) == 2) {
-        const uint32_t w0 = (uint32_t)Elem<T>::from_f32(o[0]) |
-                            ((uint32_t)Elem<T>::from_f32(o[1]) << 16);
-        const uint32_t w1 = (uint32_t)Elem<T>::from_f32(o[2]) |
-                            ((uint32_t)Elem<T>::from_f32(o[3]) << 16);
+        const uint32_t w0 = (uint32_t)scaled_to_16<T>(o[0], s) |
+                            ((uint32_t)scaled_to_16<T>(o[1], s) << 16);
+        const uint32_t w1 = (uint32_t)scaled_to_16<T>(o[2], s) |
+                            ((uint32_t)scaled_to_16<T>(o[3], s) << 16);
         *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + base + 4 * e4) =
             make_uint2(w0, w1);
       }
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
   if (ns == 0) {
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
-      if (lane + 64 * k < n4) store(lane + 64 * k, f32x4{0.f, 0.f, 0.f, 0.f});
+      if (lane + 64 * k < n4) store(lane + 64 * k, f32x4{0.f, 0.f, 0.f, 0.f}, 1.f);
     return;
   }
   const Line line = Line::make(p.prefix, p.wprefix, p.num_seqs, Hkv, p.piece_weight,
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
     const int e4 = lane + 64 * k;
     if (e4 < n4) {
       const float inv = den[k] == 0.f ? 0.f : 1.0f / den[k];
-      store(e4, num[k] * inv);
+      store(e4, num[k], inv);
     }
   }
 }

@@ -58,7 +58,7 @@ def test_growth_matches_oracle_model():
         for b in t:
             ours.claim(b); ref.claim(b)
     row = np.full(4, -1, np.int32); row[:3] = rows[1]
-    model = PagedKVModel(ref, np.zeros((64, 1, 16, 1)), np.zeros((64, 1, 1, 16)), 16)
+    model = PagedKVModel(ref, np.zeros((64, 1, 16, 1)), np.zeros((64, 1, 16, 1)), 16)
     model.add_sequence(1, rows[1], 47)
     ours.claim(11); row[3] = 11          # the engine of the example picks block 11
     for i in range(10):
@@ -76,7 +76,7 @@ def test_copy_on_write_matches_oracle_model():
     a[0], a[1] = ours.alloc(), ours.alloc()
     b = np.full(3, -1, np.int32)
     ours.fork(a, b, 2)
-    model = PagedKVModel(ref, np.zeros((8, 1, 16, 1)), np.zeros((8, 1, 1, 16)), 16)
+    model = PagedKVModel(ref, np.zeros((8, 1, 16, 1)), np.zeros((8, 1, 16, 1)), 16)
     model.add_sequence("A", [ref.alloc(), ref.alloc()], 24)
     model.fork("A", "B")
     blk, off, cow = ours.prepare_write(b, 24, 16)

@@ -55,7 +55,7 @@ def test_gather_returns_logical_rows():
             for p in range(int(b.lengths[s])):
                 blk, r = token_address(p, b.tables[s], 16)
                 assert np.array_equal(K[p], b.k_pool[blk, g, r].double().numpy())
-                assert np.array_equal(V[p], b.v_pool[blk, g, :, r].double().numpy())
+                assert np.array_equal(V[p], b.v_pool[blk, g, r].double().numpy())
 
 
 def test_closed_forms():
@@ -91,7 +91,7 @@ def test_spike_selects_the_addressed_slot():
     kp = b.k_pool.clone()
     kp[blk, h, off] = 40.0 * b.q[s, h]
     out = paged_decode(b.q, kp, b.v_pool, b.tables, b.lengths, 16, seqs=[s])
-    assert np.allclose(out[s, h], b.v_pool[blk, h, :, off].double().numpy(), atol=1e-12)
+    assert np.allclose(out[s, h], b.v_pool[blk, h, off].double().numpy(), atol=1e-12)
 
 
 def test_split_merge_is_exact():

@@ -41,7 +41,7 @@ def test_growth_example():
     assert g["pool_blocks"] * B == g["pool_slots"]
     assert g["pool_slots"] < 6144          # the per-request reservation would not fit
     k = np.zeros((g["pool_blocks"], 1, B, 2), np.float32)
-    v = np.zeros((g["pool_blocks"], 1, 2, B), np.float32)
+    v = np.zeros((g["pool_blocks"], 1, B, 2), np.float32)
     model = PagedKVModel(pool, k, v, B)
     for s, (t, L) in enumerate(zip(g["tables"], g["lengths"])):
         model.add_sequence(s, t, L)
@@ -59,8 +59,8 @@ def test_growth_example():
         assert model.tables[o] == before[o]
     assert blocks_for(g["lengths"][s] + g["alt_grow_by"], B) == g["alt_grown_blocks"]
     # the first appended token went to the last slot of block 9, the rest into block 11
-    assert k[9, 0, 15, 0] == 0 and v[9, 0, 0, 15] == 0
-    assert k[11, 0, 0, 0] == 1 and k[11, 0, 8, 0] == 9 and v[11, 0, 0, 8] == -9
+    assert k[9, 0, 15, 0] == 0 and v[9, 0, 15, 0] == 0
+    assert k[11, 0, 0, 0] == 1 and k[11, 0, 8, 0] == 9 and v[11, 0, 8, 0] == -9
     assert pool.num_free() == g["free_after_allocation"] - 1
 
 
@@ -71,7 +71,7 @@ def test_full_prefix_needs_no_copy():
     assert shareable_prefix_blocks(n, B) == g["full_prefix_blocks"] == blocks_for(n, B)
     pool = BlockPool(64)
     k = np.zeros((64, 1, B, 1), np.float32)
-    v = np.zeros((64, 1, 1, B), np.float32)
+    v = np.zeros((64, 1, B, 1), np.float32)
     model = PagedKVModel(pool, k, v, B)
     table = [pool.alloc() for _ in range(g["full_prefix_blocks"])]
     model.add_sequence("a", table, n)
@@ -89,7 +89,7 @@ def test_copy_on_write_example():
     pool = BlockPool(8)
     rng = np.random.default_rng(0)
     k = rng.standard_normal((8, H, B, d)).astype(np.float32)
-    v = rng.standard_normal((8, H, d, B)).astype(np.float32)
+    v = rng.standard_normal((8, H, B, d)).astype(np.float32)
     k0, v0 = k.copy(), v.copy()
     model = PagedKVModel(pool, k, v, B)
     names = {"P0": pool.alloc(), "P1": pool.alloc()}
@@ -109,9 +109,9 @@ def test_copy_on_write_example():
         assert pool.refcount(names[nm]) == r
     n = g["entries_copied"]
     # copied entries equal the originals bit for bit; A's block is untouched
-    assert np.array_equal(k[2, :, :n], k0[1, :, :n]) and np.array_equal(v[2, :, :, :n], v0[1, :, :, :n])
+    assert np.array_equal(k[2, :, :n], k0[1, :, :n]) and np.array_equal(v[2, :, :n], v0[1, :, :n])
     assert np.array_equal(k[1], k0[1]) and np.array_equal(v[1], v0[1])
-    assert np.array_equal(k[2, :, n], kr) and np.array_equal(v[2, :, :, n], vr)
+    assert np.array_equal(k[2, :, n], kr) and np.array_equal(v[2, :, n], vr)
     # slots past the new entry of the copy keep what the fresh block held
     assert np.array_equal(k[2, :, n + 1:], k0[2, :, n + 1:])
     # A then appends in place: P1 now has one reference, so no copy
@@ -154,7 +154,7 @@ def test_capacity_examples():
 def test_release_only_at_zero():
     a6 = load_golden("p3_capacity_examples.json")["a6"]
     pool = BlockPool(4)
-    k = np.zeros((4, 1, 16, 1)); v = np.zeros((4, 1, 1, 16))
+    k = np.zeros((4, 1, 16, 1)); v = np.zeros((4, 1, 16, 1))
     model = PagedKVModel(pool, k, v, 16)
     p0 = pool.alloc()
     model.add_sequence("A", [p0], 16)

@@ -45,7 +45,9 @@ def test_transposed_value_block_is_caught(monkeypatch):
         pos = np.arange(int(length))
         phys = np.asarray(table_row, dtype=np.int64)[pos // block_size]
         off = pos % block_size
-        return A._index(k_pool, phys, kv_head, off), A._index(v_pool, phys, kv_head, off)
+        # value block read as if stored [d][B] (head-dim rows and token slots swapped)
+        return A._index(k_pool, phys, kv_head, off), \
+            A._index(v_pool.transpose(2, 3), phys, kv_head, off)
     monkeypatch.setattr(A, "gather_kv", bad_gather)
     assert not _agrees_with_sdpa(_batch())
 

@@ -10,7 +10,7 @@ def test_config1_structure():
     assert list(b.lengths) == [25, 47, 12]
     assert b.tables.tolist() == [[3, 7, -1, -1], [0, 5, 9, -1], [4, -1, -1, -1]]
     assert b.num_blocks == 64 and b.k_pool.shape == (64, 4, 16, 64)
-    assert b.v_pool.shape == (64, 4, 64, 16) and b.q.dtype == torch.float32
+    assert b.v_pool.shape == (64, 4, 16, 64) and b.q.dtype == torch.float32
 
 
 def test_determinism():

@@ -7,8 +7,7 @@ of the method.
 
 Cache layout (one layer; K and V in separate pools):
   * ``k_pool``  ``[num_blocks][H_kv][B][d]``  -- a block holds B key rows per KV head;
-  * ``v_pool``  ``[num_blocks][H_kv][d][B]``  -- values are stored transposed inside a block,
-    so a head-dim row of one block holds that row's B token values contiguously.
+  * ``v_pool``  ``[num_blocks][H_kv][B][d]``  -- and B value rows, in the same order.
 The pages leave the in-block layout to the kernel ("PagedAttention: Virtual Memory for the KV
 Cache", section "Block size is a kernel choice too").
 
@@ -67,7 +66,7 @@ class Batch:
     num_blocks: int                # physical blocks in the pool
     q: torch.Tensor                # [S][H_q][d]
     k_pool: torch.Tensor           # [N][H_kv][B][d]
-    v_pool: torch.Tensor           # [N][H_kv][d][B]
+    v_pool: torch.Tensor           # [N][H_kv][B][d]
     k_logical: list                # per sequence [H_kv][L_s][d], in token order
     v_logical: list                # per sequence [H_kv][L_s][d]
     seed: int = 0
@@ -92,7 +91,7 @@ def empty_pools(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: i
                 dtype: torch.dtype, poison: bool = False):
     fill = float("nan") if poison else 0.0
     k_pool = torch.full((num_blocks, num_kv_heads, block_size, head_dim), fill, dtype=dtype)
-    v_pool = torch.full((num_blocks, num_kv_heads, head_dim, block_size), fill, dtype=dtype)
+    v_pool = torch.full((num_blocks, num_kv_heads, block_size, head_dim), fill, dtype=dtype)
     return k_pool, v_pool
 
 
@@ -113,7 +112,7 @@ def write_rows(k_pool, v_pool, table_row, k_seq, v_seq, start: int = 0):
         blk = int(table_row[j])
         a, b = pos - start, pos - start + (hi - lo)
         k_pool[blk, :, lo:hi, :] = k_seq[:, a:b, :]
-        v_pool[blk, :, :, lo:hi] = v_seq[:, a:b, :].transpose(1, 2)
+        v_pool[blk, :, lo:hi, :] = v_seq[:, a:b, :]
         pos += hi - lo
 
 
