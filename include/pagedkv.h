@@ -100,9 +100,9 @@ const char* pkv_last_error(void);
  *                 max_blocks_per_seq * block_size
  *   num_seqs      at most 4096 per call
  *   scale         softmax scale; <= 0 selects 1/sqrt(head_dim)
- *   num_workers   0 = automatic (8 wavefronts per compute unit of the current device, all
- *                 resident at once), else 1 .. 2^20 (any count gives the same result up to
- *                 rounding)
+ *   num_workers   0 = automatic (as many wavefronts as the chosen kernel keeps resident on
+ *                 the current device, at most 8 per compute unit), else 1 .. 2^20 (any
+ *                 count gives the same result up to rounding)
  *   workspace     device scratch, 256-byte aligned, of at least
  *                 pkv_decode_workspace_size(...) bytes for the same num_workers; no contents
  *                 are assumed between calls. Calls that overlap in time need separate
@@ -130,7 +130,8 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
  *   v_pool[slot.block][g][slot.offset][:] = v_new[i][g][:]
  * The caller has already grown the table (and made shared blocks private, see
  * cow_block_copy). Slots must be distinct; a bitwise copy, no rounding.
- *   k_new, v_new  device [num_tokens][num_kv_heads][head_dim], element type kv_dtype
+ *   k_new, v_new  device [num_tokens][num_kv_heads][head_dim], element type kv_dtype;
+ *                 num_tokens * num_kv_heads * head_dim < 2^31 per call
  *   seq_ids, positions  device int32 [num_tokens]
  * --------------------------------------------------------------------------------------- */
 int kv_cache_append(void* k_pool, void* v_pool, int kv_dtype, const void* k_new,

@@ -251,6 +251,8 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
   if (!workspace || workspace_bytes < wl.total)
     return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "paged_attn_decode: workspace %zu < %zu bytes",
                 workspace_bytes, wl.total);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(PKV_ERR_INVALID_ARG, "paged_attn_decode: workspace not 256-byte aligned");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
   if (validate_mode()) {
@@ -328,6 +330,9 @@ int kv_cache_append(void* k_pool, void* v_pool, int kv_dtype, const void* k_new,
   if (num_tokens == 0) return ok();
   if (!k_pool || !v_pool || !k_new || !v_new || !seq_ids || !positions || !block_tables)
     return fail(PKV_ERR_INVALID_ARG, "kv_cache_append: null pointer");
+  if ((int64_t)num_tokens * num_kv_heads * head_dim >= ((int64_t)1 << 31))
+    return fail(PKV_ERR_UNSUPPORTED, "kv_cache_append: %d tokens x %d heads x %d too large",
+                num_tokens, num_kv_heads, head_dim);
   const int es = elem_bytes(kv_dtype);
   if (es == 0) return fail(PKV_ERR_UNSUPPORTED, "kv_cache_append: kv_dtype %d", kv_dtype);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

@@ -15,21 +15,26 @@ namespace pkv {
 
 // One thread per E-sized unit of a new row (E = 16 bytes when every pointer allows it, else
 // the element). Keys and values share the layout, so row (i, g) of k_new / v_new lands in one
-// contiguous row of its block: the writes of a token are whole cache lines.
+// contiguous row of its block: the writes of a token are whole cache lines. The new rows are
+// loaded before the slot lookup (they do not depend on it), so a thread waits for two rounds
+// of memory latency: ids, position and row data, then the table entry. 32-bit index
+// arithmetic (the host checks num_tokens * H * units < 2^31).
 template <typename E>
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p, int units_per_row) {
   const int U = units_per_row, B = p.block_size, H = p.num_kv_heads;
-  const int64_t total = (int64_t)p.num_tokens * H * U;
+  const int total = p.num_tokens * H * U;
   E* kp = reinterpret_cast<E*>(p.k_pool);
   E* vp = reinterpret_cast<E*>(p.v_pool);
   const E* kn = reinterpret_cast<const E*>(p.k_new);
   const E* vn = reinterpret_cast<const E*>(p.v_new);
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int u = (int)(idx % U);
-    const int64_t t = idx / U;
-    const int g = (int)(t % H);
-    const int i = (int)(t / H);
+  for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += gridDim.x * blockDim.x) {
+    const int t = idx / U;            // (token, head) row
+    const int u = idx - t * U;
+    const int i = t / H;
+    const int g = t - i * H;
+    const E kx = kn[idx];
+    const E vx = vn[idx];
     const int s = p.seq_ids[i];
     const int pos = p.positions[i];
     if ((unsigned)s >= (unsigned)p.num_seqs || pos < 0) continue;
@@ -39,8 +44,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p, int units_p
     if ((unsigned)blk >= (unsigned)p.num_blocks) continue;
     const int off = pos - j * B;
     const size_t row = ((size_t)blk * H + g) * B + off;
-    kp[row * U + u] = kn[idx];
-    vp[row * U + u] = vn[idx];
+    kp[row * U + u] = kx;
+    vp[row * U + u] = vx;
   }
 }
 
@@ -75,6 +80,7 @@ hipError_t launch_append(const AppendParams& p, int elem_bytes, hipStream_t st) 
   const int units = wide ? row_bytes / 16 : p.head_dim;
   const int64_t total = (int64_t)p.num_tokens * p.num_kv_heads * units;
   if (total <= 0) return hipSuccess;
+  if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (wide)

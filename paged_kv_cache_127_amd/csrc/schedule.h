@@ -97,15 +97,23 @@ __device__ inline void build_prefixes(const int32_t* lens, int S, int cap, int p
 }
 
 // Largest s in [0, S) with Hkv * prefix[s] <= r (r < Hkv * prefix[S]); for a prefix that is
-// constant over empty sequences this is a sequence with work.
-__device__ __forceinline__ int find_seq(const int64_t* prefix, int S, int Hkv, int64_t r) {
-  int lo = 0, hi = S;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if ((int64_t)Hkv * uni(prefix[mid]) <= r) lo = mid;
-    else hi = mid;
+// constant over empty sequences this is a sequence with work. Wave-parallel: the predicate is
+// monotone in s, so a ballot over 64 candidates brackets the answer -- one round for S <= 64,
+// two (every stride-th entry, then the stride entries that follow the last passing one) for
+// S <= 4096. All 64 lanes of the wavefront must be active.
+__device__ inline int find_seq(const int64_t* prefix, int S, int Hkv, int64_t r) {
+  const int lane = threadIdx.x & 63;
+  const int stride = (S + 63) >> 6;
+  int base = 0, cnt = S;
+  if (stride > 1) {
+    const int c = stride * lane;
+    const bool ok = c < S && (int64_t)Hkv * prefix[c < S ? c : 0] <= r;
+    base = stride * ((int)__popcll(__ballot(ok)) - 1);   // prefix[0] = 0 always passes
+    cnt = S - base < stride ? S - base : stride;
   }
-  return lo;
+  const int c = base + lane;
+  const bool ok = lane < cnt && (int64_t)Hkv * prefix[lane < cnt ? c : base] <= r;
+  return base + (int)__popcll(__ballot(ok)) - 1;
 }
 
 // Start of share w of a line of N units cut into n shares. The host guarantees N * n < 2^62.

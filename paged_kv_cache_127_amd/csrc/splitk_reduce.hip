@@ -7,16 +7,16 @@
 //
 // One wavefront per segment, four per workgroup. The slots of a segment follow from the
 // schedule arithmetic alone; lane l holds f32x4 chunks l, l + 64, ... of the segment's G rows
-// (contiguous in a slot and in the output), loads (m, l, acc) of two slots at a time with
+// (contiguous in a slot and in the output), loads (m, l, acc) of four slots at a time with
 // independent loads and folds them into a running (max, numerator, denominator): a segment
-// costs one round trip for the prefixes and one per two partials.
+// costs one round trip for the prefixes and one per four partials (one for almost all).
 #include "device_common.h"
 #include "kernels.h"
 #include "schedule.h"
 
 namespace pkv {
 
-constexpr int kMergeBatch = 2;
+constexpr int kMergeBatch = 4;
 
 // KMAX = ceil(G * D / 256): f32x4 chunks per lane (G rows of D floats over 64 lanes).
 template <int D, typename T, int KMAX>

@@ -7,7 +7,9 @@ writes slot 2w, its last piece (if different) slot 2w+1, whole segments write no
 
 This checks, for many length mixes, worker counts (including more workers than steps) and
 piece weights, that the ranges tile the line, that the merge rule finds exactly the slots that
-were written, and that the weighted cut balances steps + pieces."""
+were written, and that the weighted cut balances steps + pieces. It also models the
+wave-parallel sequence search (two ballot rounds of 64 candidates)."""
+import bisect
 import random
 
 STEP_W = 4
@@ -147,3 +149,31 @@ def test_zero_piece_weight_is_an_equal_step_cut():
         sizes = [line.steps_before(line.wbegin(w + 1)) - line.steps_before(line.wbegin(w))
                  for w in range(n)]
         assert sum(sizes) == line.N and max(sizes) - min(sizes) <= 1
+
+
+def find_seq_ballot(prefix, S, Hkv, r):
+    """The wave-parallel search: 64 candidates per round, the answer is (passing lanes) - 1."""
+    stride = (S + 63) >> 6
+    base, cnt = 0, S
+    if stride > 1:
+        ok = [stride * l < S and Hkv * prefix[stride * l] <= r for l in range(64)]
+        base = stride * (sum(ok) - 1)
+        cnt = min(S - base, stride)
+    ok = [l < cnt and Hkv * prefix[base + l] <= r for l in range(64)]
+    return base + sum(ok) - 1
+
+
+def test_ballot_search_matches_bisection():
+    rnd = random.Random(3)
+    for S in (1, 2, 5, 63, 64, 65, 127, 128, 129, 255, 256, 1000, 4095, 4096):
+        ns = [rnd.choice([0, 0, 1, 3, 40]) for _ in range(S)]
+        ns[rnd.randrange(S)] += 1
+        prefix = [0]
+        for x in ns:
+            prefix.append(prefix[-1] + x)
+        Hkv = rnd.choice([1, 8])
+        for r in list(range(0, min(Hkv * prefix[S], 300))) + \
+                [rnd.randrange(Hkv * prefix[S]) for _ in range(300)]:
+            want = bisect.bisect_right([Hkv * p for p in prefix[:S]], r) - 1
+            assert find_seq_ballot(prefix, S, Hkv, r) == want
+            assert ns[want] > 0          # the largest such s is a sequence with work
