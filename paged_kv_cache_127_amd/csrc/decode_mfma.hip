@@ -25,7 +25,7 @@
 // Probabilities are split into a 16-bit high part and a 16-bit remainder (two MFMAs), which
 // keeps P.V at close to fp32 accuracy. Scores and the online softmax stay in fp32; the scale
 // (times log2 e) is applied to the fp32 scores and exp2 is used throughout.
-// The next step's loads (with its query rows) are in flight while a step computes.
+// Two steps' loads (with their query rows) are in flight while a step computes.
 #include "device_common.h"
 #include "kernels.h"
 #include "schedule.h"
@@ -196,7 +196,7 @@ void decode_mfma(DecodeParams p) {
   // piece's first step); the padding columns of the 16-wide tile repeat head G-1 and are never
   // stored.
   const int qrow = r16 < G ? r16 : G - 1;
-  auto load_step = [&](StepRegs<D>& r, const StepInfo& si) {
+  auto load_kq = [&](StepRegs<D>& r, const StepInfo& si) {
     {
       const char* qp = qbase + (((size_t)si.s * p.num_q_heads + (size_t)si.g * G + qrow) * D +
                                 8 * jg) * ES;
@@ -214,6 +214,10 @@ void decode_mfma(DecodeParams p) {
       r.k[0][c] = load16(ka + kofs0 + 32 * c * ES);
       r.k[1][c] = load16(kb + kofs1 + 32 * c * ES);
     }
+  };
+  auto load_v = [&](StepRegs<D>& r, const StepInfo& si) {
+    const int b0 = valid_block(si.b0, p.num_blocks) ? si.b0 : 0;
+    const int b1 = valid_block(si.b1, p.num_blocks) ? si.b1 : 0;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int t = VTPI * f + vrow;
@@ -279,7 +283,10 @@ void decode_mfma(DecodeParams p) {
     }
   };
 
-  auto compute_step = [&](StepRegs<D>& r, const StepInfo& si) {
+  // Step si from buffer r; the loads of step nx (two steps ahead) go into r as soon as each
+  // part of r has been consumed: K and Q after the score MFMAs, V after its rows went to LDS.
+  // The softmax and P.V of this step then run with two steps of loads in flight.
+  auto compute_step = [&](StepRegs<D>& r, const StepInfo& si, const StepInfo& nx) {
     const int nvalid = si.L - 32 * si.k;             // valid tokens in this step (>= 1)
     poison = poison || !valid_block(si.b0, p.num_blocks) ||
              (B == 16 && nvalid > 16 && !valid_block(si.b1, p.num_blocks));
@@ -290,11 +297,13 @@ void decode_mfma(DecodeParams p) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) sacc[a] = mfma16x16x32<T>(r.k[a][c], r.q[c], sacc[a]);
     }
+    load_kq(r, nx);
     // value rows into the LDS tile, then back as A operands (head-dim column 16f + lane%16,
     // tokens 8*(lane/16) .. +8 of the step)
     wave_lds_sync();   // the previous step's transposed reads come first
 #pragma unroll
     for (int f = 0; f < NF; ++f) *reinterpret_cast<u32x4*>(vstage + vw_ofs[f]) = r.v[f];
+    load_v(r, nx);
     wave_lds_sync();
     u32x4 va[NF];
 #pragma unroll
@@ -384,33 +393,34 @@ void decode_mfma(DecodeParams p) {
   };
 
   // Software pipeline over two register buffers: while step i computes, the loads of step
-  // i + 1 are in flight; the loads of step i + 2 are issued into the buffer step i has just
-  // consumed, and the block ids of the step after that are being fetched (scalar loads). Past
+  // i + 1 are in flight and those of step i + 2 are issued into the parts of step i's buffer
+  // that are consumed (inside compute_step); the block ids of the step after that are being
+  // fetched (scalar loads). Past
   // the last step the stream repeats it (cache hits), which keeps every vector load
   // unconditional. The loop runs over pairs of steps with its only exit at the bottom, so the
   // compiler's wait counts stay exact; an odd last step is finished after it.
   StepRegs<D> BA, BB;
   StepInfo sa = ss.next();
   StepInfo sb = ss.next();
-  load_step(BA, sa);
-  load_step(BB, sb);
+  load_kq(BA, sa);
+  load_v(BA, sa);
+  load_kq(BB, sb);
+  load_v(BB, sb);
   StepInfo sc = ss.next();
   for (int64_t i = 0; i + 2 <= nsteps; i += 2) {
     // BA: step i (sa); BB: step i + 1 (sb); sc describes step i + 2
     begin_step(sa);
-    compute_step(BA, sa);
-    load_step(BA, sc);
+    compute_step(BA, sa, sc);
     const StepInfo sd = ss.next();
     begin_step(sb);
-    compute_step(BB, sb);
-    load_step(BB, sd);
+    compute_step(BB, sb, sd);
     sa = sc;
     sb = sd;
     sc = ss.next();
   }
   if (nsteps & 1) {
     begin_step(sa);
-    compute_step(BA, sa);
+    compute_step(BA, sa, sa);   // its loads repeat this step's lines (cache hits, unused)
   }
   flush(false);
 }

@@ -5,11 +5,16 @@
 // (m is kept in the log2 domain). Segments of empty sequences get a zero row here; segments
 // that one range finished were written by the decode kernel and are skipped.
 //
-// One wavefront per segment, four per workgroup. The slots of a segment follow from the
-// schedule arithmetic alone; lane l holds f32x4 chunks l, l + 64, ... of the segment's G rows
-// (contiguous in a slot and in the output), loads (m, l, acc) of four slots at a time with
-// independent loads and folds them into a running (max, numerator, denominator): a segment
-// costs one round trip for the prefixes and one per four partials (one for almost all).
+// WPS wavefronts per segment, four wavefronts per workgroup. The slots of a segment follow from
+// the schedule arithmetic alone, range by range, so the WPS wavefronts split the segment's
+// ranges among themselves (range rf + j goes to wavefront j mod WPS) and each loads the
+// (m, l, acc) of up to four slots at once; lane l holds f32x4 chunks l, l + 64, ... of the
+// segment's G rows (contiguous in a slot and in the output) and folds its slots into a running
+// (max, numerator, denominator). With WPS = 4 the four running states meet in LDS and
+// wavefront 0 writes the result. WPS = 1 (one segment per wavefront) suits segments split into
+// a few ranges (fewer segments than workers is rare then); WPS = 4 suits long contexts, where
+// every segment spans many ranges: up to 16 of them cost one round trip for the prefixes and
+// one for the partials.
 #include "device_common.h"
 #include "kernels.h"
 #include "schedule.h"
@@ -19,11 +24,18 @@ namespace pkv {
 constexpr int kMergeBatch = 4;
 
 // KMAX = ceil(G * D / 256): f32x4 chunks per lane (G rows of D floats over 64 lanes).
-template <int D, typename T, int KMAX>
+template <int D, typename T, int KMAX, int WPS>
 __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
+  static_assert(WPS == 1 || WPS == 4, "wavefronts per segment");
+  constexpr int SH = WPS > 1 ? WPS : 1;
+  __shared__ float sh_m[SH][WPS > 1 ? KMAX : 1][64];
+  __shared__ float sh_den[SH][WPS > 1 ? KMAX : 1][64];
+  __shared__ f32x4 sh_num[SH][WPS > 1 ? KMAX : 1][64];
   const int lane = threadIdx.x & 63;
+  const int wv = uni((int)(threadIdx.x >> 6));
+  const int wave = wv % WPS;                         // index inside the segment's wavefronts
   const int Hkv = p.num_kv_heads;
-  const int seg = blockIdx.x * 4 + uni((int)(threadIdx.x >> 6));
+  const int seg = blockIdx.x * (4 / WPS) + wv / WPS;
   if (seg >= p.num_seqs * Hkv) return;
   const int s = seg / Hkv;
   const int g = seg - s * Hkv;
@@ -32,26 +44,28 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
   const int64_t ns = uni(p.prefix[s + 1]) - uni(p.prefix[s]);
   const size_t base = ((size_t)s * p.num_q_heads + (size_t)g * G) * D;
 
-  // o * s to the output (16-bit: the fp32 value rounded, see scaled_to_16)
-  auto store = [&](int e4, f32x4 o, float s) {
+  // o * sc to the output (16-bit: the fp32 value rounded, see scaled_to_16)
+  auto store = [&](int e4, f32x4 o, float sc) {
     if (p.out_f32) {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + base + 4 * e4) = o * s;
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + base + 4 * e4) = o * sc;
     } else {
       if constexpr (sizeof(T) == 2) {
-        const uint32_t w0 = (uint32_t)scaled_to_16<T>(o[0], s) |
-                            ((uint32_t)scaled_to_16<T>(o[1], s) << 16);
-        const uint32_t w1 = (uint32_t)scaled_to_16<T>(o[2], s) |
-                            ((uint32_t)scaled_to_16<T>(o[3], s) << 16);
+        const uint32_t w0 = (uint32_t)scaled_to_16<T>(o[0], sc) |
+                            ((uint32_t)scaled_to_16<T>(o[1], sc) << 16);
+        const uint32_t w1 = (uint32_t)scaled_to_16<T>(o[2], sc) |
+                            ((uint32_t)scaled_to_16<T>(o[3], sc) << 16);
         *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + base + 4 * e4) =
             make_uint2(w0, w1);
       }
     }
   };
 
-  if (ns == 0) {
+  if (ns == 0) {   // empty sequence: zero rows
+    if (wave == 0) {
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-      if (lane + 64 * k < n4) store(lane + 64 * k, f32x4{0.f, 0.f, 0.f, 0.f}, 1.f);
+      for (int k = 0; k < KMAX; ++k)
+        if (lane + 64 * k < n4) store(lane + 64 * k, f32x4{0.f, 0.f, 0.f, 0.f}, 1.f);
+    }
     return;
   }
   const Line line = Line::make(p.prefix, p.wprefix, p.num_seqs, Hkv, p.piece_weight,
@@ -61,10 +75,18 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
   const int64_t first = ws0 + line.pw;                                 // weighted start of step 0
   const int rf = line.owner(first);
   const int rl = line.owner(first + kStepWeight * (ns - 1));
-  if (rf == rl) return;   // one worker wrote the whole segment
-  // rf's piece is its first one (slot 2 rf) unless rf also holds the previous segment's last
-  // step, which starts at ws0 - kStepWeight
-  const int64_t first_slot = 2 * (int64_t)rf + (line.wbegin(rf) > ws0 - kStepWeight ? 0 : 1);
+  if (rf == rl) return;   // one range holds the whole segment: written by the decode kernel
+
+  // Slot of range r's piece of this segment, or -1 if r holds none of its steps. rf's piece is
+  // its first one (slot 2 rf) unless rf also holds the previous segment's last step, which
+  // starts at ws0 - kStepWeight; a later range r starts inside the segment, so its piece is its
+  // first one (slot 2r) if it holds any of the segment's steps.
+  auto slot_of = [&](int r) -> int64_t {
+    if (r == rf) return 2 * (int64_t)rf + (line.wbegin(rf) > ws0 - kStepWeight ? 0 : 1);
+    const int64_t before = line.in_segment_before(line.wbegin(r), ws0, ns);
+    const int64_t after = r == rl ? ns : line.in_segment_before(line.wbegin(r + 1), ws0, ns);
+    return after > before ? 2 * (int64_t)r : -1;
+  };
 
   float M[KMAX], den[KMAX];
   f32x4 num[KMAX];
@@ -75,23 +97,13 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
     num[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const f32x4* acc4 = reinterpret_cast<const f32x4*>(p.ws_acc);
-  // Workers rf+1 .. rl start inside the segment: their first piece (slot 2r) belongs to it if
-  // they hold any of its steps.
-  int64_t before_r = line.in_segment_before(line.wbegin(rf + 1), ws0, ns);
 #pragma unroll 1
-  for (int r0 = rf; r0 <= rl; r0 += kMergeBatch) {
+  for (int r0 = rf + wave; r0 <= rl; r0 += WPS * kMergeBatch) {
     int64_t slot[kMergeBatch];
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
-      const int r = r0 + j;
-      slot[j] = -1;
-      if (r == rf) {
-        slot[j] = first_slot;
-      } else if (r <= rl) {
-        const int64_t after_r = r == rl ? ns : line.in_segment_before(line.wbegin(r + 1), ws0, ns);
-        if (after_r > before_r) slot[j] = 2 * (int64_t)r;
-        before_r = after_r;
-      }
+      const int r = r0 + WPS * j;
+      slot[j] = r <= rl ? slot_of(r) : -1;
     }
     float mj[kMergeBatch][KMAX], lj[kMergeBatch][KMAX];
     f32x4 aj[kMergeBatch][KMAX];
@@ -124,42 +136,79 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
         M[k] = m_new;
       }
   }
+  if constexpr (WPS == 1) {
 #pragma unroll
-  for (int k = 0; k < KMAX; ++k) {
-    const int e4 = lane + 64 * k;
-    if (e4 < n4) {
-      const float inv = den[k] == 0.f ? 0.f : 1.0f / den[k];
-      store(e4, num[k], inv);
+    for (int k = 0; k < KMAX; ++k) {
+      const int e4 = lane + 64 * k;
+      if (e4 < n4) store(e4, num[k], den[k] == 0.f ? 0.f : 1.0f / den[k]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      sh_m[wave][k][lane] = M[k];
+      sh_den[wave][k][lane] = den[k];
+      sh_num[wave][k][lane] = num[k];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const int e4 = lane + 64 * k;
+      float Mx = sh_m[0][k][lane];
+#pragma unroll
+      for (int v = 1; v < WPS; ++v) Mx = fmaxf(Mx, sh_m[v][k][lane]);
+      f32x4 nm = f32x4{0.f, 0.f, 0.f, 0.f};
+      float dn = 0.f;
+      if (Mx != kNegInf) {
+#pragma unroll
+        for (int v = 0; v < WPS; ++v) {
+          const float a = fast_exp2(sh_m[v][k][lane] - Mx);
+          nm += sh_num[v][k][lane] * a;
+          dn += sh_den[v][k][lane] * a;
+        }
+      }
+      if (e4 < n4) store(e4, nm, dn == 0.f ? 0.f : 1.0f / dn);
     }
   }
 }
 
-template <int D, typename T>
-static void launch_merge_t(const DecodeParams& p, unsigned grid, hipStream_t st) {
+template <int D, typename T, int WPS>
+static void launch_merge_w(const DecodeParams& p, hipStream_t st) {
+  const int64_t segs = (int64_t)p.num_seqs * p.num_kv_heads;
+  const dim3 grid((unsigned)((segs * WPS + 3) / 4)), blk(256);
   const int chunks = (p.num_q_heads / p.num_kv_heads * D / 4 + 63) / 64;
   if (chunks <= 1)
-    hipLaunchKernelGGL((splitk_merge<D, T, 1>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((splitk_merge<D, T, 1, WPS>), grid, blk, 0, st, p);
   else if (chunks <= 2)
-    hipLaunchKernelGGL((splitk_merge<D, T, 2>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((splitk_merge<D, T, 2, WPS>), grid, blk, 0, st, p);
   else if (chunks <= 4)
-    hipLaunchKernelGGL((splitk_merge<D, T, 4>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((splitk_merge<D, T, 4, WPS>), grid, blk, 0, st, p);
   else
-    hipLaunchKernelGGL((splitk_merge<D, T, 8>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((splitk_merge<D, T, 8, WPS>), grid, blk, 0, st, p);
+}
+
+// Fewer segments than workers means every segment spans several ranges on average: four
+// wavefronts per segment; else one.
+template <int D, typename T>
+static void launch_merge_t(const DecodeParams& p, hipStream_t st) {
+  if ((int64_t)p.num_seqs * p.num_kv_heads < (int64_t)p.num_workers)
+    launch_merge_w<D, T, 4>(p, st);
+  else
+    launch_merge_w<D, T, 1>(p, st);
 }
 
 hipError_t launch_splitk_reduce(const DecodeParams& p, int kv_dtype, int head_dim,
                                 hipStream_t st) {
   const int64_t segs = (int64_t)p.num_seqs * p.num_kv_heads;
   if (segs <= 0) return hipSuccess;
-  const unsigned grid = (unsigned)((segs + 3) / 4);
   if (head_dim == 64) {
-    if (kv_dtype == 1) launch_merge_t<64, f16_t>(p, grid, st);
-    else if (kv_dtype == 2) launch_merge_t<64, bf16_t>(p, grid, st);
-    else launch_merge_t<64, float>(p, grid, st);
+    if (kv_dtype == 1) launch_merge_t<64, f16_t>(p, st);
+    else if (kv_dtype == 2) launch_merge_t<64, bf16_t>(p, st);
+    else launch_merge_t<64, float>(p, st);
   } else if (head_dim == 128) {
-    if (kv_dtype == 1) launch_merge_t<128, f16_t>(p, grid, st);
-    else if (kv_dtype == 2) launch_merge_t<128, bf16_t>(p, grid, st);
-    else launch_merge_t<128, float>(p, grid, st);
+    if (kv_dtype == 1) launch_merge_t<128, f16_t>(p, st);
+    else if (kv_dtype == 2) launch_merge_t<128, bf16_t>(p, st);
+    else launch_merge_t<128, float>(p, st);
   } else {
     return hipErrorInvalidValue;
   }
