@@ -84,6 +84,48 @@ def cpu_baseline(batch, steps: int):
     }
 
 
+def other_configs(pkv, W, torch, dev: str, workers: int, launches: int = 30):
+    """Decode-kernel roofline on the other batch configs (multi-head fp16, the GQA batch at
+    block size 32, long contexts): kernel durations from hipEvents around every launch."""
+    res = {}
+    cases = (
+        ("gqa256_b32", "GQA decode batch at block size 32 (as above)", lambda: W.config3(32)),
+        ("mha64_fp16", "MHA decode batch: 64 sequences, 32/32 heads, head_dim 128, fp16, block "
+                       "size 16, lengths uniform in [128, 2048]", W.config2),
+        ("long8_bf16", "long contexts: 8 sequences, 64/8 heads, head_dim 128, bf16, block size "
+                       "16, lengths uniform in [16384, 32768]", lambda: W.config5(steps=1)),
+    )
+    for key, desc, make in cases:
+        b = make()
+        q = b.q.to(dev)
+        kp, vp = b.k_pool.to(dev), b.v_pool.to(dev)
+        tab, lens = torch.from_numpy(b.tables).to(dev), torch.from_numpy(b.lengths).to(dev)
+        S, Hq, d = q.shape
+        out = torch.empty(S, Hq, d, dtype=torch.float32, device=dev)
+        ws = pkv.decode_workspace(S, Hq, kp.shape[1], d, workers, dev)
+        mx = int(b.lengths.max())
+        for _ in range(5):
+            pkv.paged_attn_decode(out, q, kp, vp, tab, lens, mx, num_workers=workers, workspace=ws)
+        torch.cuda.synchronize()
+        pkv.timing_enable(True, every=1)
+        for _ in range(launches):
+            pkv.paged_attn_decode(out, q, kp, vp, tab, lens, mx, num_workers=workers, workspace=ws)
+        torch.cuda.synchronize()
+        dm, dn = pkv.timing_query("decode_partial")
+        mm, mn = pkv.timing_query("splitk_reduce")
+        pkv.timing_enable(False)
+        dus, mus = dm / max(dn, 1) * 1e3, mm / max(mn, 1) * 1e3
+        gbs = b.kv_bytes / (dus * 1e-6) / 1e9
+        res[key] = {"workload": desc, "kv_bytes": b.kv_bytes, "decode_us": round(dus, 2),
+                    "merge_us": round(mus, 2), "achieved_gbs": round(gbs, 1),
+                    "frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "call_gbs": round(b.kv_bytes / ((dus + mus) * 1e-6) / 1e9, 1)}
+        print(f"bench: {key} decode {dus:.1f} us merge {mus:.1f} us", file=sys.stderr, flush=True)
+        del q, kp, vp, tab, lens, out, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,6 +136,8 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=15,
                     help="decode steps of the CPU oracle (about 0.7 s each on one core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the decode-kernel figures on the other batch configs")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -210,6 +254,10 @@ def main():
         },
         "setup_s": round(gen_s, 2),
     }
+    if not args.no_other_configs:
+        del k_pool, v_pool, q, out, ws
+        torch.cuda.empty_cache()
+        result["other_configs"] = other_configs(pkv, W, torch, dev, args.workers)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b, args.cpu_steps)
     print(json.dumps(result), flush=True)
