@@ -84,46 +84,228 @@ def cpu_baseline(batch, steps: int):
     }
 
 
+def _decode_timing(pkv, torch, launch, launches: int):
+    """(decode us, merge us, append us, copy us, step p50 us) of `launch` (one call sequence)
+    with hipEvents around every launch of each kernel and torch events around every call."""
+    for _ in range(5):
+        launch()
+    torch.cuda.synchronize()
+    pkv.timing_enable(True, every=1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(launches)]
+    for a, b_ in ev:
+        a.record()
+        launch()
+        b_.record()
+    torch.cuda.synchronize()
+    out = []
+    for name in ("decode_partial", "splitk_reduce", "append", "cow"):
+        ms, n = pkv.timing_query(name)
+        out.append(ms / n * 1e3 if n else 0.0)
+    pkv.timing_enable(False)
+    steps = sorted(a.elapsed_time(b_) * 1e3 for a, b_ in ev)
+    out.append(steps[len(steps) // 2])
+    return out
+
+
 def other_configs(pkv, W, torch, dev: str, workers: int, launches: int = 30):
-    """Decode-kernel roofline on the other batch configs (multi-head fp16, the GQA batch at
-    block size 32, long contexts): kernel durations from hipEvents around every launch."""
+    """Figures on the other batch configs: decode-kernel roofline for the HBM-bound ones (GQA
+    at block size 32, multi-head fp16, long contexts with their 8-token append per step),
+    logical GB/s for the shared-prefix batch (cache-assisted, no HBM claim), and latencies for
+    the tiny and copy-on-write configs (no roofline claim). Kernel durations from hipEvents
+    around every launch; step p50 from events around every call."""
+    import numpy as np
     res = {}
-    cases = (
-        ("gqa256_b32", "GQA decode batch at block size 32 (as above)", lambda: W.config3(32)),
-        ("mha64_fp16", "MHA decode batch: 64 sequences, 32/32 heads, head_dim 128, fp16, block "
-                       "size 16, lengths uniform in [128, 2048]", W.config2),
-        ("long8_bf16", "long contexts: 8 sequences, 64/8 heads, head_dim 128, bf16, block size "
-                       "16, lengths uniform in [16384, 32768]", lambda: W.config5(steps=1)),
-    )
-    for key, desc, make in cases:
-        b = make()
-        q = b.q.to(dev)
-        kp, vp = b.k_pool.to(dev), b.v_pool.to(dev)
-        tab, lens = torch.from_numpy(b.tables).to(dev), torch.from_numpy(b.lengths).to(dev)
-        S, Hq, d = q.shape
-        out = torch.empty(S, Hq, d, dtype=torch.float32, device=dev)
-        ws = pkv.decode_workspace(S, Hq, kp.shape[1], d, workers, dev)
-        mx = int(b.lengths.max())
-        for _ in range(5):
-            pkv.paged_attn_decode(out, q, kp, vp, tab, lens, mx, num_workers=workers, workspace=ws)
-        torch.cuda.synchronize()
-        pkv.timing_enable(True, every=1)
-        for _ in range(launches):
-            pkv.paged_attn_decode(out, q, kp, vp, tab, lens, mx, num_workers=workers, workspace=ws)
-        torch.cuda.synchronize()
-        dm, dn = pkv.timing_query("decode_partial")
-        mm, mn = pkv.timing_query("splitk_reduce")
-        pkv.timing_enable(False)
-        dus, mus = dm / max(dn, 1) * 1e3, mm / max(mn, 1) * 1e3
+
+    def stage(b):
+        t = dict(q=b.q.to(dev), kp=b.k_pool.to(dev), vp=b.v_pool.to(dev),
+                 tab=torch.from_numpy(b.tables).to(dev), lens=torch.from_numpy(b.lengths).to(dev))
+        S, Hq, d = b.q.shape
+        t["out"] = torch.empty(S, Hq, d, dtype=torch.float32, device=dev)
+        t["ws"] = pkv.decode_workspace(S, Hq, b.num_kv_heads, d, workers, dev)
+        t["mx"] = int(b.lengths.max())
+        return t
+
+    def decode_call(t, tab=None, lens=None, mx=None):
+        pkv.paged_attn_decode(t["out"], t["q"], t["kp"], t["vp"], t["tab"] if tab is None else tab,
+                              t["lens"] if lens is None else lens, t["mx"] if mx is None else mx,
+                              num_workers=workers, workspace=t["ws"])
+
+    def hbm_entry(desc, b, dus, mus, aus, step):
         gbs = b.kv_bytes / (dus * 1e-6) / 1e9
-        res[key] = {"workload": desc, "kv_bytes": b.kv_bytes, "decode_us": round(dus, 2),
-                    "merge_us": round(mus, 2), "achieved_gbs": round(gbs, 1),
-                    "frac": round(gbs / HBM_PEAK_GBS, 4),
-                    "call_gbs": round(b.kv_bytes / ((dus + mus) * 1e-6) / 1e9, 1)}
-        print(f"bench: {key} decode {dus:.1f} us merge {mus:.1f} us", file=sys.stderr, flush=True)
-        del q, kp, vp, tab, lens, out, ws
-        torch.cuda.empty_cache()
+        e = {"workload": desc, "kv_bytes": b.kv_bytes, "decode_us": round(dus, 2),
+             "merge_us": round(mus, 2), "achieved_gbs": round(gbs, 1),
+             "frac": round(gbs / HBM_PEAK_GBS, 4), "step_p50_us": round(step, 2),
+             "step_gbs": round(b.kv_bytes / (step * 1e-6) / 1e9, 1)}
+        if aus:
+            e["append_us"] = round(aus, 2)
+        return e
+
+    # GQA batch at block size 32
+    b = W.config3(32)
+    t = stage(b)
+    dus, mus, aus, cus, step = _decode_timing(pkv, torch, lambda: decode_call(t), launches)
+    res["gqa256_b32"] = hbm_entry("GQA decode batch at block size 32 (as above), decode + merge",
+                                  b, dus, mus, 0, step)
+    del t
+    # multi-head fp16 batch
+    b = W.config2()
+    t = stage(b)
+    dus, mus, aus, cus, step = _decode_timing(pkv, torch, lambda: decode_call(t), launches)
+    res["mha64_fp16"] = hbm_entry("MHA decode batch: 64 sequences, 32/32 heads, head_dim 128, "
+                                  "fp16, block size 16, lengths uniform in [128, 2048]; decode + "
+                                  "merge", b, dus, mus, 0, step)
+    del t
+    # long contexts: one 8-token append (the current token of each sequence, rewritten) + decode
+    b = W.config5(steps=1)
+    t = stage(b)
+    kn, vn = (x.to(dev) for x in W.new_tokens(b.seed, 1, b.num_seqs, b.num_kv_heads,
+                                              b.head_dim, b.dtype))
+    sid = torch.arange(b.num_seqs, dtype=torch.int32, device=dev)
+    pos = (t["lens"] - 1).to(torch.int32)
+
+    def long_step():
+        pkv.kv_cache_append(t["kp"], t["vp"], kn, vn, sid, pos, t["tab"])
+        decode_call(t)
+    dus, mus, aus, cus, step = _decode_timing(pkv, torch, long_step, launches)
+    res["long8_bf16"] = hbm_entry("long contexts: 8 sequences, 64/8 heads, head_dim 128, bf16, "
+                                  "block size 16, lengths uniform in [16384, 32768]; step = "
+                                  "8-token append + decode + merge", b, dus, mus, aus, step)
+    del t
+    # shared prefix: 128 sequences over one 800-token prefix (logical bytes; the prefix blocks
+    # are re-read by every sharer, so caches serve most of them)
+    b = W.config4a()
+    t = stage(b)
+    dus, mus, aus, cus, step = _decode_timing(pkv, torch, lambda: decode_call(t), launches)
+    res["shared_prefix128"] = {
+        "workload": "shared prefix: 128 sequences, 800-token shared prefix + U{1..512} private "
+                    "tokens, 64/8 heads, head_dim 128, bf16, block size 16; decode + merge",
+        "logical_kv_bytes": b.kv_bytes, "decode_us": round(dus, 2), "merge_us": round(mus, 2),
+        "logical_gbs": round(b.kv_bytes / (dus * 1e-6) / 1e9, 1), "cache_assisted": True,
+        "step_p50_us": round(step, 2)}
+    del t
+    # copy-on-write pairs: copy 8 slots of each pair's shared partial block, append B's token,
+    # decode all 128 sequences (the copy and append rewrite the same slots every call)
+    b = W.config4b()
+    t = stage(b)
+    free = W.config4b_free_blocks(b)
+    npairs = b.num_seqs // 2
+    tab2 = b.tables.copy()
+    src, dst = [], []
+    for i in range(npairs):
+        src.append(int(b.tables[2 * i + 1][1]))
+        dst.append(free[i])
+        tab2[2 * i + 1][1] = free[i]
+    as_dev = lambda x: torch.tensor(x, dtype=torch.int32, device=dev)
+    dsrc, ddst, dn = as_dev(src), as_dev(dst), as_dev([8] * npairs)
+    dtab2 = torch.from_numpy(tab2).to(dev)
+    lens2 = torch.from_numpy(np.tile(np.array([24, 25], np.int32), npairs)).to(dev)
+    kn, vn = (x.to(dev) for x in W.new_tokens(b.seed, 1, npairs, b.num_kv_heads, b.head_dim,
+                                              b.dtype))
+    bsid, bpos = as_dev(list(range(1, 2 * npairs, 2))), as_dev([24] * npairs)
+
+    def cow_step():
+        pkv.cow_block_copy(t["kp"], t["vp"], dsrc, ddst, dn)
+        pkv.kv_cache_append(t["kp"], t["vp"], kn, vn, bsid, bpos, dtab2)
+        decode_call(t, tab=dtab2, lens=lens2, mx=25)
+    dus, mus, aus, cus, step = _decode_timing(pkv, torch, cow_step, launches)
+    res["cow_pairs64"] = {
+        "workload": "copy-on-write: 64 pairs sharing 24 tokens; per call copy 8 slots of each "
+                    "shared partial block, append B's token, decode 128 sequences",
+        "copy_us": round(cus, 2), "append_us": round(aus, 2), "decode_us": round(dus, 2),
+        "merge_us": round(mus, 2), "step_p50_us": round(step, 2), "roofline": None}
+    del t
+    # tiny: the pages' three requests (25, 47, 12 tokens), fp32
+    b = W.config1()
+    t = stage(b)
+    dus, mus, aus, cus, step = _decode_timing(pkv, torch, lambda: decode_call(t), launches)
+    res["tiny3_fp32"] = {"workload": "tiny: 3 sequences of 25, 47, 12 tokens, 4/4 heads, head_dim "
+                                     "64, fp32, block size 16", "decode_us": round(dus, 2),
+                         "merge_us": round(mus, 2), "step_p50_us": round(step, 2),
+                         "roofline": None}
+    del t
+    torch.cuda.empty_cache()
+    for k, v in res.items():
+        print(f"bench: {k} decode {v['decode_us']} us step p50 {v['step_p50_us']} us",
+              file=sys.stderr, flush=True)
     return res
+
+
+def stream_probe(pkv, torch, dev: str, gib: int = 2, launches: int = 20):
+    """Plain streaming-read bandwidth of this device (the library's probe kernel)."""
+    buf = torch.ones((gib << 30) // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        pkv.stream_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    pkv.timing_enable(True, every=1)
+    for _ in range(launches):
+        pkv.stream_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    ms, n = pkv.timing_query("stream_read")
+    pkv.timing_enable(False)
+    nbytes = buf.numel() * 4
+    del buf
+    torch.cuda.empty_cache()
+    us = ms / n * 1e3
+    return {"bytes": nbytes, "us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
+def cpu_baseline_multi(block_size: int, steps: int = 3):
+    """The oracle over a process pool (one worker per host core this process may use, at most
+    16), run in a child interpreter that never touches the GPU: same batch, same oracle,
+    sequences split across the workers. The workers see the batch as NumPy arrays (the 16-bit
+    values widened to fp32, exactly) and use no torch, so nothing threaded is forked."""
+    import subprocess
+    code = (
+        "import os, sys, time, json\n"
+        "os.environ['OMP_NUM_THREADS'] = os.environ['OPENBLAS_NUM_THREADS'] = '1'\n"
+        "sys.path.insert(0, %r)\n"
+        "import numpy as np, multiprocessing as mp, torch\n"
+        "import workloads as W, oracle\n"
+        "b = W.config3(%d)\n"
+        "q, kp, vp = (x.float().numpy() for x in (b.q, b.k_pool, b.v_pool))\n"
+        "tables, lengths, B, kvb, S = b.tables, b.lengths, b.block_size, b.kv_bytes, b.num_seqs\n"
+        "del b\n"
+        "def run(seqs):\n"
+        "    oracle.paged_decode(q, kp, vp, tables, lengths, B, seqs=seqs)\n"
+        "    return len(seqs)\n"
+        "n = min(16, len(os.sched_getaffinity(0)))\n"
+        "parts = [list(range(i, S, n)) for i in range(n)]\n"
+        "print('cpu baseline: %%d processes' %% n, file=sys.stderr, flush=True)\n"
+        "with mp.get_context('fork').Pool(n) as pool:\n"
+        "    pool.map_async(run, parts).get(timeout=120)\n"
+        "    t = time.perf_counter()\n"
+        "    for _ in range(%d):\n"
+        "        pool.map_async(run, parts).get(timeout=120)\n"
+        "        print('cpu baseline: step done', file=sys.stderr, flush=True)\n"
+        "    dt = (time.perf_counter() - t) / %d\n"
+        "print(json.dumps({'cores': n, 'step_s': dt, 'kv_bytes': kvb, 'S': S}))\n"
+    ) % (ROOT, block_size, steps, steps)
+    try:
+        r = subprocess.run([sys.executable, "-c", code], stdout=subprocess.PIPE, text=True,
+                           timeout=400)
+    except subprocess.TimeoutExpired:
+        return {"error": "timed out"}
+    if r.returncode != 0 or not r.stdout.strip():
+        return {"error": f"exit status {r.returncode}"}
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    return {"value": round(d["kv_bytes"] / d["step_s"] / 1e9, 4), "unit": "GB/s",
+            "cores": d["cores"], "kind": "oracle",
+            "sample": f"the full batch, {steps} decode steps after one warm-up, sequences split "
+                      f"over a pool of {d['cores']} processes (one BLAS thread each)",
+            "seq_steps_per_s": round(d["S"] / d["step_s"], 2)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -137,7 +319,7 @@ def main():
                     help="decode steps of the CPU oracle (about 0.7 s each on one core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
-                    help="skip the decode-kernel figures on the other batch configs")
+                    help="skip the figures on the other batch configs and the read probe")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -254,12 +436,30 @@ def main():
         },
         "setup_s": round(gen_s, 2),
     }
+    # step-time spread: torch events around every step (on the stream the library launches on)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(100)]
+    for a, e in ev:
+        a.record()
+        step()
+        e.record()
+    torch.cuda.synchronize()
+    st_us = sorted(a.elapsed_time(e) * 1e3 for a, e in ev)
+    result["step_us_percentiles"] = {"p10": round(st_us[10], 2), "p50": round(st_us[50], 2),
+                                     "p90": round(st_us[90], 2), "steps": len(st_us)}
     if not args.no_other_configs:
         del k_pool, v_pool, q, out, ws
         torch.cuda.empty_cache()
+        probe = stream_probe(pkv, torch, dev)
+        probe["decode_frac_of_probe"] = round(achieved / probe["gbs"], 4)
+        result["read_probe"] = probe
         result["other_configs"] = other_configs(pkv, W, torch, dev, args.workers)
     if not args.no_cpu_baseline:
+        print("bench: oracle on one core", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(b, args.cpu_steps)
+        print("bench: oracle on a process pool", file=sys.stderr, flush=True)
+        result["cpu_baseline"]["cpu_model"] = cpu_model()
+        result["cpu_baseline_multi"] = cpu_baseline_multi(args.block_size)
     print(json.dumps(result), flush=True)
 
 

@@ -202,6 +202,15 @@ int pkv_seq_release(pkv_pool* pool, const int32_t* table_row, int num_blocks_use
 int pkv_timing_enable(int on);
 int pkv_timing_query(const char* name, double* total_ms, int64_t* launches);
 
+/* Streaming-read probe (measurement only): one kernel that reads `bytes` of device memory at
+ * `src` once with 16-byte loads, so that a benchmark can report the decode bandwidth as a
+ * fraction of what plain reads reach on the same device as well as of the vendor peak.
+ *   src    device, 16-byte aligned; bytes a positive multiple of 16
+ *   sink   device uint32, written only in a case that does not occur (keeps the loads alive)
+ * Asynchronous on `stream`; time it with events or pkv_timing_query("stream_read").
+ * PKV_ERR_INVALID_ARG for null pointers, misalignment or a bad size. */
+int pkv_stream_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* Contract validation on (1) or off (0) for this process, overriding PAGEDKV_VALIDATE. */
 int pkv_set_validate(int on);
 

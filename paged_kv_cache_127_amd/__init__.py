@@ -74,6 +74,7 @@ def _declare(L):
         "pkv_timing_enable": (c_int, [c_int]),
         "pkv_set_validate": (c_int, [c_int]),
         "pkv_timing_query": (c_int, [ctypes.c_char_p, P(ctypes.c_double), P(ctypes.c_int64)]),
+        "pkv_stream_read_probe": (c_int, [c_void, c_size, c_void, c_void]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -212,6 +213,13 @@ def cow_block_copy(k_pool, v_pool, src_blocks, dst_blocks, num_tokens=None, stre
         _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype), _kv_dtype(k_pool),
         _dev(src_blocks, "src_blocks", torch.int32), _dev(dst_blocks, "dst_blocks", torch.int32),
         nt, n, Hkv, d, B, N, _stream(stream)))
+
+
+def stream_read_probe(src: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Read all of ``src`` once with plain 16-byte loads (C: ``pkv_stream_read_probe``)."""
+    nbytes = src.numel() * src.element_size()
+    _check(load_library().pkv_stream_read_probe(_dev(src, "src"), nbytes,
+                                                _dev(sink, "sink", torch.int32), _stream(stream)))
 
 
 def set_validate(on: bool = True):

@@ -438,4 +438,16 @@ int pkv_timing_query(const char* name, double* total_ms, int64_t* launches) {
   return ok();
 }
 
+int pkv_stream_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink) return fail(PKV_ERR_INVALID_ARG, "pkv_stream_read_probe: null pointer");
+  if (bytes == 0 || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(src) & 15))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_stream_read_probe: %zu bytes / alignment", bytes);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int cus = cu_count();
+  hipError_t e = timed("stream_read", st,
+                       [&] { return pkv::launch_stream_read(src, bytes, sink, cus, st); });
+  if (e != hipSuccess) return launch_error(e, "pkv_stream_read_probe");
+  return ok();
+}
+
 }  // extern "C"

@@ -80,4 +80,8 @@ struct CowParams {
 };
 hipError_t launch_cow(const CowParams& p, int elem_bytes, hipStream_t st);
 
+// Streaming-read probe (probe.hip): reads `bytes` (multiple of 16) of src once.
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int num_cus,
+                              hipStream_t st);
+
 }  // namespace pkv
