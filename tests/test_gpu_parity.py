@@ -431,3 +431,14 @@ def test_validation_mode_reports_errors():
         assert max_err(db.decode(), oracle_decode(b)) <= 1e-5   # valid calls still pass
     finally:
         pkv.set_validate(False)
+
+
+def test_stream_read_probe_runs():
+    """The measurement probe reads a buffer and leaves the sink alone (its data never XORs to
+    the magic value)."""
+    buf = torch.ones(1 << 22, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pkv.stream_read_probe(buf, sink)
+    pkv.stream_read_probe(buf[: (1 << 22) - 4 * 37], sink)   # ragged tail of the slices
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0

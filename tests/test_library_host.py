@@ -141,3 +141,15 @@ def test_append_and_cow_argument_checks():
     assert L.kv_cache_append(1, 1, 2, 1, 1, 1, 1, 0, 1, 4, 2, 8, 128, 16, 64, None) == 0
     assert L.cow_block_copy(1, 1, 2, None, 1, None, 3, 8, 128, 16, 64, None) == -1
     assert L.cow_block_copy(1, 1, 2, 1, 1, None, 0, 8, 128, 16, 64, None) == 0
+
+
+def test_append_size_limit_and_probe_argument_checks():
+    """Host-side rejections, no kernel launched: an append whose rows exceed 2^31 elements,
+    and the read probe with a null pointer, a size that is not a multiple of 16 or a
+    misaligned source."""
+    L = pkv.load_library()
+    assert L.kv_cache_append(1, 1, 2, 1, 1, 1, 1, 1 << 24, 1, 4, 2, 8, 128, 16, 64, None) == -2
+    assert L.pkv_stream_read_probe(None, 1024, 16, None) == -1
+    assert L.pkv_stream_read_probe(256, 1000, 16, None) == -1
+    assert L.pkv_stream_read_probe(264, 1024, 16, None) == -1
+    assert L.pkv_stream_read_probe(256, 0, 16, None) == -1
