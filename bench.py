@@ -161,16 +161,15 @@ def other_configs(pkv, W, torch, dev: str, workers: int, launches: int = 30):
     t = stage(b)
     kn, vn = (x.to(dev) for x in W.new_tokens(b.seed, 1, b.num_seqs, b.num_kv_heads,
                                               b.head_dim, b.dtype))
-    sid = torch.arange(b.num_seqs, dtype=torch.int32, device=dev)
-    pos = (t["lens"] - 1).to(torch.int32)
 
     def long_step():
-        pkv.kv_cache_append(t["kp"], t["vp"], kn, vn, sid, pos, t["tab"])
-        decode_call(t)
+        pkv.paged_attn_decode_append(t["out"], t["q"], t["kp"], t["vp"], kn, vn, t["tab"],
+                                     t["lens"], t["mx"], num_workers=workers, workspace=t["ws"])
     dus, mus, aus, cus, step = _decode_timing(pkv, torch, long_step, launches)
     res["long8_bf16"] = hbm_entry("long contexts: 8 sequences, 64/8 heads, head_dim 128, bf16, "
                                   "block size 16, lengths uniform in [16384, 32768]; step = "
-                                  "8-token append + decode + merge", b, dus, mus, aus, step)
+                                  "decode with the 8-token append fused in + merge", b, dus, mus,
+                                  aus, step)
     del t
     # shared prefix: 128 sequences over one 800-token prefix (logical bytes; the prefix blocks
     # are re-read by every sharer, so caches serve most of them)
@@ -361,7 +360,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # One decode step: every sequence appends its newest token (position L - 1; the same slot
+    # each step, so the batch stays the same) and all sequences decode. The timed step is the
+    # fused call; the same work as two calls (kv_cache_append, then paged_attn_decode) is
+    # timed afterwards for comparison.
     def step():
+        pkv.paged_attn_decode_append(out, q, k_pool, v_pool, k_new, v_new, tables, lens, max_ctx,
+                                     num_workers=args.workers, workspace=ws)
+
+    def step_two_calls():
         pkv.kv_cache_append(k_pool, v_pool, k_new, v_new, seq_ids, positions, tables)
         pkv.paged_attn_decode(out, q, k_pool, v_pool, tables, lens, max_ctx,
                               num_workers=args.workers, workspace=ws)
@@ -381,7 +388,20 @@ def main():
     t1 = time.perf_counter()
     kernel_ms, kernel_n = pkv.timing_query("decode_partial")
     reduce_ms, reduce_n = pkv.timing_query("splitk_reduce")
+    pkv.timing_enable(False)
+
+    # the same step as two calls
+    for _ in range(args.warmup):
+        step_two_calls()
+    torch.cuda.synchronize()
+    pkv.timing_enable(True, every=TIMING_EVERY)
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        step_two_calls()
+    torch.cuda.synchronize()
+    two_ms = (time.perf_counter() - t2) * 1e3 / args.steps
     append_ms, append_n = pkv.timing_query("append")
+    dec2_ms, dec2_n = pkv.timing_query("decode_partial")
     pkv.timing_enable(False)
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -409,7 +429,8 @@ def main():
                          f"head_dim {d}, bf16 cache, block size {args.block_size}, log-normal "
                          "context lengths (median 512, sigma 1, clipped to [16, 4096]), seeded "
                          "random block placement in a 1.25x pool; one appended token per "
-                         "sequence per step"),
+                         "sequence per step (paged_attn_decode_append: append fused into the "
+                         "decode kernel)"),
             "num_seqs": S,
             "sum_context_tokens": int(b.lengths.sum()),
             "block_size": args.block_size,
@@ -432,7 +453,13 @@ def main():
         },
         "other_kernels_avg_us": {
             "splitk_reduce": round(reduce_ms / max(reduce_n, 1) * 1e3, 3),
-            "append": round(append_ms / max(append_n, 1) * 1e3, 3),
+        },
+        "two_calls": {
+            "what": "the same step as kv_cache_append + paged_attn_decode",
+            "ms_per_step": round(two_ms, 5),
+            "value": round(kv_bytes / (two_ms * 1e-3) / 1e9, 2),
+            "decode_kernel_us": round(dec2_ms / max(dec2_n, 1) * 1e3, 3),
+            "append_kernel_us": round(append_ms / max(append_n, 1) * 1e3, 3),
         },
         "setup_s": round(gen_s, 2),
     }

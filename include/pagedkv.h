@@ -122,6 +122,27 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Decode step with the step's append fused in: the same result, in the pools and in `out`,
+ * as kv_cache_append of one token per sequence -- k_new[s] / v_new[s] at position
+ * context_lens[s] - 1, for every s with context_lens[s] >= 1 -- followed by
+ * paged_attn_decode, in one launch less ([P1] "Growing a request": a generated token's keys and
+ * values join the cache and the next query attends to them). The worker that computes the
+ * step holding that position reads the row from k_new / v_new; the rows are stored into their
+ * slots by the same kernel. The table must already map position context_lens[s] - 1 (the host
+ * grows it first, as for kv_cache_append); a slot whose table entry is out of range is not
+ * written and, as in paged_attn_decode, that sequence's row comes out NaN.
+ *   k_new, v_new  device [num_seqs][num_kv_heads][head_dim], element type kv_dtype
+ *   other arguments as for paged_attn_decode; k_pool and v_pool are written.
+ * --------------------------------------------------------------------------------------- */
+int paged_attn_decode_append(void* out, int out_dtype, const void* q, void* k_pool, void* v_pool,
+                             int kv_dtype, const void* k_new, const void* v_new,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* context_lens, int max_context_len, int num_seqs,
+                             int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                             int num_blocks, float scale, int num_workers, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Append: store the keys and values of new tokens into their slots
  * ([P1] "Growing a request"; [P2] "KV Cache Fundamentals": the cache grows by one row per
  * head per generated token). For every i < num_tokens and KV head g:

@@ -55,6 +55,10 @@ def _declare(L):
         "paged_attn_decode": (c_int, [c_void, c_int, c_void, c_void, c_void, c_int, c_void, c_int,
                                       c_void, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                       c_float, c_int, c_void, c_size, c_void]),
+        "paged_attn_decode_append": (c_int, [c_void, c_int, c_void, c_void, c_void, c_int, c_void,
+                                             c_void, c_void, c_int, c_void, c_int, c_int, c_int,
+                                             c_int, c_int, c_int, c_int, c_float, c_int, c_void,
+                                             c_size, c_void]),
         "kv_cache_append": (c_int, [c_void, c_void, c_int, c_void, c_void, c_void, c_void, c_int,
                                     c_void, c_int, c_int, c_int, c_int, c_int, c_int, c_void]),
         "cow_block_copy": (c_int, [c_void, c_void, c_int, c_void, c_void, c_void, c_int, c_int,
@@ -175,6 +179,38 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
         int(block_tables.shape[1]), _dev(context_lens, "context_lens", torch.int32),
         int(max_context_len), S, Hq, Hkv, d, B, N, float(scale), int(num_workers), ws_ptr,
         ws_bytes, _stream(stream)))
+    return out
+
+
+def paged_attn_decode_append(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
+                             v_pool: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                             block_tables: torch.Tensor, context_lens: torch.Tensor,
+                             max_context_len: int, scale: float = 0.0, num_workers: int = 0,
+                             workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Append k_new[s] / v_new[s] ([S][H_kv][d]) at position context_lens[s] - 1 and decode,
+    in one call (C: ``paged_attn_decode_append``). Other arguments as paged_attn_decode."""
+    L = load_library()
+    kdt = _kv_dtype(k_pool)
+    if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape or out.shape != q.shape:
+        raise ValueError("bad tensor ranks or out shape; k_pool and v_pool must match")
+    S, Hq, d = q.shape
+    N, Hkv, B, d2 = k_pool.shape
+    if d2 != d or tuple(k_new.shape) != (S, Hkv, d) or tuple(v_new.shape) != (S, Hkv, d):
+        raise ValueError("k_new/v_new must be [S][H_kv][d]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+        raise ValueError("block_tables must be [S][max_blocks] and context_lens [S]")
+    if out.dtype not in (torch.float32, k_pool.dtype):
+        raise TypeError("out must be float32 or the cache dtype")
+    if workspace is None:
+        workspace = decode_workspace(S, Hq, Hkv, d, num_workers, q.device)
+    _check(L.paged_attn_decode_append(
+        _dev(out, "out"), _DT[out.dtype], _dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool", k_pool.dtype), kdt, _dev(k_new, "k_new", k_pool.dtype),
+        _dev(v_new, "v_new", k_pool.dtype), _dev(block_tables, "block_tables", torch.int32),
+        int(block_tables.shape[1]), _dev(context_lens, "context_lens", torch.int32),
+        int(max_context_len), S, Hq, Hkv, d, B, N, float(scale), int(num_workers),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
     return out
 
 

@@ -182,29 +182,36 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
       .total;
 }
 
-int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_pool,
-                      const void* v_pool, int kv_dtype, const int32_t* block_tables,
-                      int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
-                      int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                      int block_size, int num_blocks, float scale, int num_workers,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Decode (paged_attn_decode), optionally with each sequence's newest token taken from k_new /
+// v_new and stored into its slot by the same kernel (paged_attn_decode_append).
+int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const void* k_pool,
+                const void* v_pool, int kv_dtype, const void* k_new, const void* v_new,
+                const int32_t* block_tables, int max_blocks_per_seq,
+                const int32_t* context_lens, int max_context_len, int num_seqs,
+                int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                float scale, int num_workers, void* workspace, size_t workspace_bytes,
+                void* stream) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
       num_blocks <= 0 || max_context_len < 0)
-    return fail(PKV_ERR_INVALID_ARG, "paged_attn_decode: non-positive size");
+    return fail(PKV_ERR_INVALID_ARG, "%s: non-positive size", fn);
   if (num_seqs == 0) return ok();
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
-    return fail(PKV_ERR_INVALID_ARG, "paged_attn_decode: null pointer");
+    return fail(PKV_ERR_INVALID_ARG, "%s: null pointer", fn);
   if (elem_bytes(kv_dtype) == 0)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: kv_dtype %d", kv_dtype);
+    return fail(PKV_ERR_UNSUPPORTED, "%s: kv_dtype %d", fn, kv_dtype);
   if (!(out_dtype == PKV_F32 || out_dtype == kv_dtype))
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: out_dtype %d with kv_dtype %d",
+    return fail(PKV_ERR_UNSUPPORTED, "%s: out_dtype %d with kv_dtype %d", fn,
                 out_dtype, kv_dtype);
   if (head_dim != 64 && head_dim != 128)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: head_dim %d (64 or 128)", head_dim);
+    return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128)", fn, head_dim);
   if (block_size != 16 && block_size != 32)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: block_size %d (16 or 32)", block_size);
+    return fail(PKV_ERR_UNSUPPORTED, "%s: block_size %d (16 or 32)", fn, block_size);
   if (num_q_heads % num_kv_heads != 0)
-    return fail(PKV_ERR_INVALID_ARG, "paged_attn_decode: %d query heads not a multiple of %d KV heads",
+    return fail(PKV_ERR_INVALID_ARG, "%s: %d query heads not a multiple of %d KV heads", fn,
                 num_q_heads, num_kv_heads);
   const int G = num_q_heads / num_kv_heads;
   const bool wide = kv_dtype != PKV_F32;
@@ -214,17 +221,17 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
   } else if (G == 1 || (!wide && (G == 2 || G == 4 || G == 8))) {
     use_mfma = false;
   } else {
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: %d query heads per KV head", G);
+    return fail(PKV_ERR_UNSUPPORTED, "%s: %d query heads per KV head", fn, G);
   }
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return fail(PKV_ERR_INVALID_ARG,
-                "paged_attn_decode: max_context_len %d exceeds table capacity %d x %d",
+                "%s: max_context_len %d exceeds table capacity %d x %d", fn,
                 max_context_len, max_blocks_per_seq, block_size);
   if (num_seqs > pkv::kMaxSeqsPerCall)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: %d sequences (at most %d per call)",
+    return fail(PKV_ERR_UNSUPPORTED, "%s: %d sequences (at most %d per call)", fn,
                 num_seqs, pkv::kMaxSeqsPerCall);
   if (num_workers < 0 || num_workers > (1 << 20))
-    return fail(PKV_ERR_INVALID_ARG, "paged_attn_decode: num_workers %d", num_workers);
+    return fail(PKV_ERR_INVALID_ARG, "%s: num_workers %d", fn, num_workers);
   const int waves_env = env_int("PAGEDKV_DECODE_WAVES", 4);
   const int waves = (waves_env == 1 || waves_env == 2 || waves_env == 4) ? waves_env : 4;
   int n = num_workers;
@@ -245,21 +252,21 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
     const double weight_max = (double)num_kv_heads * num_seqs *
                               (4.0 * ((double)max_context_len / 32.0 + 1.0) + pw);
     if (weight_max * (double)n >= 4.0e18)
-      return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: problem too large for one call");
+      return fail(PKV_ERR_UNSUPPORTED, "%s: problem too large for one call", fn);
   }
   const WsLayout wl = ws_layout(num_seqs, G, head_dim, n);
   if (!workspace || workspace_bytes < wl.total)
-    return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "paged_attn_decode: workspace %zu < %zu bytes",
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", fn,
                 workspace_bytes, wl.total);
   if (reinterpret_cast<uintptr_t>(workspace) & 255)
-    return fail(PKV_ERR_INVALID_ARG, "paged_attn_decode: workspace not 256-byte aligned");
+    return fail(PKV_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
   if (validate_mode()) {
     std::vector<int32_t> lens, tabs;
     if (!copy_ints(lens, context_lens, num_seqs, st) ||
         !copy_ints(tabs, block_tables, (size_t)num_seqs * max_blocks_per_seq, st))
-      return fail(PKV_ERR_LAUNCH, "paged_attn_decode: validation copy failed");
+      return fail(PKV_ERR_LAUNCH, "%s: validation copy failed", fn);
     for (int s = 0; s < num_seqs; ++s) {
       if (lens[s] < 0 || lens[s] > max_context_len)
         return fail(PKV_ERR_VALIDATION, "context_lens[%d] = %d outside [0, %d]", s, lens[s],
@@ -279,6 +286,10 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
   p.q = q;
   p.k_pool = k_pool;
   p.v_pool = v_pool;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k_pool_w = k_new ? const_cast<void*>(k_pool) : nullptr;
+  p.v_pool_w = k_new ? const_cast<void*>(v_pool) : nullptr;
   p.tables = block_tables;
   p.lens = context_lens;
   p.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
@@ -311,12 +322,44 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
       return pkv::launch_decode_valu(p, kv_dtype, head_dim, block_size, G, waves, st);
     });
   }
-  if (e != hipSuccess) return launch_error(e, "paged_attn_decode: decode kernel");
+  if (e != hipSuccess)
+    return fail(PKV_ERR_LAUNCH, "%s: decode kernel: %s", fn, hipGetErrorString(e));
   e = timed("splitk_reduce", st,
             [&] { return pkv::launch_splitk_reduce(p, kv_dtype, head_dim, st); });
   if (e != hipSuccess)
-    return launch_error(e, "paged_attn_decode: merge kernel");
+    return fail(PKV_ERR_LAUNCH, "%s: merge kernel: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_pool,
+                      const void* v_pool, int kv_dtype, const int32_t* block_tables,
+                      int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                      int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, float scale, int num_workers,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl("paged_attn_decode", out, out_dtype, q, k_pool, v_pool, kv_dtype, nullptr,
+                     nullptr, block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                     num_workers, workspace, workspace_bytes, stream);
+}
+
+int paged_attn_decode_append(void* out, int out_dtype, const void* q, void* k_pool, void* v_pool,
+                             int kv_dtype, const void* k_new, const void* v_new,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* context_lens, int max_context_len, int num_seqs,
+                             int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                             int num_blocks, float scale, int num_workers, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new))
+    return fail(PKV_ERR_INVALID_ARG, "paged_attn_decode_append: null pointer");
+  return decode_impl("paged_attn_decode_append", out, out_dtype, q, k_pool, v_pool, kv_dtype,
+                     k_new, v_new, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, scale, num_workers, workspace, workspace_bytes, stream);
 }
 
 int kv_cache_append(void* k_pool, void* v_pool, int kv_dtype, const void* k_new,

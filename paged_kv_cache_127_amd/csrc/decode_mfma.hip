@@ -207,23 +207,35 @@ void decode_mfma(DecodeParams p) {
     const int b1 = valid_block(si.b1, p.num_blocks) ? si.b1 : 0;   // then poison
     const char* t0 = kbase + ((size_t)b0 * Hkv + si.g) * kv_block_stride;
     const char* t1 = kbase + ((size_t)b1 * Hkv + si.g) * kv_block_stride;
-    const char* ka = (B == 16 && tokA0 >= 16) ? t1 : t0;
-    const char* kb = (B == 16 && tokA0 + 4 >= 16) ? t1 : t0;
+    const char* ka = ((B == 16 && tokA0 >= 16) ? t1 : t0) + kofs0;
+    const char* kb = ((B == 16 && tokA0 + 4 >= 16) ? t1 : t0) + kofs1;
+    if (p.k_new && si.k == si.ns - 1) {   // fused append: the newest token's row from k_new
+      const int tn = si.L - 1 - 32 * si.k;
+      const char* kn = reinterpret_cast<const char*>(p.k_new) +
+                       ((size_t)si.s * Hkv + si.g) * RB + 8 * jg * ES;
+      if (tokA0 == tn) ka = kn;
+      if (tokA0 + 4 == tn) kb = kn;
+    }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      r.k[0][c] = load16(ka + kofs0 + 32 * c * ES);
-      r.k[1][c] = load16(kb + kofs1 + 32 * c * ES);
+      r.k[0][c] = load16(ka + 32 * c * ES);
+      r.k[1][c] = load16(kb + 32 * c * ES);
     }
   };
   auto load_v = [&](StepRegs<D>& r, const StepInfo& si) {
     const int b0 = valid_block(si.b0, p.num_blocks) ? si.b0 : 0;
     const int b1 = valid_block(si.b1, p.num_blocks) ? si.b1 : 0;
+    const bool sub = p.k_new && si.k == si.ns - 1;   // fused append (see load_kq)
+    const int tn = si.L - 1 - 32 * si.k;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int t = VTPI * f + vrow;
       const int blk = (B == 16 && t >= 16) ? b1 : b0;
-      r.v[f] = load16(vbase + ((size_t)blk * Hkv + si.g) * kv_block_stride +
-                      (size_t)(t & (B - 1)) * RB + 16 * vch);
+      const char* a = vbase + ((size_t)blk * Hkv + si.g) * kv_block_stride +
+                      (size_t)(t & (B - 1)) * RB + 16 * vch;
+      if (sub && t == tn)
+        a = reinterpret_cast<const char*>(p.v_new) + ((size_t)si.s * Hkv + si.g) * RB + 16 * vch;
+      r.v[f] = load16(a);
     }
   };
 
@@ -239,8 +251,8 @@ void decode_mfma(DecodeParams p) {
       const int kind = (int)(tag & 3);
       if (kind == 2 && lane < G) {
         const int64_t slot = tag >> 2;
-        p.ws_m[slot * G + lane] = so[G * D + lane];
-        p.ws_l[slot * G + lane] = so[G * D + G + lane];
+        store_nt(p.ws_m + slot * G + lane, so[G * D + lane]);
+        store_nt(p.ws_l + slot * G + lane, so[G * D + G + lane]);
       }
 #pragma unroll
       for (int k = 0; k < (16 * D / 4) / 64; ++k) {
@@ -248,16 +260,15 @@ void decode_mfma(DecodeParams p) {
         if (e4 < n4) {
           const f32x4 o = *reinterpret_cast<const f32x4*>(so + 4 * e4);
           if (kind == 0) {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + dst + 4 * e4) = o;
+            store_nt(reinterpret_cast<float*>(p.out) + dst + 4 * e4, o);
           } else if (kind == 1) {
             const uint32_t w0 = (uint32_t)Elem<T>::from_f32(o[0]) |
                                 ((uint32_t)Elem<T>::from_f32(o[1]) << 16);
             const uint32_t w1 = (uint32_t)Elem<T>::from_f32(o[2]) |
                                 ((uint32_t)Elem<T>::from_f32(o[3]) << 16);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + dst + 4 * e4) =
-                make_uint2(w0, w1);
+            store_nt(reinterpret_cast<uint16_t*>(p.out) + dst + 4 * e4, u32x2{w0, w1});
           } else {
-            *reinterpret_cast<f32x4*>(p.ws_acc + dst + 4 * e4) = o;
+            store_nt(p.ws_acc + dst + 4 * e4, o);
           }
         }
       }

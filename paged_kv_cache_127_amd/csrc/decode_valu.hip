@@ -100,14 +100,19 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
                                (size_t)ch * EPC) * ES);
     const int b0 = valid_block(si.b0, p.num_blocks) ? si.b0 : 0;   // out-of-range: block 0,
     const int b1 = valid_block(si.b1, p.num_blocks) ? si.b1 : 0;   // then poison
+    // fused append: the newest token's rows come from k_new / v_new
+    const bool sub = p.k_new && si.k == si.ns - 1;
+    const int tn = si.L - 1 - 32 * si.k;
+    const size_t nofs = ((size_t)si.s * Hkv + si.g) * D * ES + (size_t)ch * 16;
 #pragma unroll
     for (int c = 0; c < NI; ++c) {
       const int tt = TPI * c + row;
       const int blk = (B == 16 && tt >= 16) ? b1 : b0;
       const size_t ofs = ((size_t)blk * Hkv + si.g) * blk_stride +
                          (size_t)(tt & (B - 1)) * D * ES + (size_t)ch * 16;
-      r.k[c] = load16(kbase + ofs);
-      r.v[c] = load16(vbase + ofs);
+      const bool nw = sub && tt == tn;
+      r.k[c] = load16(nw ? reinterpret_cast<const char*>(p.k_new) + nofs : kbase + ofs);
+      r.v[c] = load16(nw ? reinterpret_cast<const char*>(p.v_new) + nofs : vbase + ofs);
     }
   };
 
@@ -212,8 +217,8 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
               float* op = reinterpret_cast<float*>(p.out) + orow * D + d0;
 #pragma unroll
               for (int e4 = 0; e4 < EPC; e4 += 4)
-                *reinterpret_cast<f32x4*>(op + e4) =
-                    f32x4{o[e4] * inv, o[e4 + 1] * inv, o[e4 + 2] * inv, o[e4 + 3] * inv};
+                store_nt(op + e4,
+                         f32x4{o[e4] * inv, o[e4 + 1] * inv, o[e4 + 2] * inv, o[e4 + 3] * inv});
             } else {
               if constexpr (ES == 2) {
                 u32x4 w;
@@ -221,21 +226,20 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
                 for (int u = 0; u < 4; ++u)
                   w[u] = (uint32_t)scaled_to_16<T>(o[2 * u], inv) |
                          ((uint32_t)scaled_to_16<T>(o[2 * u + 1], inv) << 16);
-                *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.out) + orow * D + d0) = w;
+                store_nt(reinterpret_cast<uint16_t*>(p.out) + orow * D + d0, w);
               }
             }
           }
         } else {
           const size_t pr = slot * G + h;
           if (lane == 0) {
-            p.ws_m[pr] = m_run[h];
-            p.ws_l[pr] = l_tot;
+            store_nt(p.ws_m + pr, m_run[h]);
+            store_nt(p.ws_l + pr, l_tot);
           }
           if (row == 0) {
 #pragma unroll
             for (int e4 = 0; e4 < EPC; e4 += 4)
-              *reinterpret_cast<f32x4*>(p.ws_acc + pr * D + d0 + e4) =
-                  f32x4{o[e4], o[e4 + 1], o[e4 + 2], o[e4 + 3]};
+              store_nt(p.ws_acc + pr * D + d0 + e4, f32x4{o[e4], o[e4 + 1], o[e4 + 2], o[e4 + 3]});
           }
         }
       }

@@ -44,23 +44,52 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
   const int64_t ns = uni(p.prefix[s + 1]) - uni(p.prefix[s]);
   const size_t base = ((size_t)s * p.num_q_heads + (size_t)g * G) * D;
 
+  // Fused append (k_new set): the segment's newest row -- token L - 1, keys on lanes [0, LPR),
+  // values on [LPR, 2 LPR), 16 bytes per lane -- goes into its slot here, after the decode
+  // kernel (which took that row from k_new / v_new) has finished: nothing in this call reads
+  // the slot any more. The length, the new data and then the table entry are loaded alongside
+  // the merge's own loads; a slot whose table entry is out of range is not written.
+  constexpr int RB = D * (int)sizeof(T);   // bytes per row
+  constexpr int LPR = RB / 16;
+  const bool app = p.k_new != nullptr && wave == 0 && lane < 2 * LPR;
+  const int kvsel = lane < LPR ? 0 : 1;
+  const int ch = lane % LPR;
+  int Lnew = 0, blk = -1;
+  u32x4 xnew = u32x4{0u, 0u, 0u, 0u};
+  if (app) {
+    const int cap = min(p.max_context_len, p.max_blocks * p.block_size);
+    Lnew = clamp_len(p.lens[s], cap);
+    if (Lnew > 0) {
+      xnew = load16(reinterpret_cast<const char*>(kvsel ? p.v_new : p.k_new) +
+                    ((size_t)s * Hkv + g) * RB + 16 * ch);
+      blk = p.tables[(size_t)s * p.max_blocks + (Lnew - 1) / p.block_size];
+    }
+  }
+  auto append_store = [&]() {
+    if (app && Lnew > 0 && valid_block(blk, p.num_blocks)) {
+      const int off = (Lnew - 1) % p.block_size;
+      char* dst = reinterpret_cast<char*>(kvsel ? p.v_pool_w : p.k_pool_w) +
+                  (((size_t)blk * Hkv + g) * p.block_size + off) * RB + 16 * ch;
+      *reinterpret_cast<u32x4*>(dst) = xnew;
+    }
+  };
+
   // o * sc to the output (16-bit: the fp32 value rounded, see scaled_to_16)
   auto store = [&](int e4, f32x4 o, float sc) {
     if (p.out_f32) {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + base + 4 * e4) = o * sc;
+      store_nt(reinterpret_cast<float*>(p.out) + base + 4 * e4, o * sc);
     } else {
       if constexpr (sizeof(T) == 2) {
         const uint32_t w0 = (uint32_t)scaled_to_16<T>(o[0], sc) |
                             ((uint32_t)scaled_to_16<T>(o[1], sc) << 16);
         const uint32_t w1 = (uint32_t)scaled_to_16<T>(o[2], sc) |
                             ((uint32_t)scaled_to_16<T>(o[3], sc) << 16);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + base + 4 * e4) =
-            make_uint2(w0, w1);
+        store_nt(reinterpret_cast<uint16_t*>(p.out) + base + 4 * e4, u32x2{w0, w1});
       }
     }
   };
 
-  if (ns == 0) {   // empty sequence: zero rows
+  if (ns == 0) {   // empty sequence: zero rows (and no new row: its length is 0)
     if (wave == 0) {
 #pragma unroll
       for (int k = 0; k < KMAX; ++k)
@@ -75,7 +104,10 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
   const int64_t first = ws0 + line.pw;                                 // weighted start of step 0
   const int rf = line.owner(first);
   const int rl = line.owner(first + kStepWeight * (ns - 1));
-  if (rf == rl) return;   // one range holds the whole segment: written by the decode kernel
+  if (rf == rl) {   // one range holds the whole segment: written by the decode kernel
+    append_store();
+    return;
+  }
 
   // Slot of range r's piece of this segment, or -1 if r holds none of its steps. rf's piece is
   // its first one (slot 2 rf) unless rf also holds the previous segment's last step, which
@@ -136,6 +168,7 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
         M[k] = m_new;
       }
   }
+  append_store();
   if constexpr (WPS == 1) {
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {

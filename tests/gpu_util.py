@@ -39,6 +39,22 @@ class DeviceBatch:
         torch.cuda.synchronize()
         return out.cpu()
 
+    def decode_append(self, k_new, v_new, q=None, workers=0, lens=None, max_ctx=None,
+                      tables=None):
+        """paged_attn_decode_append with NaN-filled output and workspace (as decode())."""
+        q = self.q if q is None else q
+        out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=q.device)
+        S, Hq, d = q.shape
+        ws = torch.full((pkv.pkv_decode_workspace_size(S, Hq, self.k_pool.shape[1], d, workers),),
+                        255, dtype=torch.uint8, device=q.device)
+        pkv.paged_attn_decode_append(out, q, self.k_pool, self.v_pool, k_new, v_new,
+                                     self.tables if tables is None else tables,
+                                     self.lens if lens is None else lens,
+                                     self.max_ctx if max_ctx is None else max_ctx,
+                                     num_workers=workers, workspace=ws)
+        torch.cuda.synchronize()
+        return out.cpu()
+
 
 def oracle_decode(b, q=None, seqs=None, k_pool=None, v_pool=None, tables=None, lengths=None):
     return oracle.paged_decode(b.q if q is None else q,

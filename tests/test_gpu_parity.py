@@ -442,3 +442,94 @@ def test_stream_read_probe_runs():
     pkv.stream_read_probe(buf[: (1 << 22) - 4 * 37], sink)   # ragged tail of the slices
     torch.cuda.synchronize()
     assert int(sink.item()) == 0
+
+
+# ---- decode with the step's append fused in ----------------------------------------------
+@pytest.mark.parametrize("case", [("bf16", 16, 2, 128, 16), ("bf16", 64, 8, 128, 32),
+                                  ("f16", 4, 4, 128, 16), ("f32", 8, 2, 64, 16),
+                                  ("f16", 16, 4, 64, 32)], ids=str)
+@pytest.mark.parametrize("workers", [0, 1, 5, 5000])
+def test_decode_append_equals_append_then_decode(case, workers):
+    """The fused call leaves the pools bit-identical to kv_cache_append of each sequence's
+    newest token, and its output is bit-identical to paged_attn_decode after that append (and
+    within tolerance of the oracle). The ragged lengths put the new token at every boundary
+    of a 32-token step and of a block, including a one-token context."""
+    dt, hq, hkv, d, B = case
+    b = W.small_batch(RAGGED, hq, hkv, d, B, DT[dt], seed=81, poison=True)
+    S = b.num_seqs
+    k_new, v_new = W.new_tokens(b.seed, 3, S, hkv, d, DT[dt])
+    pos = b.lengths.astype(np.int32) - 1
+    two = DeviceBatch(b)
+    pkv.kv_cache_append(two.k_pool, two.v_pool, k_new.cuda(), v_new.cuda(),
+                        torch.arange(S, dtype=torch.int32, device="cuda"),
+                        torch.from_numpy(pos).cuda(), two.tables)
+    ref_out = two.decode(workers=workers)
+    one = DeviceBatch(b)
+    got = one.decode_append(k_new.cuda(), v_new.cuda(), workers=workers)
+    assert torch.equal(bits(one.k_pool.cpu()), bits(two.k_pool.cpu()))
+    assert torch.equal(bits(one.v_pool.cpu()), bits(two.v_pool.cpu()))
+    assert torch.equal(bits(got), bits(ref_out))
+    kr, vr = b.k_pool.clone(), b.v_pool.clone()
+    for s in range(S):
+        blk, off = oracle.token_address(int(pos[s]), b.tables[s], B)
+        kr[blk, :, off] = k_new[s]
+        vr[blk, :, off] = v_new[s]
+    assert torch.equal(bits(one.k_pool.cpu()), bits(kr)) and torch.equal(bits(one.v_pool.cpu()), bits(vr))
+    ref = oracle.paged_decode(b.q, kr, vr, b.tables, b.lengths, B)
+    assert max_err(got, ref) <= TOL[DT[dt]]
+
+
+def test_decode_append_long_context_steps():
+    """Long contexts (split across many ranges), three steps of the fused call, each appending
+    one token per sequence and decoding, against the oracle; pools bit-exact."""
+    steps = 3
+    b = W.config5(steps=steps)
+    db = DeviceBatch(b)
+    S = b.num_seqs
+    pool = pkv.BlockPool(b.num_blocks)
+    for row in b.tables:
+        for x in row[row >= 0]:
+            pool.claim(int(x))
+    tables = b.tables.copy()
+    lens = b.lengths.copy()
+    kr, vr = b.k_pool.clone(), b.v_pool.clone()
+    for step in range(1, steps + 1):
+        k_new, v_new = W.new_tokens(b.seed, step, S, 8, 128, torch.bfloat16)
+        for s in range(S):
+            blk, off, cow = pool.prepare_write(tables[s], int(lens[s]), 16)
+            assert cow is None
+            kr[blk, :, off] = k_new[s]
+            vr[blk, :, off] = v_new[s]
+        lens = lens + 1
+        q = W.new_queries(b, step)
+        dtab = torch.from_numpy(tables).cuda()
+        got = db.decode_append(k_new.cuda(), v_new.cuda(), q=q.cuda(),
+                               lens=torch.from_numpy(lens.astype(np.int32)).cuda(),
+                               max_ctx=int(lens.max()), tables=dtab)
+        assert torch.equal(bits(db.k_pool.cpu()), bits(kr))
+        assert torch.equal(bits(db.v_pool.cpu()), bits(vr))
+        err = max_err(got, oracle.paged_decode(q, kr, vr, tables, lens, 16))
+        print(f"fused long-context step {step} max-abs {err:.3g}")
+        assert err <= 2e-3
+
+
+def test_decode_append_out_of_range_slot():
+    """A sequence whose newest token's table entry is out of range: nothing is written for it,
+    its row is NaN, the others are exact."""
+    b = W.small_batch([40, 70, 33], 16, 2, 128, 16, torch.bfloat16, seed=83)
+    db = DeviceBatch(b)
+    k_new, v_new = W.new_tokens(b.seed, 4, 3, 2, 128, torch.bfloat16)
+    tab = db.tables.clone()
+    tab[1, (70 - 1) // 16] = b.num_blocks + 7
+    before_k, before_v = db.k_pool.cpu().clone(), db.v_pool.cpu().clone()
+    got = db.decode_append(k_new.cuda(), v_new.cuda(), tables=tab)
+    assert torch.isnan(got[1]).all() and not torch.isnan(got[0]).any() and not torch.isnan(got[2]).any()
+    kr, vr = before_k.clone(), before_v.clone()
+    for s in (0, 2):
+        L = int(b.lengths[s])
+        blk, off = oracle.token_address(L - 1, b.tables[s], 16)
+        kr[blk, :, off] = k_new[s]
+        vr[blk, :, off] = v_new[s]
+    assert torch.equal(bits(db.k_pool.cpu()), bits(kr)) and torch.equal(bits(db.v_pool.cpu()), bits(vr))
+    ref = oracle.paged_decode(b.q, kr, vr, b.tables, b.lengths, 16)
+    assert max_err(got, ref, [0, 2]) <= 2e-3
