@@ -533,3 +533,48 @@ def test_decode_append_out_of_range_slot():
     assert torch.equal(bits(db.k_pool.cpu()), bits(kr)) and torch.equal(bits(db.v_pool.cpu()), bits(vr))
     ref = oracle.paged_decode(b.q, kr, vr, b.tables, b.lengths, 16)
     assert max_err(got, ref, [0, 2]) <= 2e-3
+
+
+def test_decode_step_replays_in_a_hip_graph():
+    """A serving loop may capture its decode step in a HIP graph: every call launches on the
+    caller's stream, allocates nothing and records no memset (the workspace is passed in and
+    needs no clearing). The fused step and the plain decode, captured together, replay three
+    times -- with eager work and synchronisations between the replays -- and every replay
+    matches the eager results bit for bit."""
+    b = W.small_batch(RAGGED, 64, 8, 128, 16, torch.bfloat16, seed=91, poison=True)
+    db = DeviceBatch(b)
+    S = b.num_seqs
+    k_new, v_new = (x.cuda() for x in W.new_tokens(b.seed, 1, S, 8, 128, torch.bfloat16))
+    out1 = torch.empty(db.q.shape, dtype=torch.float32, device="cuda")
+    out2 = torch.empty_like(out1)
+    ws1 = pkv.decode_workspace(S, 64, 8, 128, 0, "cuda")
+    ws2 = pkv.decode_workspace(S, 64, 8, 128, 0, "cuda")
+
+    def step():
+        pkv.paged_attn_decode_append(out1, db.q, db.k_pool, db.v_pool, k_new, v_new, db.tables,
+                                     db.lens, db.max_ctx, workspace=ws1)
+        pkv.paged_attn_decode(out2, db.q, db.k_pool, db.v_pool, db.tables, db.lens, db.max_ctx,
+                              workspace=ws2)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref1, ref2 = out1.clone(), out2.clone()
+    pools = (db.k_pool.clone(), db.v_pool.clone())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        out1.fill_(float("nan"))
+        out2.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(out1.cpu()), bits(ref1.cpu()))
+        assert torch.equal(bits(out2.cpu()), bits(ref2.cpu()))
+        assert torch.equal(bits(db.k_pool.cpu()), bits(pools[0].cpu()))
+        assert torch.equal(bits(db.v_pool.cpu()), bits(pools[1].cpu()))
+    assert not torch.isnan(ref1).any()
