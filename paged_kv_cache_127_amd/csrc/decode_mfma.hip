@@ -26,6 +26,8 @@
 // keeps P.V at close to fp32 accuracy. Scores and the online softmax stay in fp32; the scale
 // (times log2 e) is applied to the fp32 scores and exp2 is used throughout.
 // Two steps' loads (with their query rows) are in flight while a step computes.
+// Fused append (k_new set): in a segment's last step, the lanes of the row of token L - 1 read
+// it from k_new / v_new instead of the pool (the merge kernel stores it into its slot later).
 #include "device_common.h"
 #include "kernels.h"
 #include "schedule.h"
@@ -154,12 +156,12 @@ void decode_mfma(DecodeParams p) {
   const int vrow = lane / VLPR;
   const int vch = lane % VLPR;
 
-  // Output ring (dynamic LDS after the schedule arrays): piece results are staged here and
-  // written to memory only when the ring is full or the range is done. A vector store that is
-  // still in flight makes every later wait for a vector load a full drain (loads and stores
-  // share one counter and stores complete out of order), so stores stay out of the streaming
-  // loop. Entry: G rows of D floats, then the G running maxima and sums (partials); header:
-  // destination element offset and (slot << 2 | kind).
+  // Output ring (dynamic LDS after the schedule arrays and the workgroup's value tiles): piece
+  // results are staged here and written to memory only when the ring is full or the range is
+  // done. A vector store that is still in flight makes every later wait for a vector load a
+  // full drain (loads and stores share one counter and stores complete out of order), so
+  // stores stay out of the streaming loop. Entry: G rows of D floats, then the G running maxima
+  // and sums (partials); header: destination element offset and (slot << 2 | kind).
   const int R = p.ring_cap;
   const int EF = G * D + 2 * G;
   char* ring = reinterpret_cast<char*>(smem) + ring_offset(S) + (size_t)W * 32 * RB +
