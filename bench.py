@@ -170,6 +170,14 @@ def other_configs(pkv, W, torch, dev: str, workers: int, launches: int = 30):
                                   "block size 16, lengths uniform in [16384, 32768]; step = "
                                   "decode with the 8-token append fused in + merge", b, dus, mus,
                                   aus, step)
+    # the engine's table-row upload per step (pinned host rows -> device, on the same stream)
+    host_tab = torch.from_numpy(b.tables).pin_memory()
+
+    def long_step_upload():
+        t["tab"].copy_(host_tab, non_blocking=True)
+        long_step()
+    _, _, _, _, step_up = _decode_timing(pkv, torch, long_step_upload, launches)
+    res["long8_bf16"]["step_with_table_upload_p50_us"] = round(step_up, 2)
     del t
     # shared prefix: 128 sequences over one 800-token prefix (logical bytes; the prefix blocks
     # are re-read by every sharer, so caches serve most of them)
