@@ -14,10 +14,11 @@ from typing import Optional
 import torch  # loaded first: the library then binds to the HIP runtime torch already loaded
 
 __all__ = [
-    "PagedKVError", "paged_attn_decode", "kv_cache_append", "cow_block_copy",
-    "pkv_decode_workspace_size", "decode_workspace",
-    "pkv_decode_auto_workers", "BlockPool", "timing_enable",
-    "timing_query", "set_validate", "library_path", "load_library", "PKV_F32", "PKV_F16", "PKV_BF16",
+    "PagedKVError", "paged_attn_decode", "paged_attn_decode_append", "kv_cache_append",
+    "cow_block_copy", "pkv_decode_workspace_size", "decode_workspace",
+    "pkv_decode_auto_workers", "BlockPool", "timing_enable", "timing_query",
+    "stream_read_probe", "set_validate", "library_path", "load_library", "PKV_F32", "PKV_F16",
+    "PKV_BF16",
 ]
 
 PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2

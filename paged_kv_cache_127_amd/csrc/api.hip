@@ -117,7 +117,10 @@ bool copy_ints(std::vector<int32_t>& dst, const int32_t* src, size_t n, hipStrea
   return hipStreamSynchronize(st) == hipSuccess;
 }
 
-constexpr int kWorkersPerCU = 8;   // two resident wavefronts per SIMD, four SIMDs per CU
+// Upper bound of the automatic worker count per compute unit (two resident wavefronts per SIMD,
+// four SIMDs); the automatic workspace size assumes it, the kernels' actual residency (one
+// wavefront per SIMD for the matrix-core kernel) is never above it.
+constexpr int kWorkersPerCU = 8;
 
 int cu_count() {
   static int cache[64] = {0};
