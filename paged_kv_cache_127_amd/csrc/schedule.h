@@ -146,6 +146,20 @@ struct Line {
     l.Nw = (int64_t)Hkv * uni(wts[S]);
     return l;
   }
+  // The same cut from the totals alone (steps[S], wts[S]); for code that needs no search.
+  __device__ static Line from_totals(int64_t steps_total, int64_t wts_total, int S, int Hkv,
+                                     int pw, int n) {
+    Line l;
+    l.steps = nullptr;
+    l.wts = nullptr;
+    l.S = S;
+    l.Hkv = Hkv;
+    l.pw = pw;
+    l.n = n;
+    l.N = (int64_t)Hkv * steps_total;
+    l.Nw = (int64_t)Hkv * wts_total;
+    return l;
+  }
   __device__ int64_t wbegin(int w) const { return range_begin(Nw, n, w); }
   __device__ int owner(int64_t x) const { return worker_of(Nw, n, x); }
 

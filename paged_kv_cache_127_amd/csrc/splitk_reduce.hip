@@ -41,7 +41,13 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
   const int g = seg - s * Hkv;
   const int G = p.num_q_heads / Hkv;
   const int n4 = G * D / 4;                          // f32x4 chunks of the segment's rows
-  const int64_t ns = uni(p.prefix[s + 1]) - uni(p.prefix[s]);
+  // the schedule values are wave-uniform: scalar loads through the constant address space
+  typedef const __attribute__((address_space(4))) int64_t* cptr64;
+  const cptr64 pre = (cptr64)p.prefix;
+  const cptr64 wpre = (cptr64)p.wprefix;
+  const int S = p.num_seqs;
+  const int64_t ns = pre[s + 1] - pre[s];
+  const int64_t wpre_s = wpre[s], steps_total = pre[S], wts_total = wpre[S];
   const size_t base = ((size_t)s * p.num_q_heads + (size_t)g * G) * D;
 
   // Fused append (k_new set): the segment's newest row -- token L - 1, keys on lanes [0, LPR),
@@ -51,18 +57,20 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
   // the merge's own loads; a slot whose table entry is out of range is not written.
   constexpr int RB = D * (int)sizeof(T);   // bytes per row
   constexpr int LPR = RB / 16;
-  const bool app = p.k_new != nullptr && wave == 0 && lane < 2 * LPR;
+  const bool app_wave = p.k_new != nullptr && wave == 0;      // uniform
+  const bool app = app_wave && lane < 2 * LPR;
   const int kvsel = lane < LPR ? 0 : 1;
   const int ch = lane % LPR;
   int Lnew = 0, blk = -1;
   u32x4 xnew = u32x4{0u, 0u, 0u, 0u};
-  if (app) {
+  if (app_wave) {
     const int cap = min(p.max_context_len, p.max_blocks * p.block_size);
-    Lnew = clamp_len(p.lens[s], cap);
+    Lnew = clamp_len(((ctable_t)p.lens)[s], cap);
     if (Lnew > 0) {
-      xnew = load16(reinterpret_cast<const char*>(kvsel ? p.v_new : p.k_new) +
-                    ((size_t)s * Hkv + g) * RB + 16 * ch);
-      blk = p.tables[(size_t)s * p.max_blocks + (Lnew - 1) / p.block_size];
+      blk = ((ctable_t)p.tables)[(size_t)s * p.max_blocks + (Lnew - 1) / p.block_size];
+      if (app)
+        xnew = load16(reinterpret_cast<const char*>(kvsel ? p.v_new : p.k_new) +
+                      ((size_t)s * Hkv + g) * RB + 16 * ch);
     }
   }
   auto append_store = [&]() {
@@ -97,10 +105,10 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
     }
     return;
   }
-  const Line line = Line::make(p.prefix, p.wprefix, p.num_seqs, Hkv, p.piece_weight,
-                               p.num_workers);
+  const Line line = Line::from_totals(steps_total, wts_total, S, Hkv, p.piece_weight,
+                                      p.num_workers);
   const int64_t seg_w = kStepWeight * ns + line.pw;
-  const int64_t ws0 = (int64_t)Hkv * uni(p.wprefix[s]) + g * seg_w;   // weighted segment start
+  const int64_t ws0 = (int64_t)Hkv * wpre_s + g * seg_w;              // weighted segment start
   const int64_t first = ws0 + line.pw;                                 // weighted start of step 0
   const int rf = line.owner(first);
   const int rl = line.owner(first + kStepWeight * (ns - 1));
