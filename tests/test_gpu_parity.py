@@ -578,3 +578,40 @@ def test_decode_step_replays_in_a_hip_graph():
         assert torch.equal(bits(db.k_pool.cpu()), bits(pools[0].cpu()))
         assert torch.equal(bits(db.v_pool.cpu()), bits(pools[1].cpu()))
     assert not torch.isnan(ref1).any()
+
+
+def test_random_shapes_sweep():
+    """Forty seeded random small problems across the supported space -- cache dtype, G, head
+    dim, block size, worker count, ragged lengths with empty contexts -- through both entry
+    points: plain decode and the fused append + decode, against the oracle."""
+    rng = np.random.default_rng(2024)
+    shapes = [("bf16", 2), ("bf16", 3), ("bf16", 8), ("bf16", 16), ("f16", 1), ("f16", 4),
+              ("f16", 12), ("f32", 1), ("f32", 2), ("f32", 8)]
+    for i in range(40):
+        dt, G = shapes[i % len(shapes)]
+        hkv = int(rng.choice([1, 2, 4]))
+        d = int(rng.choice([64, 128]))
+        B = int(rng.choice([16, 32]))
+        S = int(rng.integers(1, 10))
+        lens = [int(x) for x in rng.integers(0, 300, size=S)]
+        lens[int(rng.integers(0, S))] = max(1, lens[0])          # at least one context
+        workers = int(rng.choice([0, 1, 3, 64, 2000]))
+        case = (dt, G, hkv, d, B, lens, workers)
+        print("case", case, flush=True)
+        b = W.small_batch(lens, G * hkv, hkv, d, B, DT[dt], seed=3000 + i, poison=True)
+        got = DeviceBatch(b).decode(workers=workers)
+        assert max_err(got, oracle_decode(b)) <= TOL[DT[dt]], case
+        # fused: sequences with a context get their newest token from k_new / v_new
+        k_new, v_new = W.new_tokens(b.seed, 5, S, hkv, d, DT[dt])
+        db = DeviceBatch(b)
+        got2 = db.decode_append(k_new.cuda(), v_new.cuda(), workers=workers)
+        kr, vr = b.k_pool.clone(), b.v_pool.clone()
+        for s, L in enumerate(lens):
+            if L > 0:
+                blk, off = oracle.token_address(L - 1, b.tables[s], B)
+                kr[blk, :, off] = k_new[s]
+                vr[blk, :, off] = v_new[s]
+        assert torch.equal(bits(db.k_pool.cpu()), bits(kr)), case
+        assert torch.equal(bits(db.v_pool.cpu()), bits(vr)), case
+        ref2 = oracle.paged_decode(b.q, kr, vr, b.tables, b.lengths, B)
+        assert max_err(got2, ref2) <= TOL[DT[dt]], case

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 import torch.nn.functional as F
+from hypothesis import given, settings, strategies as st
 
 import workloads as W
 from oracle import (attend, contiguous_decode, gather_kv, merge_states, paged_decode,
@@ -135,3 +136,26 @@ def test_shared_prefix_equals_private_copies():
                       private.lengths, 16)
     assert np.array_equal(o1, o2)
     assert np.allclose(o1, sdpa_decode(shared), atol=1e-12)
+
+
+
+@settings(max_examples=60, deadline=None)
+@given(lengths=st.lists(st.integers(0, 70), min_size=1, max_size=4),
+       block_size=st.sampled_from([16, 32]), group=st.sampled_from([1, 2, 8]),
+       hkv=st.sampled_from([1, 2]), d=st.sampled_from([8, 16]),
+       dtype=st.sampled_from([torch.float32, torch.bfloat16]), seed=st.integers(0, 10_000))
+def test_random_small_cases_match_sdpa(lengths, block_size, group, hkv, d, dtype, seed):
+    """Random small batches (S <= 4, L <= 70, empty contexts included, both block sizes,
+    G in {1, 2, 8}): the paged oracle equals torch SDPA on the logical rows (zero rows for
+    empty contexts), with poisoned unused slots and random placement."""
+    b = W.small_batch(lengths, hkv * group, hkv, d, block_size, dtype, seed=seed, poison=True)
+    got = paged_decode(b.q, b.k_pool, b.v_pool, b.tables, b.lengths, block_size)
+    for s, L in enumerate(lengths):
+        if L == 0:
+            assert np.array_equal(got[s], np.zeros_like(got[s]))
+        else:
+            q = b.q[s].to(torch.float64)[None, :, None, :]
+            k = b.k_logical[s].to(torch.float64)[None]
+            v = b.v_logical[s].to(torch.float64)[None]
+            ref = F.scaled_dot_product_attention(q, k, v, enable_gqa=True)[0, :, 0, :].numpy()
+            assert np.allclose(got[s], ref, rtol=0, atol=1e-12)
