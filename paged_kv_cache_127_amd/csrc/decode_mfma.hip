@@ -209,13 +209,8 @@ void decode_mfma(DecodeParams p) {
     const int b1 = valid_block(si.b1, p.num_blocks) ? si.b1 : 0;   // then poison
     const char* t0 = kbase + ((size_t)b0 * Hkv + si.g) * kv_block_stride;
     const char* t1 = kbase + ((size_t)b1 * Hkv + si.g) * kv_block_stride;
-    // rows past the context (last step of a segment) re-read row 0 of the step: those lines
-    // are fetched for row 0 anyway, and the rows are masked
-    const int nvalid = si.L - 32 * si.k;
-    const char* ka = tokA0 < nvalid ? ((B == 16 && tokA0 >= 16) ? t1 : t0) + kofs0
-                                    : t0 + 8 * jg * ES;
-    const char* kb = tokA0 + 4 < nvalid ? ((B == 16 && tokA0 + 4 >= 16) ? t1 : t0) + kofs1
-                                        : t0 + 8 * jg * ES;
+    const char* ka = ((B == 16 && tokA0 >= 16) ? t1 : t0) + kofs0;
+    const char* kb = ((B == 16 && tokA0 + 4 >= 16) ? t1 : t0) + kofs1;
     if (p.k_new && si.k == si.ns - 1) {   // fused append: the newest token's row from k_new
       const int tn = si.L - 1 - 32 * si.k;
       const char* kn = reinterpret_cast<const char*>(p.k_new) +
@@ -234,14 +229,12 @@ void decode_mfma(DecodeParams p) {
     const int b1 = valid_block(si.b1, p.num_blocks) ? si.b1 : 0;
     const bool sub = p.k_new && si.k == si.ns - 1;   // fused append (see load_kq)
     const int tn = si.L - 1 - 32 * si.k;
-    const int nvalid = si.L - 32 * si.k;             // rows past it re-read row 0 (masked)
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int t = VTPI * f + vrow;
-      const int tr = t < nvalid ? t : 0;
-      const int blk = (B == 16 && tr >= 16) ? b1 : b0;
+      const int blk = (B == 16 && t >= 16) ? b1 : b0;
       const char* a = vbase + ((size_t)blk * Hkv + si.g) * kv_block_stride +
-                      (size_t)(tr & (B - 1)) * RB + 16 * vch;
+                      (size_t)(t & (B - 1)) * RB + 16 * vch;
       if (sub && t == tn)
         a = reinterpret_cast<const char*>(p.v_new) + ((size_t)si.s * Hkv + si.g) * RB + 16 * vch;
       r.v[f] = load16(a);

@@ -104,14 +104,12 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
     const bool sub = p.k_new && si.k == si.ns - 1;
     const int tn = si.L - 1 - 32 * si.k;
     const size_t nofs = ((size_t)si.s * Hkv + si.g) * D * ES + (size_t)ch * 16;
-    const int nvalid = si.L - 32 * si.k;   // rows past it re-read row 0 (cached, masked)
 #pragma unroll
     for (int c = 0; c < NI; ++c) {
       const int tt = TPI * c + row;
-      const int tr = tt < nvalid ? tt : 0;
-      const int blk = (B == 16 && tr >= 16) ? b1 : b0;
+      const int blk = (B == 16 && tt >= 16) ? b1 : b0;
       const size_t ofs = ((size_t)blk * Hkv + si.g) * blk_stride +
-                         (size_t)(tr & (B - 1)) * D * ES + (size_t)ch * 16;
+                         (size_t)(tt & (B - 1)) * D * ES + (size_t)ch * 16;
       const bool nw = sub && tt == tn;
       r.k[c] = load16(nw ? reinterpret_cast<const char*>(p.k_new) + nofs : kbase + ofs);
       r.v[c] = load16(nw ? reinterpret_cast<const char*>(p.v_new) + nofs : vbase + ofs);
