@@ -10,7 +10,8 @@ Sources (web pages; cited by title and section):
   * "PagedAttention: Virtual Memory for the KV Cache" -- block counts, the block table and
     its indexing rule, growth, prefix sharing and copy-on-write of a partial block.
   * "Paged Attention and vLLM" -- the attention equation over table-gathered keys, the
-    per-block partial softmax and its log-sum-exp merge, the copy-on-write rule.
+    per-block partial softmax and its log-sum-exp merge, the copy-on-write rule, block swap of
+    a preempted sequence to CPU memory and back.
   * "KV Cache Optimization and Management" -- reference counting, release at count zero,
     worked capacity examples.
 
@@ -21,11 +22,11 @@ unpinned".
 from .attention import (attend, contiguous_decode, gather_kv, merge_states,
                         paged_decode, paged_decode_split, partial_state, token_address)
 from .bookkeeping import (BlockPool, PagedKVModel, RefcountError, PoolExhausted,
-                          blocks_for, capacity_report, reserved_slots, shareable_prefix_blocks)
+                          blocks_for, copy_blocks, capacity_report, reserved_slots, shareable_prefix_blocks)
 
 __all__ = [
     "attend", "contiguous_decode", "gather_kv", "merge_states",
     "paged_decode", "paged_decode_split", "partial_state", "token_address", "BlockPool",
-    "PagedKVModel", "RefcountError", "PoolExhausted", "blocks_for", "capacity_report",
+    "PagedKVModel", "RefcountError", "PoolExhausted", "blocks_for", "copy_blocks", "capacity_report",
     "reserved_slots", "shareable_prefix_blocks",
 ]

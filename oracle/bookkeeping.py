@@ -13,11 +13,22 @@ Sources:
   * "KV Cache Optimization and Management": blocks are allocated one at a time as a sequence
     grows; a reference count tracks sharers and a block returns to the free pool only at zero
     (section "PagedAttention: borrowing virtual memory", answer A6); capacity examples.
+  * "Paged Attention and vLLM", section "Continuous Batching and Scheduler": a preempted
+    sequence's physical blocks are evicted to CPU memory a block at a time and swapped back
+    when it resumes, so the cost is the evicted blocks only.
 
 Readings: the pages name no allocation order (the example takes block 11 while lower ones are
 free), so ``BlockPool.alloc`` hands out the lowest free block and ``claim`` takes a named one.
 A copy-on-write copies the valid slots [0, n) of every KV head of K and V, where n is the
 writer's offset inside the shared block.
+
+Swap (the pages give the mechanism, not its bookkeeping): host memory holds a second pool of
+blocks with the device pools' block shape, managed by its own ``BlockPool``. Swapping out a
+group of sequences gives each distinct device block they reference one host block, copies it
+whole (every head, every slot, K and V), moves the group's references from the device block to
+the host block and rewrites the group's tables with host ids. A device block that a sequence
+outside the group also references stays resident for it. Swapping in is the mirror image, with
+fresh device blocks. A whole block moves even when only some of its slots are valid.
 """
 from __future__ import annotations
 
@@ -109,6 +120,22 @@ class BlockPool:
         return self.ref[block]
 
 
+def copy_blocks(dst_k: np.ndarray, dst_v: np.ndarray, src_k: np.ndarray, src_v: np.ndarray,
+                src_ids, dst_ids) -> int:
+    """Batched whole-block copy between two pools of one block shape ``[H_kv][B][d]``:
+    block ``src_ids[i]`` of (src_k, src_v) goes to block ``dst_ids[i]`` of (dst_k, dst_v).
+    A pair whose id falls outside its pool is skipped. Returns the number of pairs copied."""
+    done = 0
+    for s, d in zip(src_ids, dst_ids):
+        s, d = int(s), int(d)
+        if not (0 <= s < src_k.shape[0] and 0 <= d < dst_k.shape[0]):
+            continue
+        dst_k[d] = src_k[s]
+        dst_v[d] = src_v[s]
+        done += 1
+    return done
+
+
 class PagedKVModel:
     """Pools of raw K/V values plus per-sequence tables and lengths.
 
@@ -125,6 +152,7 @@ class PagedKVModel:
         self.tables: dict = {}
         self.lengths: dict = {}
         self.copies: list = []        # (src, dst, n) copy-on-write records, in order
+        self.swapped: set = set()     # sequences whose tables hold host block ids
 
     # -- sequence lifetime --------------------------------------------------------------
     def add_sequence(self, s, table, length: int) -> None:
@@ -145,6 +173,60 @@ class PagedKVModel:
         del self.tables[s]
         del self.lengths[s]
         return freed
+
+    # -- preemption ---------------------------------------------------------------------
+    def swap_out(self, group, host: BlockPool, host_k: np.ndarray, host_v: np.ndarray) -> list:
+        """Evict the blocks of the sequences in ``group`` to the host pool.
+
+        Each distinct device block gets one host block (the lowest free); the block is copied
+        whole, the group's references move to the host block and the device block loses them
+        (it returns to the free pool at zero). Returns the (device block, host block) pairs
+        in the order of first reference.
+        """
+        mapping: dict = {}
+        for s in group:
+            if s in self.swapped:
+                raise ValueError(f"sequence {s} is already swapped out")
+            for b in self.tables[s]:
+                if b in mapping:
+                    host.incref(mapping[b])
+                else:
+                    mapping[b] = host.alloc()
+        pairs = list(mapping.items())
+        copy_blocks(host_k, host_v, self.k, self.v, [p[0] for p in pairs], [p[1] for p in pairs])
+        for s in group:
+            t = self.tables[s]
+            for j, b in enumerate(t):
+                self.pool.decref(b)
+                t[j] = mapping[b]
+            self.swapped.add(s)
+        return pairs
+
+    def swap_in(self, group, host: BlockPool, host_k: np.ndarray, host_v: np.ndarray,
+                claims=None) -> list:
+        """Bring a swapped-out group back: each distinct host block gets a device block
+        (``claims`` names them in order of first reference, else the lowest free), is copied
+        whole, and the group's references move back. Returns the (host block, device block)
+        pairs."""
+        mapping: dict = {}
+        claims = iter(claims) if claims is not None else None
+        for s in group:
+            if s not in self.swapped:
+                raise ValueError(f"sequence {s} is not swapped out")
+            for b in self.tables[s]:
+                if b in mapping:
+                    self.pool.incref(mapping[b])
+                else:
+                    mapping[b] = self.pool.claim(next(claims)) if claims else self.pool.alloc()
+        pairs = list(mapping.items())
+        copy_blocks(self.k, self.v, host_k, host_v, [p[0] for p in pairs], [p[1] for p in pairs])
+        for s in group:
+            t = self.tables[s]
+            for j, b in enumerate(t):
+                host.decref(b)
+                t[j] = mapping[b]
+            self.swapped.discard(s)
+        return pairs
 
     # -- writes -------------------------------------------------------------------------
     def prepare_write(self, s, claim=None):
