@@ -238,6 +238,84 @@ def other_configs(pkv, W, torch, dev: str, workers: int, launches: int = 30):
     return res
 
 
+def swap_figures(pkv, W, torch, dev: str, preempt: int = 32, launches: int = 10):
+    """Preemption of the first `preempt` sequences of the GQA batch (block size 16): every block
+    they hold goes to pinned host memory in one kv_swap_out and comes back into other free
+    device blocks in one kv_swap_in. Kernel durations from hipEvents around every launch. The
+    host-link ceiling is a plain DMA copy (torch copy_, i.e. hipMemcpyAsync) of the same bytes
+    between one contiguous device buffer and pinned host memory, each direction."""
+    b = W.config3(16)
+    kp, vp = b.k_pool.to(dev), b.v_pool.to(dev)
+    blocks = [int(x) for s in range(preempt) for x in b.tables[s] if x >= 0]
+    n = len(blocks)
+    used = set(int(x) for x in b.tables.ravel() if x >= 0)
+    free = [x for x in range(b.num_blocks) if x not in used][:n]
+    if len(free) < n:
+        raise RuntimeError("pool too small for the swap-in destinations")
+    shape = (n,) + tuple(kp.shape[1:])
+    hk = torch.empty(shape, dtype=kp.dtype, pin_memory=True)
+    hv = torch.empty(shape, dtype=kp.dtype, pin_memory=True)
+    ids = lambda x: torch.tensor(x, dtype=torch.int32, device=dev)
+    dev_ids, host_ids, back_ids = ids(blocks), ids(list(range(n))), ids(free)
+
+    def kernel_us(name, fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        pkv.timing_enable(True, every=1)
+        for _ in range(launches):
+            fn()
+        torch.cuda.synchronize()
+        ms, cnt = pkv.timing_query(name)
+        pkv.timing_enable(False)
+        return ms / cnt * 1e3
+
+    out_us = kernel_us("swap_out", lambda: pkv.kv_swap_out(kp, vp, hk, hv, dev_ids, host_ids))
+    in_us = kernel_us("swap_in", lambda: pkv.kv_swap_in(kp, vp, hk, hv, host_ids, back_ids))
+    torch.cuda.synchronize()
+    moved = (torch.equal(hk[0].view(torch.int16), b.k_pool[blocks[0]].view(torch.int16)) and
+             torch.equal(kp[free[-1]].cpu().view(torch.int16),
+                         b.k_pool[blocks[-1]].view(torch.int16)))
+    nbytes = 2 * hk.numel() * hk.element_size()
+    del kp, vp
+    dbuf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    hbuf = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+
+    def dma_us(dst, src):
+        for _ in range(2):
+            dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(launches)]
+        for a, e in ev:
+            a.record()
+            dst.copy_(src, non_blocking=True)
+            e.record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(e) * 1e3 for a, e in ev)
+        return t[len(t) // 2]
+
+    d2h_us, h2d_us = dma_us(hbuf, dbuf), dma_us(dbuf, hbuf)
+    del dbuf, hbuf
+    torch.cuda.empty_cache()
+    gbs = lambda us: round(nbytes / (us * 1e-6) / 1e9, 2)
+    res = {
+        "workload": f"preempt the first {preempt} sequences of the GQA decode batch (block size "
+                    f"16): {n} blocks of 8 heads x 16 slots x 128 bf16, keys and values, out to "
+                    "pinned host memory in one call and back into other free blocks in one call",
+        "blocks": n, "bytes": nbytes, "data_checked": bool(moved),
+        "swap_out_us": round(out_us, 2), "swap_out_gbs": gbs(out_us),
+        "swap_in_us": round(in_us, 2), "swap_in_gbs": gbs(in_us),
+        "dma_d2h_us": round(d2h_us, 2), "dma_d2h_gbs": gbs(d2h_us),
+        "dma_h2d_us": round(h2d_us, 2), "dma_h2d_gbs": gbs(h2d_us),
+        "out_frac_of_dma": round(d2h_us / out_us, 4), "in_frac_of_dma": round(h2d_us / in_us, 4),
+        "bound": "host link (ceiling: contiguous DMA copy of the same bytes)",
+    }
+    print(f"bench: swap out {res['swap_out_gbs']} GB/s in {res['swap_in_gbs']} GB/s "
+          f"(DMA {res['dma_d2h_gbs']} / {res['dma_h2d_gbs']})", file=sys.stderr, flush=True)
+    return res
+
+
 def stream_probe(pkv, torch, dev: str, gib: int = 2, launches: int = 20):
     """Plain streaming-read bandwidth of this device (the library's probe kernel)."""
     buf = torch.ones((gib << 30) // 4, dtype=torch.float32, device=dev)
@@ -489,6 +567,7 @@ def main():
         probe["decode_frac_of_probe"] = round(achieved / probe["gbs"], 4)
         result["read_probe"] = probe
         result["other_configs"] = other_configs(pkv, W, torch, dev, args.workers)
+        result["swap"] = swap_figures(pkv, W, torch, dev)
     if not args.no_cpu_baseline:
         print("bench: oracle on one core", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(b, args.cpu_steps)

@@ -174,6 +174,34 @@ int cow_block_copy(void* k_pool, void* v_pool, int kv_dtype, const int32_t* src_
                    int num_kv_heads, int head_dim, int block_size, int num_blocks, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Block swap between the device pools and a pool of blocks in host memory ([P2] "Continuous
+ * Batching and Scheduler": a preempted sequence's physical blocks are evicted to CPU memory a
+ * block at a time and swapped back when it resumes, so resuming costs only those blocks).
+ *   host_k, host_v  host [num_host_blocks][num_kv_heads][block_size][head_dim], element type
+ *                   kv_dtype: the device pools' block shape. They must be pinned host memory
+ *                   that the device can address (hipHostMalloc, or a framework's pinned
+ *                   allocator); anything else is rejected with PKV_ERR_INVALID_ARG before a
+ *                   launch. The caller owns them and sizes them for num_host_blocks blocks.
+ *   device_blocks, host_blocks  int32 [num_pairs], device memory or pinned host memory.
+ * kv_swap_out copies device block device_blocks[i] (every head, every slot, keys and values)
+ * to host block host_blocks[i]; kv_swap_in copies host block host_blocks[i] to device block
+ * device_blocks[i]. Destinations must be distinct; a pair with an id outside its pool is
+ * skipped. One launch moves the whole list, reading or writing host memory directly across
+ * the host link. The copy is complete when the stream reaches it: synchronize (or wait on an
+ * event) before the host reads host_k / host_v, and before it reuses evicted device blocks
+ * from another stream. Which blocks to evict, and the table and reference-count bookkeeping
+ * (pkv_pool_* on a second pool of host block ids), are the caller's.
+ * --------------------------------------------------------------------------------------- */
+int kv_swap_out(const void* k_pool, const void* v_pool, int kv_dtype, void* host_k,
+                void* host_v, int num_host_blocks, const int32_t* device_blocks,
+                const int32_t* host_blocks, int num_pairs, int num_kv_heads, int head_dim,
+                int block_size, int num_blocks, void* stream);
+int kv_swap_in(void* k_pool, void* v_pool, int kv_dtype, const void* host_k, const void* host_v,
+               int num_host_blocks, const int32_t* host_blocks, const int32_t* device_blocks,
+               int num_pairs, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+               void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Host block pool: free list and reference counts of `num_blocks` physical block ids. No
  * device memory. A block returns to the free list only when its count reaches zero
  * ([P3] "PagedAttention: borrowing virtual memory", answer A6); a full pool is reported, not

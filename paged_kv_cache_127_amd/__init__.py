@@ -15,7 +15,7 @@ import torch  # loaded first: the library then binds to the HIP runtime torch al
 
 __all__ = [
     "PagedKVError", "paged_attn_decode", "paged_attn_decode_append", "kv_cache_append",
-    "cow_block_copy", "pkv_decode_workspace_size", "decode_workspace",
+    "cow_block_copy", "kv_swap_out", "kv_swap_in", "pkv_decode_workspace_size", "decode_workspace",
     "pkv_decode_auto_workers", "BlockPool", "timing_enable", "timing_query",
     "stream_read_probe", "set_validate", "library_path", "load_library", "PKV_F32", "PKV_F16",
     "PKV_BF16",
@@ -64,6 +64,10 @@ def _declare(L):
                                     c_void, c_int, c_int, c_int, c_int, c_int, c_int, c_void]),
         "cow_block_copy": (c_int, [c_void, c_void, c_int, c_void, c_void, c_void, c_int, c_int,
                                    c_int, c_int, c_int, c_void]),
+        "kv_swap_out": (c_int, [c_void, c_void, c_int, c_void, c_void, c_int, c_void, c_void,
+                                c_int, c_int, c_int, c_int, c_int, c_void]),
+        "kv_swap_in": (c_int, [c_void, c_void, c_int, c_void, c_void, c_int, c_void, c_void,
+                               c_int, c_int, c_int, c_int, c_int, c_void]),
         "pkv_pool_create": (c_void, [c_int]),
         "pkv_pool_destroy": (None, [c_void]),
         "pkv_pool_alloc": (c_int, [c_void, i32p]),
@@ -250,6 +254,45 @@ def cow_block_copy(k_pool, v_pool, src_blocks, dst_blocks, num_tokens=None, stre
         _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype), _kv_dtype(k_pool),
         _dev(src_blocks, "src_blocks", torch.int32), _dev(dst_blocks, "dst_blocks", torch.int32),
         nt, n, Hkv, d, B, N, _stream(stream)))
+
+
+def _host_pool(t: torch.Tensor, name: str, like: torch.Tensor) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.is_cuda or not t.is_pinned():
+        raise ValueError(f"{name} must be a pinned host tensor (pin_memory=True)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != like.dtype or tuple(t.shape[1:]) != tuple(like.shape[1:]):
+        raise ValueError(f"{name} must be [num_host_blocks]{list(like.shape[1:])} of {like.dtype}")
+    return t.data_ptr()
+
+
+def _swap(fn, k_pool, v_pool, host_k, host_v, first_ids, second_ids, stream):
+    N, Hkv, B, d = k_pool.shape
+    if v_pool.shape != k_pool.shape or host_v.shape != host_k.shape:
+        raise ValueError("K and V pools must have equal shapes")
+    n = int(first_ids.shape[0])
+    if first_ids.dim() != 1 or tuple(second_ids.shape) != (n,):
+        raise ValueError("block id lists must be [num_pairs]")
+    _check(fn(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype), _kv_dtype(k_pool),
+              _host_pool(host_k, "host_k", k_pool), _host_pool(host_v, "host_v", k_pool),
+              int(host_k.shape[0]), _dev(first_ids, "block ids", torch.int32),
+              _dev(second_ids, "block ids", torch.int32), n, Hkv, d, B, N, _stream(stream)))
+
+
+def kv_swap_out(k_pool, v_pool, host_k, host_v, device_blocks, host_blocks, stream=None):
+    """Copy whole blocks device_blocks[i] of the pools to host_blocks[i] of the pinned host
+    pools (C: ``kv_swap_out``). Asynchronous: synchronize before reading the host pools."""
+    _swap(load_library().kv_swap_out, k_pool, v_pool, host_k, host_v, device_blocks,
+          host_blocks, stream)
+
+
+def kv_swap_in(k_pool, v_pool, host_k, host_v, host_blocks, device_blocks, stream=None):
+    """Copy whole blocks host_blocks[i] of the pinned host pools to device_blocks[i] of the
+    pools (C: ``kv_swap_in``)."""
+    _swap(load_library().kv_swap_in, k_pool, v_pool, host_k, host_v, host_blocks,
+          device_blocks, stream)
 
 
 def stream_read_probe(src: torch.Tensor, sink: torch.Tensor, stream=None):

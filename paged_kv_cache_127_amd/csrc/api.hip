@@ -446,6 +446,102 @@ int cow_block_copy(void* k_pool, void* v_pool, int kv_dtype, const int32_t* src_
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Device address of a host buffer that the GPU may access directly (pinned with hipHostMalloc
+// or registered), or nullptr. Pageable memory, device memory and unknown pointers give
+// nullptr; the query's own error is cleared so that it does not surface at the next launch.
+void* mapped_host_address(const void* p) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (a.type != hipMemoryTypeHost) return nullptr;
+  return a.devicePointer;
+}
+
+// Shared body of kv_swap_out (to_host = true) and kv_swap_in.
+int swap_impl(const char* fn, bool to_host, void* k_pool, void* v_pool, int kv_dtype,
+              void* host_k, void* host_v, int num_host_blocks, const int32_t* src_blocks,
+              const int32_t* dst_blocks, int num_pairs, int num_kv_heads, int head_dim,
+              int block_size, int num_blocks, void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0 || num_host_blocks <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "%s: non-positive size", fn);
+  if (!k_pool || !v_pool || !host_k || !host_v || !src_blocks || !dst_blocks)
+    return fail(PKV_ERR_INVALID_ARG, "%s: null pointer", fn);
+  const int es = elem_bytes(kv_dtype);
+  if (es == 0) return fail(PKV_ERR_UNSUPPORTED, "%s: kv_dtype %d", fn, kv_dtype);
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * es;
+  if (block_bytes % 16 != 0 || block_bytes / 16 >= ((int64_t)1 << 31))
+    return fail(PKV_ERR_UNSUPPORTED, "%s: block of %lld bytes", fn, (long long)block_bytes);
+  if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool) |
+       reinterpret_cast<uintptr_t>(host_k) | reinterpret_cast<uintptr_t>(host_v)) & 15)
+    return fail(PKV_ERR_INVALID_ARG, "%s: pools must be 16-byte aligned", fn);
+  if (num_pairs == 0) return ok();
+  void* hk = mapped_host_address(host_k);
+  void* hv = mapped_host_address(host_v);
+  if (!hk || !hv)
+    return fail(PKV_ERR_INVALID_ARG,
+                "%s: host_k / host_v must be pinned host memory mapped for the device", fn);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int src_count = to_host ? num_blocks : num_host_blocks;
+  const int dst_count = to_host ? num_host_blocks : num_blocks;
+  if (validate_mode()) {
+    std::vector<int32_t> src, dst;
+    if (!copy_ints(src, src_blocks, num_pairs, st) || !copy_ints(dst, dst_blocks, num_pairs, st))
+      return fail(PKV_ERR_LAUNCH, "%s: validation copy failed", fn);
+    std::unordered_set<int32_t> dsts;
+    for (int i = 0; i < num_pairs; ++i) {
+      if (src[i] < 0 || src[i] >= src_count)
+        return fail(PKV_ERR_VALIDATION, "pair %d: source block %d outside [0, %d)", i, src[i],
+                    src_count);
+      if (dst[i] < 0 || dst[i] >= dst_count)
+        return fail(PKV_ERR_VALIDATION, "pair %d: destination block %d outside [0, %d)", i,
+                    dst[i], dst_count);
+      if (!dsts.insert(dst[i]).second)
+        return fail(PKV_ERR_VALIDATION, "pair %d: destination used twice", i);
+    }
+  }
+  pkv::SwapParams p{};
+  if (to_host) {
+    p = {k_pool, v_pool, hk, hv, src_blocks, dst_blocks, num_pairs, src_count, dst_count,
+         (int)(block_bytes / 16)};
+  } else {
+    p = {hk, hv, k_pool, v_pool, src_blocks, dst_blocks, num_pairs, src_count, dst_count,
+         (int)(block_bytes / 16)};
+  }
+  hipError_t e = timed(to_host ? "swap_out" : "swap_in", st,
+                       [&] { return pkv::launch_block_copy(p, st); });
+  if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_swap_out(const void* k_pool, const void* v_pool, int kv_dtype, void* host_k,
+                void* host_v, int num_host_blocks, const int32_t* device_blocks,
+                const int32_t* host_blocks, int num_pairs, int num_kv_heads, int head_dim,
+                int block_size, int num_blocks, void* stream) {
+  return swap_impl("kv_swap_out", true, const_cast<void*>(k_pool), const_cast<void*>(v_pool),
+                   kv_dtype, host_k, host_v, num_host_blocks, device_blocks, host_blocks,
+                   num_pairs, num_kv_heads, head_dim, block_size, num_blocks, stream);
+}
+
+int kv_swap_in(void* k_pool, void* v_pool, int kv_dtype, const void* host_k, const void* host_v,
+               int num_host_blocks, const int32_t* host_blocks, const int32_t* device_blocks,
+               int num_pairs, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+               void* stream) {
+  return swap_impl("kv_swap_in", false, k_pool, v_pool, kv_dtype, const_cast<void*>(host_k),
+                   const_cast<void*>(host_v), num_host_blocks, host_blocks, device_blocks,
+                   num_pairs, num_kv_heads, head_dim, block_size, num_blocks, stream);
+}
+
 int pkv_set_validate(int on) {
   g_validate = on ? 1 : 0;
   return ok();

@@ -80,6 +80,23 @@ struct CowParams {
 };
 hipError_t launch_cow(const CowParams& p, int elem_bytes, hipStream_t st);
 
+// Whole-block copy between two pools of one block shape (swap.hip): block src_ids[i] of
+// (src_k, src_v) to block dst_ids[i] of (dst_k, dst_v). `units` = 16-byte units per block of
+// one pool; every base pointer is 16-byte aligned. One side may be mapped host memory.
+struct SwapParams {
+  const void* src_k;
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
+  const int32_t* src_ids;
+  const int32_t* dst_ids;
+  int num_pairs;
+  int src_count;   // blocks in the source pool
+  int dst_count;   // blocks in the destination pool
+  int units;
+};
+hipError_t launch_block_copy(const SwapParams& p, hipStream_t st);
+
 // Streaming-read probe (probe.hip): reads `bytes` (multiple of 16) of src once.
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int num_cus,
                               hipStream_t st);

@@ -153,3 +153,26 @@ def test_append_size_limit_and_probe_argument_checks():
     assert L.pkv_stream_read_probe(256, 1000, 16, None) == -1
     assert L.pkv_stream_read_probe(264, 1024, 16, None) == -1
     assert L.pkv_stream_read_probe(256, 0, 16, None) == -1
+
+
+def test_swap_argument_checks():
+    """Rejections that come before any HIP call: sizes, null pointers, cache dtype, alignment;
+    zero pairs with valid arguments is a no-op."""
+    L = pkv.load_library()
+    ok = (0x1000, 0x2000, 2, 0x3000, 0x4000, 4, 0x5000, 0x6000, 3, 2, 64, 16, 8, None)
+
+    def call(fn, **kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return fn(*a)
+
+    for fn in (L.kv_swap_out, L.kv_swap_in):
+        assert call(fn, a8=0) == 0
+        assert call(fn, a8=-1) == -1
+        assert call(fn, a5=0) == -1                     # no host blocks
+        assert call(fn, a9=0) == -1                     # no heads
+        assert call(fn, a3=None) == -1 and call(fn, a6=None) == -1 and call(fn, a0=None) == -1
+        assert call(fn, a2=5) == -2                     # unknown cache dtype
+        assert call(fn, a4=0x4008) == -1                # host pool not 16-byte aligned
+        assert call(fn, a1=0x2004) == -1
