@@ -273,6 +273,24 @@ def swap_figures(pkv, W, torch, dev: str, preempt: int = 32, launches: int = 10)
     out_us = kernel_us("swap_out", lambda: pkv.kv_swap_out(kp, vp, hk, hv, dev_ids, host_ids))
     in_us = kernel_us("swap_in", lambda: pkv.kv_swap_in(kp, vp, hk, hv, host_ids, back_ids))
     torch.cuda.synchronize()
+    # the GQA decode alone, then with swap-outs running on a second stream meanwhile
+    q, tab, lens = b.q.to(dev), torch.from_numpy(b.tables).to(dev), torch.from_numpy(b.lengths).to(dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ws = pkv.decode_workspace(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, 0, dev)
+    dec = lambda: pkv.paged_attn_decode(out, q, kp, vp, tab, lens, int(b.lengths.max()),
+                                        workspace=ws)
+    dec_alone = kernel_us("decode_partial", dec)
+    s2 = torch.cuda.Stream()
+    pkv.timing_enable(True, every=1)
+    for _ in range(3):
+        pkv.kv_swap_out(kp, vp, hk, hv, dev_ids, host_ids, stream=s2)
+    for _ in range(20):      # about 4 ms of decode against 5 ms of swap-out
+        dec()
+    torch.cuda.synchronize()
+    dms, dn = pkv.timing_query("decode_partial")
+    sms, sn = pkv.timing_query("swap_out")
+    pkv.timing_enable(False)
+    del q, tab, lens, out, ws
     moved = (torch.equal(hk[0].view(torch.int16), b.k_pool[blocks[0]].view(torch.int16)) and
              torch.equal(kp[free[-1]].cpu().view(torch.int16),
                          b.k_pool[blocks[-1]].view(torch.int16)))
@@ -310,6 +328,10 @@ def swap_figures(pkv, W, torch, dev: str, preempt: int = 32, launches: int = 10)
         "dma_h2d_us": round(h2d_us, 2), "dma_h2d_gbs": gbs(h2d_us),
         "out_frac_of_dma": round(d2h_us / out_us, 4), "in_frac_of_dma": round(h2d_us / in_us, 4),
         "bound": "host link (ceiling: contiguous DMA copy of the same bytes)",
+        "overlap": {"what": "swap-outs on a second stream while the GQA decode (plain call) runs",
+                    "decode_us_alone": round(dec_alone, 2),
+                    "decode_us_during_swap": round(dms / dn * 1e3, 2),
+                    "swap_out_gbs_during_decode": gbs(sms / sn * 1e3)},
     }
     print(f"bench: swap out {res['swap_out_gbs']} GB/s in {res['swap_in_gbs']} GB/s "
           f"(DMA {res['dma_d2h_gbs']} / {res['dma_h2d_gbs']})", file=sys.stderr, flush=True)

@@ -20,13 +20,15 @@ closed forms, library routines or brute force, not to itself. No function is "pa
 unpinned".
 """
 from .attention import (attend, contiguous_decode, gather_kv, merge_states,
-                        paged_decode, paged_decode_split, partial_state, token_address)
+                        paged_decode, paged_decode_split, partial_state, shared_prefix_decode,
+                        token_address)
 from .bookkeeping import (BlockPool, PagedKVModel, RefcountError, PoolExhausted,
                           blocks_for, copy_blocks, capacity_report, reserved_slots, shareable_prefix_blocks)
 
 __all__ = [
     "attend", "contiguous_decode", "gather_kv", "merge_states",
-    "paged_decode", "paged_decode_split", "partial_state", "token_address", "BlockPool",
+    "paged_decode", "paged_decode_split", "partial_state", "shared_prefix_decode",
+    "token_address", "BlockPool",
     "PagedKVModel", "RefcountError", "PoolExhausted", "blocks_for", "copy_blocks", "capacity_report",
     "reserved_slots", "shareable_prefix_blocks",
 ]

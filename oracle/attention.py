@@ -171,6 +171,49 @@ def paged_decode_split(q, k_pool, v_pool, tables, lengths, block_size: int,
     return out
 
 
+def shared_prefix_decode(q, k_pool, v_pool, prefix_blocks, prefix_len: int, tables, lengths,
+                         block_size: int, scale=None):
+    """The same output for a batch whose sequences all begin with one shared prefix, computed
+    the way prefix sharing allows: the prefix's keys and values are gathered once, through the
+    shared block list ("PagedAttention: Virtual Memory for the KV Cache", section "Sharing a
+    prefix and copying a partial block": sharers point their tables at the same full blocks),
+    each query row's partial state over the prefix and over its own suffix tokens
+    [prefix_len, L_s) is taken, and the two merge with the log-sum-exp rule ("Paged Attention
+    and vLLM", section "Paged Attention CUDA Kernel").
+
+    Reading: the shared prefix is whole blocks (``prefix_len`` a multiple of ``block_size``,
+    ``prefix_blocks`` its ``prefix_len / block_size`` physical ids); every sequence holds at
+    least ``prefix_len`` tokens; its suffix token p sits at ``tables[s][p // B]``, offset
+    ``p % B`` (table entries before ``prefix_len / B`` are not read)."""
+    S, Hq, Hkv, G, d = _heads(q, k_pool)
+    B = int(block_size)
+    P = int(prefix_len)
+    if P % B or len(prefix_blocks) * B < P:
+        raise ValueError("the shared prefix must be whole blocks")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    qf = _f64(q)
+    out = np.zeros((S, Hq, d))
+    pos = np.arange(P)
+    phys = np.asarray(prefix_blocks, dtype=np.int64)[pos // B]
+    for g in range(Hkv):
+        Kp = _index(k_pool, phys, g, pos % B)     # gathered once for every sharer
+        Vp = _index(v_pool, phys, g, pos % B)
+        for s in range(S):
+            L = int(lengths[s])
+            if L < P:
+                raise ValueError(f"sequence {s} is shorter than the shared prefix")
+            spos = np.arange(P, L)
+            sphys = np.asarray(tables[s], dtype=np.int64)[spos // B]
+            Ks = _index(k_pool, sphys, g, spos % B)
+            Vs = _index(v_pool, sphys, g, spos % B)
+            for i in range(G):
+                h = g * G + i
+                out[s, h] = merge_states([partial_state(qf[s, h], Kp, Vp, scale),
+                                          partial_state(qf[s, h], Ks, Vs, scale)])
+    return out
+
+
 def contiguous_decode(q, k_logical, v_logical, scale=None):
     """The same output from the logical (never paged) per-sequence K/V ``[H_kv][L][d]``."""
     qf = _f64(q)

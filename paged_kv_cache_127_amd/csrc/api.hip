@@ -514,8 +514,9 @@ int swap_impl(const char* fn, bool to_host, void* k_pool, void* v_pool, int kv_d
     p = {hk, hv, k_pool, v_pool, src_blocks, dst_blocks, num_pairs, src_count, dst_count,
          (int)(block_bytes / 16)};
   }
+  const int cus = cu_count();
   hipError_t e = timed(to_host ? "swap_out" : "swap_in", st,
-                       [&] { return pkv::launch_block_copy(p, st); });
+                       [&] { return pkv::launch_block_copy(p, cus, st); });
   if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "%s: %s", fn, hipGetErrorString(e));
   return ok();
 }

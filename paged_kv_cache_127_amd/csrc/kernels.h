@@ -95,7 +95,7 @@ struct SwapParams {
   int dst_count;   // blocks in the destination pool
   int units;
 };
-hipError_t launch_block_copy(const SwapParams& p, hipStream_t st);
+hipError_t launch_block_copy(const SwapParams& p, int num_cus, hipStream_t st);
 
 // Streaming-read probe (probe.hip): reads `bytes` (multiple of 16) of src once.
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int num_cus,

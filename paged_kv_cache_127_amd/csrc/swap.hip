@@ -5,10 +5,12 @@
 // One launch moves a whole list of blocks. The host pool is pinned memory mapped into the
 // GPU's address space, so the kernel reads or writes it directly across the host link: no
 // staging copy in HBM and no DMA call per block. A block of one pool is one contiguous run of
-// H_kv * B * d elements. Workgroup (pair, chunk) moves up to 16 KiB of keys and 16 KiB of
-// values of one pair in 16-byte accesses; each lane issues its eight loads before its stores,
-// and each wave instruction covers one contiguous KiB. Pairs with an id outside its pool are
+// H_kv * B * d elements. A (pair, chunk) item is up to 16 KiB of keys and 16 KiB of values of
+// one pair, moved in 16-byte accesses; each lane issues its eight loads before its stores, and
+// each wave instruction covers one contiguous KiB. Pairs with an id outside its pool are
 // skipped (never dereferenced).
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -45,30 +47,39 @@ __device__ __forceinline__ void move_chunk(const u32x4* __restrict__ sk,
 }
 
 __global__ __launch_bounds__(kSwapThreads) void block_copy_kernel(SwapParams p, int chunks) {
-  const int pair = blockIdx.x / chunks;
-  const int chunk = blockIdx.x - pair * chunks;
-  const int s = p.src_ids[pair];
-  const int d = p.dst_ids[pair];
-  if ((unsigned)s >= (unsigned)p.src_count || (unsigned)d >= (unsigned)p.dst_count) return;
-  const int U = p.units;
-  const u32x4* sk = reinterpret_cast<const u32x4*>(p.src_k) + (size_t)s * U;
-  const u32x4* sv = reinterpret_cast<const u32x4*>(p.src_v) + (size_t)s * U;
-  u32x4* dk = reinterpret_cast<u32x4*>(p.dst_k) + (size_t)d * U;
-  u32x4* dv = reinterpret_cast<u32x4*>(p.dst_v) + (size_t)d * U;
-  const int c0 = chunk * kSwapChunk;
-  if (c0 + kSwapChunk <= U)
-    move_chunk<true>(sk, sv, dk, dv, c0, U);
-  else
-    move_chunk<false>(sk, sv, dk, dv, c0, U);
+  const int items = p.num_pairs * chunks;
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int pair = it / chunks;
+    const int chunk = it - pair * chunks;
+    const int s = p.src_ids[pair];
+    const int d = p.dst_ids[pair];
+    if ((unsigned)s >= (unsigned)p.src_count || (unsigned)d >= (unsigned)p.dst_count) continue;
+    const int U = p.units;
+    const u32x4* sk = reinterpret_cast<const u32x4*>(p.src_k) + (size_t)s * U;
+    const u32x4* sv = reinterpret_cast<const u32x4*>(p.src_v) + (size_t)s * U;
+    u32x4* dk = reinterpret_cast<u32x4*>(p.dst_k) + (size_t)d * U;
+    u32x4* dv = reinterpret_cast<u32x4*>(p.dst_v) + (size_t)d * U;
+    const int c0 = chunk * kSwapChunk;
+    if (c0 + kSwapChunk <= U)
+      move_chunk<true>(sk, sv, dk, dv, c0, U);
+    else
+      move_chunk<false>(sk, sv, dk, dv, c0, U);
+  }
 }
 
-hipError_t launch_block_copy(const SwapParams& p, hipStream_t st) {
+// The host link, not the device, bounds a swap: 8 to 16 workgroups already keep enough 16-byte
+// accesses in flight to reach it. The grid is one workgroup per compute unit, looping over
+// (pair, chunk) items. With decode running on another stream meanwhile, an even spread of one
+// workgroup per CU slows every decode worker alike; a smaller grid sits on some CUs only and
+// stretches the static decode schedule more (measured: decode 277 us with one workgroup per CU,
+// 313-334 us with 32-64 workgroups, 182 us alone).
+hipError_t launch_block_copy(const SwapParams& p, int num_cus, hipStream_t st) {
   if (p.num_pairs <= 0 || p.units <= 0) return hipSuccess;
   const int chunks = (p.units + kSwapChunk - 1) / kSwapChunk;
-  const int64_t grid = (int64_t)p.num_pairs * chunks;
-  if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(block_copy_kernel, dim3((unsigned)grid), dim3(kSwapThreads), 0, st, p,
-                     chunks);
+  const int64_t items = (int64_t)p.num_pairs * chunks;
+  if (items >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int grid = (int)std::min<int64_t>(items, std::max(num_cus, 1));
+  hipLaunchKernelGGL(block_copy_kernel, dim3(grid), dim3(kSwapThreads), 0, st, p, chunks);
   return hipGetLastError();
 }
 

@@ -264,6 +264,49 @@ def config4a(num_seqs: int = 128, prefix_len: int = 800, poison: bool = False) -
                  seed, "config4a")
 
 
+def shared_prefix_batch(suffix_lens, prefix_len: int, num_q_heads: int, num_kv_heads: int,
+                        head_dim: int, block_size: int, dtype: torch.dtype, seed: int,
+                        poison: bool = False) -> Batch:
+    """Sequences that all begin with one ``prefix_len``-token prefix held in shared whole
+    blocks (the first ``prefix_len / B`` entries of every table), followed by private suffixes
+    of ``suffix_lens`` tokens (0 allowed); random placement in a 1.25x pool. Same draw order as
+    :func:`config4a`: suffix lengths are given, then placement, Q, prefix K/V, suffix K/V."""
+    B, Hkv, d = block_size, num_kv_heads, head_dim
+    assert prefix_len % B == 0
+    suffix = np.asarray(suffix_lens, dtype=np.int32)
+    S = len(suffix)
+    lengths = (prefix_len + suffix).astype(np.int32)
+    npre = prefix_len // B
+    nsuf = [_ceil_div(int(x), B) for x in suffix]
+    need = npre + sum(nsuf)
+    nblk = max(1, math.ceil(1.25 * need))
+    perm = rng_for(seed, _PLACE).permutation(nblk).astype(np.int32)
+    max_blocks = max(1, npre + max(nsuf, default=0))
+    tables = np.full((S, max_blocks), -1, dtype=np.int32)
+    tables[:, :npre] = perm[:npre]
+    cur = npre
+    for s in range(S):
+        tables[s, npre:npre + nsuf[s]] = perm[cur:cur + nsuf[s]]
+        cur += nsuf[s]
+    q = normal(rng_for(seed, _Q), (S, num_q_heads, d), dtype)
+    rkv = rng_for(seed, _KV)
+    kp = normal(rkv, (Hkv, prefix_len, d), dtype)
+    vp = normal(rkv, (Hkv, prefix_len, d), dtype)
+    rs = rng_for(seed, _SUFFIX)
+    k_log, v_log = [], []
+    k_pool, v_pool = empty_pools(nblk, Hkv, B, d, dtype, poison)
+    if S:
+        write_rows(k_pool, v_pool, tables[0], kp, vp)
+    for s in range(S):
+        ks = normal(rs, (Hkv, int(suffix[s]), d), dtype)
+        vs = normal(rs, (Hkv, int(suffix[s]), d), dtype)
+        write_rows(k_pool, v_pool, tables[s], ks, vs, start=prefix_len)
+        k_log.append(torch.cat([kp, ks], dim=1))
+        v_log.append(torch.cat([vp, vs], dim=1))
+    return Batch(dtype, B, num_q_heads, Hkv, d, lengths, tables, nblk, q, k_pool, v_pool, k_log,
+                 v_log, seed, "shared_prefix")
+
+
 def config4a_private(shared: Batch) -> Batch:
     """The same logical data as :func:`config4a` with every sequence holding private copies of
     the prefix blocks (no sharing)."""
