@@ -108,6 +108,29 @@ def _decode_timing(pkv, torch, launch, launches: int):
     return out
 
 
+def _kernel_times(pkv, torch, launch, names, launches: int):
+    """({kernel name: mean us}, step p50 us) of `launch`, hipEvents around every launch of each
+    library kernel and torch events around every call."""
+    for _ in range(5):
+        launch()
+    torch.cuda.synchronize()
+    pkv.timing_enable(True, every=1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(launches)]
+    for a, b_ in ev:
+        a.record()
+        launch()
+        b_.record()
+    torch.cuda.synchronize()
+    out = {}
+    for name in names:
+        ms, n = pkv.timing_query(name)
+        out[name] = ms / n * 1e3 if n else 0.0
+    pkv.timing_enable(False)
+    steps = sorted(a.elapsed_time(b_) * 1e3 for a, b_ in ev)
+    return out, steps[len(steps) // 2]
+
+
 def other_configs(pkv, W, torch, dev: str, workers: int, launches: int = 30):
     """Figures on the other batch configs: decode-kernel roofline for the HBM-bound ones (GQA
     at block size 32, multi-head fp16, long contexts with their 8-token append per step),
@@ -190,7 +213,29 @@ def other_configs(pkv, W, torch, dev: str, workers: int, launches: int = 30):
         "logical_kv_bytes": b.kv_bytes, "decode_us": round(dus, 2), "merge_us": round(mus, 2),
         "logical_gbs": round(b.kv_bytes / (dus * 1e-6) / 1e9, 1), "cache_assisted": True,
         "step_p50_us": round(step, 2)}
-    del t
+    # the same batch through the shared-prefix call: the 50 prefix blocks read once for all
+    # 128 sharers (prefix states), the decode over the suffixes, the per-row merge
+    P = 800
+    S, Hq, d = b.q.shape
+    pre = t["tab"][0, :P // b.block_size].contiguous()
+    ws_sp = pkv.shared_prefix_workspace(S, Hq, b.num_kv_heads, d, P, workers, dev)
+
+    def sp_call():
+        pkv.paged_attn_decode_shared_prefix(t["out"], t["q"], t["kp"], t["vp"], pre, P, t["tab"],
+                                            t["lens"], t["mx"], num_workers=workers,
+                                            workspace=ws_sp)
+    kt, sp_step = _kernel_times(pkv, torch, sp_call, ("prefix_states", "decode_partial",
+                                                       "splitk_reduce", "prefix_combine"),
+                                launches)
+    unique = 2 * (P + int(b.lengths.sum()) - S * P) * b.num_kv_heads * d * 2
+    res["shared_prefix128"]["shared_prefix_call"] = {
+        "what": "paged_attn_decode_shared_prefix on the same batch (prefix read once)",
+        "kernel_us": {k: round(v, 2) for k, v in kt.items()},
+        "step_p50_us": round(sp_step, 2), "unique_kv_bytes": unique,
+        "unique_gbs": round(unique / (sp_step * 1e-6) / 1e9, 1),
+        "logical_gbs": round(b.kv_bytes / (sp_step * 1e-6) / 1e9, 1),
+        "speedup_vs_plain_step": round(step / sp_step, 3)}
+    del t, ws_sp
     # copy-on-write pairs: copy 8 slots of each pair's shared partial block, append B's token,
     # decode all 128 sequences (the copy and append rewrite the same slots every call)
     b = W.config4b()

@@ -143,6 +143,41 @@ int paged_attn_decode_append(void* out, int out_dtype, const void* q, void* k_po
                              size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Decode step of sequences that all begin with one shared prefix: the same result as
+ * paged_attn_decode on the same arguments (up to rounding order), with the prefix's keys and
+ * values read once per step for all sharers instead of once per sequence ([P1] "Sharing a
+ * prefix and copying a partial block": sharers' tables point at the same full blocks; [P3]
+ * "RadixAttention: caching, not just packing, the prefix": requests that begin with the same
+ * prompt hold it once and differ only in their own suffixes). The softmax state of every
+ * query row over the prefix and its state over the sequence's own suffix merge exactly by the
+ * log-sum-exp rule ([P2] "Paged Attention CUDA Kernel"): one matrix-core kernel takes the
+ * states of all S * G rows of each KV head over the prefix, the decode kernel runs over each
+ * suffix, and a third kernel merges the two per row.
+ *   prefix_blocks  device int32 [prefix_len / block_size]: the shared blocks, in token order
+ *   prefix_len     tokens of the prefix: a positive multiple of block_size (only whole blocks
+ *                  are shared), at most max_context_len
+ *   block_tables   as for paged_attn_decode; entries [0, prefix_len / block_size) of every row
+ *                  equal prefix_blocks and are not read
+ *   context_lens   every context_lens[s] >= prefix_len (the suffix may be empty)
+ *   workspace      device, 256-byte aligned, at least pkv_shared_prefix_workspace_size(...)
+ *                  bytes for the same sizes, num_workers and prefix_len
+ * 16-bit caches with 2 to 16 query heads per KV head (PKV_ERR_UNSUPPORTED otherwise); one call
+ * per group of sequences that share a prefix. Under PAGEDKV_VALIDATE the shared table entries,
+ * the lengths and the prefix ids are checked first.
+ * --------------------------------------------------------------------------------------- */
+size_t pkv_shared_prefix_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                        int head_dim, int num_workers, int prefix_len);
+int paged_attn_decode_shared_prefix(void* out, int out_dtype, const void* q, const void* k_pool,
+                                    const void* v_pool, int kv_dtype,
+                                    const int32_t* prefix_blocks, int prefix_len,
+                                    const int32_t* block_tables, int max_blocks_per_seq,
+                                    const int32_t* context_lens, int max_context_len,
+                                    int num_seqs, int num_q_heads, int num_kv_heads,
+                                    int head_dim, int block_size, int num_blocks, float scale,
+                                    int num_workers, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Append: store the keys and values of new tokens into their slots
  * ([P1] "Growing a request"; [P2] "KV Cache Fundamentals": the cache grows by one row per
  * head per generated token). For every i < num_tokens and KV head g:

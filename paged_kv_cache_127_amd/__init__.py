@@ -15,7 +15,8 @@ import torch  # loaded first: the library then binds to the HIP runtime torch al
 
 __all__ = [
     "PagedKVError", "paged_attn_decode", "paged_attn_decode_append", "kv_cache_append",
-    "cow_block_copy", "kv_swap_out", "kv_swap_in", "pkv_decode_workspace_size", "decode_workspace",
+    "cow_block_copy", "kv_swap_out", "kv_swap_in", "paged_attn_decode_shared_prefix",
+    "shared_prefix_workspace", "pkv_decode_workspace_size", "decode_workspace",
     "pkv_decode_auto_workers", "BlockPool", "timing_enable", "timing_query",
     "stream_read_probe", "set_validate", "library_path", "load_library", "PKV_F32", "PKV_F16",
     "PKV_BF16",
@@ -64,6 +65,11 @@ def _declare(L):
                                     c_void, c_int, c_int, c_int, c_int, c_int, c_int, c_void]),
         "cow_block_copy": (c_int, [c_void, c_void, c_int, c_void, c_void, c_void, c_int, c_int,
                                    c_int, c_int, c_int, c_void]),
+        "pkv_shared_prefix_workspace_size": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int]),
+        "paged_attn_decode_shared_prefix": (c_int, [c_void, c_int, c_void, c_void, c_void, c_int,
+                                                    c_void, c_int, c_void, c_int, c_void, c_int,
+                                                    c_int, c_int, c_int, c_int, c_int, c_int,
+                                                    c_float, c_int, c_void, c_size, c_void]),
         "kv_swap_out": (c_int, [c_void, c_void, c_int, c_void, c_void, c_int, c_void, c_void,
                                 c_int, c_int, c_int, c_int, c_int, c_void]),
         "kv_swap_in": (c_int, [c_void, c_void, c_int, c_void, c_void, c_int, c_void, c_void,
@@ -184,6 +190,51 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
         int(block_tables.shape[1]), _dev(context_lens, "context_lens", torch.int32),
         int(max_context_len), S, Hq, Hkv, d, B, N, float(scale), int(num_workers), ws_ptr,
         ws_bytes, _stream(stream)))
+    return out
+
+
+def shared_prefix_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, prefix_len,
+                            num_workers=0, device="cuda") -> torch.Tensor:
+    """Allocate a workspace for paged_attn_decode_shared_prefix with these sizes."""
+    n = int(load_library().pkv_shared_prefix_workspace_size(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, num_workers, prefix_len))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def paged_attn_decode_shared_prefix(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
+                                    v_pool: torch.Tensor, prefix_blocks: torch.Tensor,
+                                    prefix_len: int, block_tables: torch.Tensor,
+                                    context_lens: torch.Tensor, max_context_len: int,
+                                    scale: float = 0.0, num_workers: int = 0,
+                                    workspace: Optional[torch.Tensor] = None,
+                                    stream=None) -> torch.Tensor:
+    """paged_attn_decode for sequences that all begin with the ``prefix_len`` tokens held in
+    the shared blocks ``prefix_blocks`` (int32 [prefix_len / B]), which are read once for all of
+    them (C: ``paged_attn_decode_shared_prefix``). Other arguments as paged_attn_decode."""
+    L = load_library()
+    kdt = _kv_dtype(k_pool)
+    if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape or out.shape != q.shape:
+        raise ValueError("bad tensor ranks or out shape; k_pool and v_pool must match")
+    S, Hq, d = q.shape
+    N, Hkv, B, d2 = k_pool.shape
+    if d2 != d:
+        raise ValueError("head_dim of q and the pools differ")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+        raise ValueError("block_tables must be [S][max_blocks] and context_lens [S]")
+    if prefix_blocks.dim() != 1 or prefix_blocks.shape[0] * B < int(prefix_len):
+        raise ValueError("prefix_blocks must list the prefix_len / B shared blocks")
+    if out.dtype not in (torch.float32, k_pool.dtype):
+        raise TypeError("out must be float32 or the cache dtype")
+    if workspace is None:
+        workspace = shared_prefix_workspace(S, Hq, Hkv, d, prefix_len, num_workers, q.device)
+    _check(L.paged_attn_decode_shared_prefix(
+        _dev(out, "out"), _DT[out.dtype], _dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool", k_pool.dtype), kdt, _dev(prefix_blocks, "prefix_blocks", torch.int32),
+        int(prefix_len), _dev(block_tables, "block_tables", torch.int32),
+        int(block_tables.shape[1]), _dev(context_lens, "context_lens", torch.int32),
+        int(max_context_len), S, Hq, Hkv, d, B, N, float(scale), int(num_workers),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
     return out
 
 

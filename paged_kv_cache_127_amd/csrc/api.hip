@@ -197,7 +197,7 @@ int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const v
                 const int32_t* context_lens, int max_context_len, int num_seqs,
                 int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
                 float scale, int num_workers, void* workspace, size_t workspace_bytes,
-                void* stream) {
+                void* stream, float* lse = nullptr, bool validate = true) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
       num_blocks <= 0 || max_context_len < 0)
     return fail(PKV_ERR_INVALID_ARG, "%s: non-positive size", fn);
@@ -265,7 +265,7 @@ int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const v
     return fail(PKV_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
-  if (validate_mode()) {
+  if (validate && validate_mode()) {
     std::vector<int32_t> lens, tabs;
     if (!copy_ints(lens, context_lens, num_seqs, st) ||
         !copy_ints(tabs, block_tables, (size_t)num_seqs * max_blocks_per_seq, st))
@@ -314,6 +314,7 @@ int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const v
   p.ws_m = reinterpret_cast<float*>(ws + wl.m);
   p.ws_l = reinterpret_cast<float*>(ws + wl.l);
   p.prefix = reinterpret_cast<int64_t*>(ws + wl.prefix);
+  p.lse = lse;
 
   hipError_t e;
   if (use_mfma) {
@@ -521,9 +522,154 @@ int swap_impl(const char* fn, bool to_host, void* k_pool, void* v_pool, int kv_d
   return ok();
 }
 
+// Workspace of the shared-prefix call: the suffix decode's workspace, then the suffix lengths,
+// the suffix rows' log-sum-exp, an fp32 suffix output (used when the output is 16-bit) and the
+// prefix states of every chunk group.
+struct SpLayout {
+  size_t decode, suffix_lens, lse, o, m, l, acc, total;
+  int chunk_groups, steps_per_chunk;
+};
+
+SpLayout sp_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int n,
+                   int prefix_len) {
+  const int G = num_q_heads / num_kv_heads;
+  SpLayout L;
+  pkv::prefix_plan(num_seqs, G, num_kv_heads, prefix_len, cu_count(), &L.chunk_groups,
+                   &L.steps_per_chunk);
+  const size_t SH = (size_t)num_seqs * num_q_heads;
+  L.decode = ws_layout(num_seqs, G, head_dim, n).total;
+  L.suffix_lens = align256(L.decode);
+  L.lse = L.suffix_lens + align256((size_t)num_seqs * sizeof(int32_t));
+  L.o = L.lse + align256(SH * sizeof(float));
+  L.m = L.o + align256(SH * head_dim * sizeof(float));
+  L.l = L.m + align256((size_t)L.chunk_groups * SH * sizeof(float));
+  L.acc = L.l + align256((size_t)L.chunk_groups * SH * sizeof(float));
+  L.total = L.acc + align256((size_t)L.chunk_groups * SH * head_dim * sizeof(float));
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t pkv_shared_prefix_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                        int head_dim, int num_workers, int prefix_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_q_heads % num_kv_heads != 0 || num_workers < 0 || prefix_len <= 0)
+    return 0;
+  return sp_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, choose_workers(num_workers),
+                   prefix_len)
+      .total;
+}
+
+int paged_attn_decode_shared_prefix(void* out, int out_dtype, const void* q, const void* k_pool,
+                                    const void* v_pool, int kv_dtype,
+                                    const int32_t* prefix_blocks, int prefix_len,
+                                    const int32_t* block_tables, int max_blocks_per_seq,
+                                    const int32_t* context_lens, int max_context_len,
+                                    int num_seqs, int num_q_heads, int num_kv_heads,
+                                    int head_dim, int block_size, int num_blocks, float scale,
+                                    int num_workers, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  const char* fn = "paged_attn_decode_shared_prefix";
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+      num_blocks <= 0 || max_context_len < 0 || num_workers < 0)
+    return fail(PKV_ERR_INVALID_ARG, "%s: non-positive size", fn);
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_pool || !v_pool || !prefix_blocks || !block_tables || !context_lens)
+    return fail(PKV_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (kv_dtype != PKV_F16 && kv_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: kv_dtype %d (fp16 or bf16 caches)", fn, kv_dtype);
+  if (!(out_dtype == PKV_F32 || out_dtype == kv_dtype))
+    return fail(PKV_ERR_UNSUPPORTED, "%s: out_dtype %d with kv_dtype %d", fn, out_dtype,
+                kv_dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128)", fn, head_dim);
+  if (block_size != 16 && block_size != 32)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: block_size %d (16 or 32)", fn, block_size);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "%s: %d query heads not a multiple of %d KV heads", fn,
+                num_q_heads, num_kv_heads);
+  const int G = num_q_heads / num_kv_heads;
+  if (G < 2 || G > 16)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: %d query heads per KV head (2 to 16)", fn, G);
+  if (prefix_len <= 0 || prefix_len % block_size != 0 || prefix_len > max_context_len)
+    return fail(PKV_ERR_INVALID_ARG,
+                "%s: prefix_len %d must be a positive multiple of %d, at most %d", fn,
+                prefix_len, block_size, max_context_len);
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PKV_ERR_INVALID_ARG, "%s: max_context_len %d exceeds table capacity %d x %d",
+                fn, max_context_len, max_blocks_per_seq, block_size);
+  const int n = choose_workers(num_workers);
+  const SpLayout sl = sp_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, n, prefix_len);
+  if (!workspace || workspace_bytes < sl.total)
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", fn,
+                workspace_bytes, sl.total);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(PKV_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int nb = prefix_len / block_size;
+
+  if (validate_mode()) {
+    std::vector<int32_t> lens, tabs, pre;
+    if (!copy_ints(lens, context_lens, num_seqs, st) || !copy_ints(pre, prefix_blocks, nb, st) ||
+        !copy_ints(tabs, block_tables, (size_t)num_seqs * max_blocks_per_seq, st))
+      return fail(PKV_ERR_LAUNCH, "%s: validation copy failed", fn);
+    for (int j = 0; j < nb; ++j)
+      if (pre[j] < 0 || pre[j] >= num_blocks)
+        return fail(PKV_ERR_VALIDATION, "prefix_blocks[%d] = %d outside [0, %d)", j, pre[j],
+                    num_blocks);
+    for (int s = 0; s < num_seqs; ++s) {
+      if (lens[s] < prefix_len || lens[s] > max_context_len)
+        return fail(PKV_ERR_VALIDATION, "context_lens[%d] = %d outside [%d, %d]", s, lens[s],
+                    prefix_len, max_context_len);
+      const int32_t* row = tabs.data() + (size_t)s * max_blocks_per_seq;
+      for (int j = 0; j < nb; ++j)
+        if (row[j] != pre[j])
+          return fail(PKV_ERR_VALIDATION, "block_tables[%d][%d] = %d is not prefix block %d", s,
+                      j, row[j], pre[j]);
+      const int nbs = (lens[s] + block_size - 1) / block_size;
+      for (int j = nb; j < nbs; ++j)
+        if (row[j] < 0 || row[j] >= num_blocks)
+          return fail(PKV_ERR_VALIDATION, "block_tables[%d][%d] = %d outside [0, %d)", s, j,
+                      row[j], num_blocks);
+    }
+  }
+
+  char* ws = reinterpret_cast<char*>(workspace);
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim);
+  int32_t* suffix_lens = reinterpret_cast<int32_t*>(ws + sl.suffix_lens);
+  float* lse = reinterpret_cast<float*>(ws + sl.lse);
+  float* o_suffix = out_dtype == PKV_F32 ? reinterpret_cast<float*>(out)
+                                         : reinterpret_cast<float*>(ws + sl.o);
+  float* st_m = reinterpret_cast<float*>(ws + sl.m);
+  float* st_l = reinterpret_cast<float*>(ws + sl.l);
+  float* st_acc = reinterpret_cast<float*>(ws + sl.acc);
+
+  pkv::PrefixParams pp{q, k_pool, v_pool, prefix_blocks, context_lens, suffix_lens, st_m, st_l,
+                       st_acc, num_seqs, num_q_heads, num_kv_heads, num_blocks, prefix_len,
+                       sl.chunk_groups, sl.steps_per_chunk, sc * 1.4426950408889634f};
+  hipError_t e = timed("prefix_states", st, [&] {
+    return pkv::launch_prefix_states(pp, kv_dtype, head_dim, block_size, st);
+  });
+  if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "%s: prefix kernel: %s", fn,
+                                   hipGetErrorString(e));
+  // the suffix: the same tables past the prefix entries (row stride unchanged), the lengths
+  // the prefix kernel wrote, normalised fp32 rows and their log-sum-exp
+  const int rc = decode_impl(fn, o_suffix, PKV_F32, q, k_pool, v_pool, kv_dtype, nullptr,
+                             nullptr, block_tables + nb, max_blocks_per_seq, suffix_lens,
+                             max_context_len - prefix_len, num_seqs, num_q_heads, num_kv_heads,
+                             head_dim, block_size, num_blocks, scale, n, workspace, sl.decode,
+                             stream, lse, false);
+  if (rc != PKV_OK) return rc;
+  pkv::CombineParams cp{out, o_suffix, lse, st_m, st_l, st_acc, out_dtype == PKV_F32 ? 1 : 0,
+                        num_seqs, num_q_heads, num_kv_heads, sl.chunk_groups};
+  e = timed("prefix_combine", st,
+            [&] { return pkv::launch_prefix_combine(cp, kv_dtype, head_dim, st); });
+  if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "%s: combine kernel: %s", fn,
+                                   hipGetErrorString(e));
+  return ok();
+}
 
 int kv_swap_out(const void* k_pool, const void* v_pool, int kv_dtype, void* host_k,
                 void* host_v, int num_host_blocks, const int32_t* device_blocks,

@@ -28,22 +28,14 @@
 // Two steps' loads (with their query rows) are in flight while a step computes.
 // Fused append (k_new set): in a segment's last step, the lanes of the row of token L - 1 read
 // it from k_new / v_new instead of the pool (the merge kernel stores it into its slot later).
+// With p.lse set, a whole segment also writes each row's log-sum-exp m + log2(l) (the
+// shared-prefix path merges the output with the prefix's states through it).
 #include "device_common.h"
 #include "kernels.h"
+#include "mfma_common.h"
 #include "schedule.h"
 
 namespace pkv {
-
-template <typename T>
-__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
-  if constexpr (__is_same(T, bf16_t)) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-}
 
 template <int D>
 struct StepRegs {
@@ -51,40 +43,6 @@ struct StepRegs {
   u32x4 v[D / 16];      // value rows, 16 bytes per lane per instruction
   u32x4 q[D / 32];      // Q operand (the step's query rows)
 };
-
-// Swizzle of the 32-byte pieces of value row t in the LDS tile (D / 16 pieces per row): the 16
-// rows one transposed read touches (t = 8q + 4h + 0..3, q = 0..3) land on distinct piece
-// positions in every 256-byte bank window.
-template <int D>
-__device__ __forceinline__ int piece_swizzle(int t) {
-  if constexpr (D == 128) return (t & 3) | (((t >> 3) & 1) << 2);
-  else return ((t >> 1) & 1) | (((t >> 3) & 1) << 1);
-}
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-// Four 16-bit elements, transposed across each 16-lane group (ds_read_b64_tr_b16).
-__device__ __forceinline__ uint2 lds_read_tr16(const char* lds_byte_addr) {
-  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_v4i16*)(__attribute__((address_space(3))) char*)lds_byte_addr);
-  return __builtin_bit_cast(uint2, r);
-}
-
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Split two fp32 probabilities into packed 16-bit high parts and remainders.
-template <typename T>
-__device__ __forceinline__ void split_pair(float p0, float p1, uint32_t& hi, uint32_t& lo) {
-  uint16_t h0 = Elem<T>::from_f32(p0), h1 = Elem<T>::from_f32(p1);
-  float r0 = p0 - Elem<T>::to_f32(h0), r1 = p1 - Elem<T>::to_f32(h1);
-  hi = (uint32_t)h0 | ((uint32_t)h1 << 16);
-  lo = (uint32_t)Elem<T>::from_f32(r0) | ((uint32_t)Elem<T>::from_f32(r1) << 16);
-}
 
 #ifndef PKV_MFMA_WAVES_PER_EU
 #define PKV_MFMA_WAVES_PER_EU 1
@@ -255,6 +213,8 @@ void decode_mfma(DecodeParams p) {
         const int64_t slot = tag >> 2;
         store_nt(p.ws_m + slot * G + lane, so[G * D + lane]);
         store_nt(p.ws_l + slot * G + lane, so[G * D + G + lane]);
+      } else if (kind != 2 && p.lse && lane < G) {
+        store_nt(p.lse + dst / D + lane, so[G * D + lane]);
       }
 #pragma unroll
       for (int k = 0; k < (16 * D / 4) / 64; ++k) {
@@ -389,6 +349,8 @@ void decode_mfma(DecodeParams p) {
         if (!whole && jg == 0) {
           so[G * D + r16] = m_run;
           so[G * D + G + r16] = l_tot;
+        } else if (whole && jg == 0 && p.lse) {
+          so[G * D + r16] = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
         }
       }
       if (lane == 0) {

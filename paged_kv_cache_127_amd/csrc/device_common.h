@@ -148,6 +148,9 @@ struct DecodeParams {
   float* ws_l;         // [slots][G]    partial running sum
   int64_t* prefix;     // [S + 1] exclusive prefix of steps per sequence
   int64_t* wprefix;    // [S + 1] exclusive prefix of schedule weights per sequence
+  // [S][H_q] log2-domain log-sum-exp of each output row, m + log2(l) (-inf for an empty
+  // context), written beside the output when set (matrix-core kernel and merge only)
+  float* lse;
   int out_f32;         // 1: fp32 output, 0: output in the cache's 16-bit type
   int max_blocks;
   int max_context_len;   // lengths are clamped to [0, max_context_len]

@@ -1,0 +1,428 @@
+// Shared-prefix decode: the prefix part.
+//
+// Sequences that begin with the same whole blocks ("PagedAttention: Virtual Memory for the KV
+// Cache", section "Sharing a prefix and copying a partial block": sharers' tables point at the
+// same physical blocks) need those blocks' keys and values only once per step. The softmax state
+// over a token range merges with the state over the rest by the log-sum-exp rule ("Paged
+// Attention and vLLM", section "Paged Attention CUDA Kernel"), so the work splits exactly:
+//   prefix_states: for every KV head g, the S * G query rows of all sharers against the prefix
+//     tokens -- a dense [rows x tokens] attention block on the matrix cores, each key/value
+//     fragment loaded once per wavefront and used by RB row blocks of 16 rows;
+//   the decode kernel over each sequence's own suffix (tables and lengths past the prefix),
+//     writing its normalised output and the row's log-sum-exp;
+//   prefix_combine: per row, the suffix output and the prefix states merged into the result.
+//
+// prefix_states. Rows of KV head g are r = s * G + i (query head g * G + i of sequence s). A
+// workgroup of four wavefronts takes (g, row group of RB * 16 rows, chunk group); wavefront w
+// runs chunk 4 * cg + w, a run of 32-token steps of the prefix. Per step the MFMA operands are
+// laid out as in the decode kernel: key rows tau(a, i) = 8 * (i / 4) + 4a + i % 4 as the A
+// operand, so that the scores S^T[token][row] come out with lane l holding row l % 16 and
+// tokens 8 * (l / 16) + 4a + e -- the B-operand layout of the P.V product; value rows pass
+// through the wavefront's swizzled LDS tile and come back transposed as the A operand of
+// O^T[d][row] += V^T . P^T, with P split into a 16-bit high part and a remainder. At the end the
+// four wavefronts merge their states through LDS (the value tiles, no longer needed) and
+// wavefront 0 writes one state (m, l, acc) per row and chunk group: m in the log2 domain, acc
+// not normalised. The first workgroup also writes the suffix lengths max(L_s - P, 0).
+#include <algorithm>
+
+#include "device_common.h"
+#include "kernels.h"
+#include "mfma_common.h"
+#include "schedule.h"
+
+namespace pkv {
+
+constexpr int kPrefixRB = 4;          // 16-row blocks per wavefront
+constexpr int kPrefixWaves = 4;       // chunks per workgroup
+constexpr int kCombineMaxGroups = 16; // chunk groups the combine kernel folds
+
+template <typename T, int D, int B, int RBK>
+__global__ __launch_bounds__(64 * kPrefixWaves) __attribute__((amdgpu_waves_per_eu(1)))
+void prefix_states(PrefixParams p) {
+  static_assert(B == 16 || B == 32, "block size");
+  constexpr int NC = D / 32;
+  constexpr int NF = D / 16;
+  constexpr int ES = 2;
+  constexpr int ROWB = D * ES;           // bytes per key / value row
+  constexpr int VLPR = D / 8;            // lanes per value row (16 bytes each)
+  constexpr int VTPI = 64 / VLPR;        // value rows per load instruction
+  constexpr int TILE = 32 * ROWB;        // value tile per wavefront
+  static_assert(RBK * NF * 64 * 16 <= kPrefixWaves * TILE, "merge area");
+  __shared__ __attribute__((aligned(16))) char lds[kPrefixWaves * TILE];
+  __shared__ float lds_ml[2][RBK][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uni((int)(threadIdx.x >> 6));
+  const int r16 = lane & 15;
+  const int jg = lane >> 4;
+  const int S = p.num_seqs, Hq = p.num_q_heads, Hkv = p.num_kv_heads;
+  const int G = Hq / Hkv;
+  const int R = S * G;
+  const int P = p.prefix_len;
+  if (blockIdx.x == 0)
+    for (int s = threadIdx.x; s < S; s += blockDim.x) p.suffix_lens[s] = max(p.lens[s] - P, 0);
+
+  const int groups = ceil_div(R, 16 * RBK);
+  const int cgroups = p.chunk_groups;
+  const int cg = blockIdx.x % cgroups;
+  const int rg = (blockIdx.x / cgroups) % groups;
+  const int g = blockIdx.x / (cgroups * groups);   // grid = Hkv * groups * cgroups
+  const int nsteps = ceil_div(P, 32);
+  const int chunk = cg * kPrefixWaves + wave;
+  const int k0 = min(chunk * p.steps_per_chunk, nsteps);
+  const int k1 = min(k0 + p.steps_per_chunk, nsteps);
+  const int nb = P / B;                            // prefix blocks
+
+  const char* kbase = reinterpret_cast<const char*>(p.k_pool);
+  const char* vbase = reinterpret_cast<const char*>(p.v_pool);
+  const size_t tile_stride = (size_t)B * D * ES;   // bytes per (block, head)
+  const int tokA0 = 8 * (r16 >> 2) + (r16 & 3);
+  const int kofs0 = ((tokA0 & (B - 1)) * D + 8 * jg) * ES;
+  const int kofs1 = (((tokA0 + 4) & (B - 1)) * D + 8 * jg) * ES;
+  const int vrow = lane / VLPR;
+  const int vch = lane % VLPR;
+  const int vtok = 8 * jg;
+
+  // query rows of the RB row blocks (padding rows repeat the last row and are never stored)
+  u32x4 q[RBK][NC];
+#pragma unroll
+  for (int rb = 0; rb < RBK; ++rb) {
+    const int r = min((rg * RBK + rb) * 16 + r16, R - 1);
+    const int s = r / G;
+    const int i = r - s * G;
+    const char* qp = reinterpret_cast<const char*>(p.q) +
+                     (((size_t)s * Hq + (size_t)g * G + i) * D + 8 * jg) * ES;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) q[rb][c] = load16(qp + 32 * c * ES);
+  }
+
+  char* vstage = lds + wave * TILE;
+  int vw_ofs[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int t = VTPI * f + vrow;
+    vw_ofs[f] = t * ROWB + (((vch >> 1) ^ piece_swizzle<D>(t)) << 5) + 16 * (vch & 1);
+  }
+  int vr_ofs[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int t = 8 * jg + 4 * hh + (r16 >> 2);
+    vr_ofs[hh] = t * ROWB + (piece_swizzle<D>(t) << 5) + 8 * (r16 & 3);
+  }
+
+  float m_run[RBK], l_run[RBK];
+  f32x4 oacc[RBK][NF];
+#pragma unroll
+  for (int rb = 0; rb < RBK; ++rb) {
+    m_run[rb] = kNegInf;
+    l_run[rb] = 0.f;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) oacc[rb][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bool poison = false;
+
+  // physical blocks of step k (B = 16: two blocks; a second block past the prefix repeats the
+  // first and its slots are masked); out-of-range ids read block 0 and poison the state
+  auto step_blocks = [&](int k, int& b0, int& b1) {
+    const int j0 = B == 16 ? 2 * k : k;
+    b0 = p.prefix_blocks[j0];
+    b1 = (B == 16 && j0 + 1 < nb) ? p.prefix_blocks[j0 + 1] : b0;
+  };
+  u32x4 kr[2][NC], vr[NF];
+  auto load_k = [&](int b0, int b1) {
+    b0 = valid_block(b0, p.num_blocks) ? b0 : 0;
+    b1 = valid_block(b1, p.num_blocks) ? b1 : 0;
+    const char* t0 = kbase + ((size_t)b0 * Hkv + g) * tile_stride;
+    const char* t1 = kbase + ((size_t)b1 * Hkv + g) * tile_stride;
+    const char* ka = ((B == 16 && tokA0 >= 16) ? t1 : t0) + kofs0;
+    const char* kb = ((B == 16 && tokA0 + 4 >= 16) ? t1 : t0) + kofs1;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kr[0][c] = load16(ka + 32 * c * ES);
+      kr[1][c] = load16(kb + 32 * c * ES);
+    }
+  };
+  auto load_v = [&](int b0, int b1) {
+    b0 = valid_block(b0, p.num_blocks) ? b0 : 0;
+    b1 = valid_block(b1, p.num_blocks) ? b1 : 0;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int t = VTPI * f + vrow;
+      const int blk = (B == 16 && t >= 16) ? b1 : b0;
+      vr[f] = load16(vbase + ((size_t)blk * Hkv + g) * tile_stride + (size_t)(t & (B - 1)) * ROWB +
+                     16 * vch);
+    }
+  };
+
+  if (k0 < k1) {
+    int b0, b1;
+    step_blocks(k0, b0, b1);
+    load_k(b0, b1);
+    load_v(b0, b1);
+#pragma unroll 1
+    for (int k = k0; k < k1; ++k) {
+      const int nvalid = min(32, P - 32 * k);
+      poison = poison || !valid_block(b0, p.num_blocks) || !valid_block(b1, p.num_blocks);
+      // next step's blocks (the last step re-reads its own: loads stay unconditional)
+      int n0, n1;
+      step_blocks(min(k + 1, k1 - 1), n0, n1);
+      f32x4 sacc[RBK][2];
+#pragma unroll
+      for (int rb = 0; rb < RBK; ++rb)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          sacc[rb][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < NC; ++c) sacc[rb][a] = mfma16x16x32<T>(kr[a][c], q[rb][c], sacc[rb][a]);
+        }
+      load_k(n0, n1);
+      wave_lds_sync();
+#pragma unroll
+      for (int f = 0; f < NF; ++f) *reinterpret_cast<u32x4*>(vstage + vw_ofs[f]) = vr[f];
+      load_v(n0, n1);
+      wave_lds_sync();
+      u32x4 va[NF];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const uint2 lo = lds_read_tr16(vstage + (vr_ofs[0] ^ (f << 5)));
+        const uint2 hi = lds_read_tr16(vstage + (vr_ofs[1] ^ (f << 5)));
+        va[f] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+      if (nvalid < 32) {
+        const int nv = nvalid - vtok;
+        u32x4 msk;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          msk[u] = (2 * u < nv ? 0xffffu : 0u) | (2 * u + 1 < nv ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) va[f] &= msk;
+      }
+#pragma unroll
+      for (int rb = 0; rb < RBK; ++rb) {
+        float z[8];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int tok = vtok + 4 * a + e;
+            z[4 * a + e] = tok < nvalid ? sacc[rb][a][e] * p.scale_log2 : kNegInf;
+          }
+        float mx = z[0];
+#pragma unroll
+        for (int t = 1; t < 8; ++t) mx = fmaxf(mx, z[t]);
+        mx = cross_max<16>(mx);
+        const float m_new = fmaxf(m_run[rb], mx);
+        const float alpha = fast_exp2(m_run[rb] - m_new);
+        float pr[8];
+        float ps = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          pr[t] = fast_exp2(z[t] - m_new);
+          ps += pr[t];
+        }
+        l_run[rb] = l_run[rb] * alpha + ps;
+        m_run[rb] = m_new;
+        u32x4 phi, plo;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          uint32_t h, l;
+          split_pair<T>(pr[2 * u], pr[2 * u + 1], h, l);
+          phi[u] = h;
+          plo[u] = l;
+        }
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          oacc[rb][f] *= alpha;
+          oacc[rb][f] = mfma16x16x32<T>(va[f], phi, oacc[rb][f]);
+          oacc[rb][f] = mfma16x16x32<T>(va[f], plo, oacc[rb][f]);
+        }
+      }
+      b0 = n0;
+      b1 = n1;
+    }
+  }
+  float l_tot[RBK];
+#pragma unroll
+  for (int rb = 0; rb < RBK; ++rb) {
+    l_tot[rb] = cross_sum<16>(l_run[rb]);
+    if (poison) l_tot[rb] = __builtin_nanf("");
+  }
+
+  // Merge the four wavefronts' states: wavefronts 3, 2, 1 in turn leave theirs in LDS (same
+  // lane -> (row, column) mapping in every wavefront, so each lane reads back its own slots) and
+  // the next lower one folds it in; wavefront 0 ends with the workgroup's state.
+  f32x4* mrg = reinterpret_cast<f32x4*>(lds);
+  __syncthreads();   // every wavefront is done with its value tile
+#pragma unroll 1
+  for (int from = kPrefixWaves - 1; from >= 1; --from) {
+    if (wave == from) {
+#pragma unroll
+      for (int rb = 0; rb < RBK; ++rb) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) mrg[(rb * NF + f) * 64 + lane] = oacc[rb][f];
+        lds_ml[0][rb][lane] = m_run[rb];
+        lds_ml[1][rb][lane] = l_tot[rb];
+      }
+    }
+    __syncthreads();
+    if (wave == from - 1) {
+#pragma unroll
+      for (int rb = 0; rb < RBK; ++rb) {
+        const float mo = lds_ml[0][rb][lane];
+        const float lo = lds_ml[1][rb][lane];
+        const float mn = fmaxf(m_run[rb], mo);
+        const float a_self = mn == kNegInf ? 0.f : fast_exp2(m_run[rb] - mn);
+        const float a_other = mn == kNegInf ? 0.f : fast_exp2(mo - mn);
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          oacc[rb][f] = oacc[rb][f] * a_self + mrg[(rb * NF + f) * 64 + lane] * a_other;
+        l_tot[rb] = l_tot[rb] * a_self + lo * a_other;
+        m_run[rb] = mn;
+      }
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
+
+  // state of chunk group cg: st_m / st_l [cgroups][S * Hq], st_acc [cgroups][S * Hq][D]
+  const size_t SH = (size_t)S * Hq;
+#pragma unroll
+  for (int rb = 0; rb < RBK; ++rb) {
+    const int r = (rg * RBK + rb) * 16 + r16;
+    if (r >= R) continue;
+    const int s = r / G;
+    const int i = r - s * G;
+    const size_t row = (size_t)cg * SH + (size_t)s * Hq + (size_t)g * G + i;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) store_nt(p.st_acc + row * D + 16 * f + 4 * jg, oacc[rb][f]);
+    if (jg == 0) {
+      store_nt(p.st_m + row, m_run[rb]);
+      store_nt(p.st_l + row, l_tot[rb]);
+    }
+  }
+}
+
+// prefix_combine: one wavefront per (sequence, KV head); lane l holds f32x4 chunks l, l + 64, ..
+// of the segment's G rows. Per row, with lse the suffix's log-sum-exp and (m_c, l_c, acc_c) the
+// prefix states: M = max(lse, m_c), o = (o_suffix 2^(lse - M) + sum_c acc_c 2^(m_c - M)) /
+// (2^(lse - M) + sum_c l_c 2^(m_c - M)). The output may alias o_suffix (fp32 output): each lane
+// reads its chunks before writing them.
+template <int D, typename T, int KMAX>
+__global__ __launch_bounds__(256) void prefix_combine(CombineParams p) {
+  const int lane = threadIdx.x & 63;
+  const int seg = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  const int Hkv = p.num_kv_heads;
+  if (seg >= p.num_seqs * Hkv) return;
+  const int s = seg / Hkv;
+  const int g = seg - s * Hkv;
+  const int G = p.num_q_heads / Hkv;
+  const int n4 = G * D / 4;
+  const size_t SH = (size_t)p.num_seqs * p.num_q_heads;
+  const size_t row0 = (size_t)s * p.num_q_heads + (size_t)g * G;
+  const int C = p.chunk_groups;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    const int e4 = lane + 64 * k;
+    if (e4 >= n4) continue;
+    const size_t row = row0 + (size_t)(4 * e4) / D;
+    const size_t off = row0 * D + 4 * (size_t)e4;
+    const float lse = p.lse[row];
+    const f32x4 os = *reinterpret_cast<const f32x4*>(p.o_suffix + off);
+    float M = lse;
+    for (int c = 0; c < C; ++c) M = fmaxf(M, p.st_m[c * SH + row]);
+    f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    if (M != kNegInf) {
+      const float ws = fast_exp2(lse - M);
+      num = os * ws;
+      den = ws;
+      for (int c = 0; c < C; ++c) {
+        const float a = fast_exp2(p.st_m[c * SH + row] - M);
+        num += *reinterpret_cast<const f32x4*>(p.st_acc + (c * SH + row0) * D + 4 * e4) * a;
+        den += p.st_l[c * SH + row] * a;
+      }
+    }
+    const float sc = den == 0.f ? 0.f : 1.0f / den;
+    if (p.out_f32) {
+      store_nt(reinterpret_cast<float*>(p.out) + off, num * sc);
+    } else {
+      const uint32_t w0 = (uint32_t)scaled_to_16<T>(num[0], sc) |
+                          ((uint32_t)scaled_to_16<T>(num[1], sc) << 16);
+      const uint32_t w1 = (uint32_t)scaled_to_16<T>(num[2], sc) |
+                          ((uint32_t)scaled_to_16<T>(num[3], sc) << 16);
+      store_nt(reinterpret_cast<uint16_t*>(p.out) + off, u32x2{w0, w1});
+    }
+  }
+}
+
+void prefix_plan(int num_seqs, int group, int num_kv_heads, int prefix_len, int num_cus,
+                 int* chunk_groups, int* steps_per_chunk) {
+  const int nsteps = (prefix_len + 31) / 32;
+  const int64_t groups = ((int64_t)num_seqs * group + 16 * kPrefixRB - 1) / (16 * kPrefixRB);
+  const int64_t base = (int64_t)num_kv_heads * groups;   // workgroups per chunk group
+  int64_t cg = base > 0 ? (std::max(num_cus, 1) + base - 1) / base : 1;
+  const int64_t cg_max = std::min<int64_t>((nsteps + kPrefixWaves - 1) / kPrefixWaves,
+                                           kCombineMaxGroups);
+  cg = std::max<int64_t>(1, std::min(cg, cg_max));
+  const int chunks = (int)cg * kPrefixWaves;
+  *steps_per_chunk = std::max(1, (nsteps + chunks - 1) / chunks);
+  *chunk_groups = (int)cg;
+}
+
+template <typename T, int D, int B>
+static void launch_prefix_tdb(const PrefixParams& p, hipStream_t st) {
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int64_t groups = ((int64_t)p.num_seqs * G + 16 * kPrefixRB - 1) / (16 * kPrefixRB);
+  const int64_t grid = (int64_t)p.num_kv_heads * groups * p.chunk_groups;
+  hipLaunchKernelGGL((prefix_states<T, D, B, kPrefixRB>), dim3((unsigned)grid),
+                     dim3(64 * kPrefixWaves), 0, st, p);
+}
+
+template <typename T, int D>
+static void launch_prefix_td(const PrefixParams& p, int block_size, hipStream_t st) {
+  if (block_size == 16) launch_prefix_tdb<T, D, 16>(p, st);
+  else launch_prefix_tdb<T, D, 32>(p, st);
+}
+
+hipError_t launch_prefix_states(const PrefixParams& p, int kv_dtype, int head_dim,
+                                int block_size, hipStream_t st) {
+  if (p.num_seqs <= 0) return hipSuccess;
+  if (kv_dtype == 2) {
+    if (head_dim == 128) launch_prefix_td<bf16_t, 128>(p, block_size, st);
+    else launch_prefix_td<bf16_t, 64>(p, block_size, st);
+  } else if (kv_dtype == 1) {
+    if (head_dim == 128) launch_prefix_td<f16_t, 128>(p, block_size, st);
+    else launch_prefix_td<f16_t, 64>(p, block_size, st);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int D, typename T>
+static void launch_combine_t(const CombineParams& p, hipStream_t st) {
+  const int64_t segs = (int64_t)p.num_seqs * p.num_kv_heads;
+  const dim3 grid((unsigned)((segs + 3) / 4)), blk(256);
+  const int chunks = (p.num_q_heads / p.num_kv_heads * D / 4 + 63) / 64;
+  if (chunks <= 1) hipLaunchKernelGGL((prefix_combine<D, T, 1>), grid, blk, 0, st, p);
+  else if (chunks <= 2) hipLaunchKernelGGL((prefix_combine<D, T, 2>), grid, blk, 0, st, p);
+  else if (chunks <= 4) hipLaunchKernelGGL((prefix_combine<D, T, 4>), grid, blk, 0, st, p);
+  else hipLaunchKernelGGL((prefix_combine<D, T, 8>), grid, blk, 0, st, p);
+}
+
+hipError_t launch_prefix_combine(const CombineParams& p, int kv_dtype, int head_dim,
+                                 hipStream_t st) {
+  if (p.num_seqs <= 0) return hipSuccess;
+  if (kv_dtype == 2) {
+    if (head_dim == 128) launch_combine_t<128, bf16_t>(p, st);
+    else launch_combine_t<64, bf16_t>(p, st);
+  } else if (kv_dtype == 1) {
+    if (head_dim == 128) launch_combine_t<128, f16_t>(p, st);
+    else launch_combine_t<64, f16_t>(p, st);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -3,7 +3,8 @@
 // with the log-sum-exp rule of "Paged Attention and vLLM", section "Paged Attention CUDA Kernel":
 //   m* = max_k m_k,  o = sum_k 2^(m_k - m*) acc_k / sum_k 2^(m_k - m*) l_k
 // (m is kept in the log2 domain). Segments of empty sequences get a zero row here; segments
-// that one range finished were written by the decode kernel and are skipped.
+// that one range finished were written by the decode kernel and are skipped. With p.lse set,
+// each merged row's log-sum-exp m* + log2(sum) is written too (-inf for an empty sequence).
 //
 // WPS wavefronts per segment, four wavefronts per workgroup. The slots of a segment follow from
 // the schedule arithmetic alone, range by range, so the WPS wavefronts split the segment's
@@ -97,11 +98,19 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
     }
   };
 
+  // log-sum-exp of row (4 e4) / D, written by the lane holding the row's first chunk
+  auto store_lse = [&](int e4, float m, float den) {
+    if (p.lse && e4 < n4 && (4 * e4) % D == 0)
+      p.lse[base / D + (4 * e4) / D] = den > 0.f ? m + __log2f(den) : kNegInf;
+  };
+
   if (ns == 0) {   // empty sequence: zero rows (and no new row: its length is 0)
     if (wave == 0) {
 #pragma unroll
-      for (int k = 0; k < KMAX; ++k)
+      for (int k = 0; k < KMAX; ++k) {
         if (lane + 64 * k < n4) store(lane + 64 * k, f32x4{0.f, 0.f, 0.f, 0.f}, 1.f);
+        store_lse(lane + 64 * k, kNegInf, 0.f);
+      }
     }
     return;
   }
@@ -182,6 +191,7 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
     for (int k = 0; k < KMAX; ++k) {
       const int e4 = lane + 64 * k;
       if (e4 < n4) store(e4, num[k], den[k] == 0.f ? 0.f : 1.0f / den[k]);
+      store_lse(e4, M[k], den[k]);
     }
   } else {
 #pragma unroll
@@ -209,6 +219,7 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
         }
       }
       if (e4 < n4) store(e4, nm, dn == 0.f ? 0.f : 1.0f / dn);
+      store_lse(e4, Mx, dn);
     }
   }
 }

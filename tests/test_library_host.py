@@ -176,3 +176,27 @@ def test_swap_argument_checks():
         assert call(fn, a2=5) == -2                     # unknown cache dtype
         assert call(fn, a4=0x4008) == -1                # host pool not 16-byte aligned
         assert call(fn, a1=0x2004) == -1
+
+
+def test_shared_prefix_argument_checks():
+    """Host-side rejections of paged_attn_decode_shared_prefix (no kernel launched)."""
+    L = pkv.load_library()
+    base = dict(out=0x1000, out_dtype=0, q=0x1000, k=0x1000, v=0x1000, kv_dtype=2, pre=0x1000,
+                P=32, tables=0x1000, max_blocks=8, lens=0x1000, max_ctx=128, S=2, Hq=16, Hkv=2,
+                d=128, B=16, N=16, scale=0.0, workers=0, ws=None, ws_bytes=0, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.paged_attn_decode_shared_prefix(*a.values())
+
+    assert call(S=0) == 0
+    assert call(pre=None) == -1
+    assert call(kv_dtype=0) == -2                 # fp32 cache
+    assert call(Hq=2) == -2                       # G = 1
+    assert call(P=24) == -1 and call(P=0) == -1 and call(P=144) == -1
+    assert call(d=96) == -2 and call(B=8) == -2
+    assert call() == -3                           # no workspace
+    assert L.pkv_shared_prefix_workspace_size(2, 16, 2, 128, 0, 0) == 0
+    assert L.pkv_shared_prefix_workspace_size(2, 16, 2, 128, 0, 32) > \
+        L.pkv_decode_workspace_size(2, 16, 2, 128, 0)
