@@ -84,51 +84,38 @@ def cpu_baseline(batch, steps: int):
     }
 
 
-def _decode_timing(pkv, torch, launch, launches: int):
-    """(decode us, merge us, append us, copy us, step p50 us) of `launch` (one call sequence)
-    with hipEvents around every launch of each kernel and torch events around every call."""
-    for _ in range(5):
-        launch()
-    torch.cuda.synchronize()
-    pkv.timing_enable(True, every=1)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(launches)]
-    for a, b_ in ev:
-        a.record()
-        launch()
-        b_.record()
-    torch.cuda.synchronize()
-    out = []
-    for name in ("decode_partial", "splitk_reduce", "append", "cow"):
-        ms, n = pkv.timing_query(name)
-        out.append(ms / n * 1e3 if n else 0.0)
-    pkv.timing_enable(False)
-    steps = sorted(a.elapsed_time(b_) * 1e3 for a, b_ in ev)
-    out.append(steps[len(steps) // 2])
-    return out
-
-
 def _kernel_times(pkv, torch, launch, names, launches: int):
-    """({kernel name: mean us}, step p50 us) of `launch`, hipEvents around every launch of each
-    library kernel and torch events around every call."""
+    """({kernel name: mean us}, step p50 us) of `launch` (one call sequence): the step from
+    torch events around every call with the library's own timing off, then the kernels from
+    hipEvents around every launch of each library kernel in a second run."""
     for _ in range(5):
         launch()
     torch.cuda.synchronize()
-    pkv.timing_enable(True, every=1)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(launches)]
     for a, b_ in ev:
         a.record()
         launch()
         b_.record()
+    torch.cuda.synchronize()
+    steps = sorted(a.elapsed_time(b_) * 1e3 for a, b_ in ev)
+    pkv.timing_enable(True, every=1)
+    for _ in range(launches):
+        launch()
     torch.cuda.synchronize()
     out = {}
     for name in names:
         ms, n = pkv.timing_query(name)
         out[name] = ms / n * 1e3 if n else 0.0
     pkv.timing_enable(False)
-    steps = sorted(a.elapsed_time(b_) * 1e3 for a, b_ in ev)
     return out, steps[len(steps) // 2]
+
+
+def _decode_timing(pkv, torch, launch, launches: int):
+    """(decode us, merge us, append us, copy us, step p50 us) of `launch` (see _kernel_times)."""
+    names = ("decode_partial", "splitk_reduce", "append", "cow")
+    kt, step = _kernel_times(pkv, torch, launch, names, launches)
+    return [kt[n] for n in names] + [step]
 
 
 def other_configs(pkv, W, torch, dev: str, workers: int, launches: int = 30):

@@ -189,6 +189,19 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
 
 namespace {
 
+// Shared-prefix mode of the decode: the decode writes normalised fp32 rows to `out` and their
+// log-sum-exp to lse; the merge folds every segment with the prefix states and writes the
+// results to final_out. The caller has validated the device contents.
+struct PrefixFold {
+  float* lse;
+  void* final_out;
+  int final_f32;
+  const float* m;
+  const float* l;
+  const float* acc;
+  int groups;
+};
+
 // Decode (paged_attn_decode), optionally with each sequence's newest token taken from k_new /
 // v_new and stored into its slot by the same kernel (paged_attn_decode_append).
 int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const void* k_pool,
@@ -197,7 +210,7 @@ int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const v
                 const int32_t* context_lens, int max_context_len, int num_seqs,
                 int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
                 float scale, int num_workers, void* workspace, size_t workspace_bytes,
-                void* stream, float* lse = nullptr, bool validate = true) {
+                void* stream, const PrefixFold* pf = nullptr) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
       num_blocks <= 0 || max_context_len < 0)
     return fail(PKV_ERR_INVALID_ARG, "%s: non-positive size", fn);
@@ -265,7 +278,7 @@ int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const v
     return fail(PKV_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
-  if (validate && validate_mode()) {
+  if (!pf && validate_mode()) {
     std::vector<int32_t> lens, tabs;
     if (!copy_ints(lens, context_lens, num_seqs, st) ||
         !copy_ints(tabs, block_tables, (size_t)num_seqs * max_blocks_per_seq, st))
@@ -314,7 +327,17 @@ int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const v
   p.ws_m = reinterpret_cast<float*>(ws + wl.m);
   p.ws_l = reinterpret_cast<float*>(ws + wl.l);
   p.prefix = reinterpret_cast<int64_t*>(ws + wl.prefix);
-  p.lse = lse;
+  p.final_out = out;
+  p.final_f32 = p.out_f32;
+  if (pf) {
+    p.lse = pf->lse;
+    p.final_out = pf->final_out;
+    p.final_f32 = pf->final_f32;
+    p.pst_m = pf->m;
+    p.pst_l = pf->l;
+    p.pst_acc = pf->acc;
+    p.pst_groups = pf->groups;
+  }
 
   hipError_t e;
   if (use_mfma) {
@@ -655,19 +678,15 @@ int paged_attn_decode_shared_prefix(void* out, int out_dtype, const void* q, con
   if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "%s: prefix kernel: %s", fn,
                                    hipGetErrorString(e));
   // the suffix: the same tables past the prefix entries (row stride unchanged), the lengths
-  // the prefix kernel wrote, normalised fp32 rows and their log-sum-exp
+  // the prefix kernel wrote; the merge folds each row's suffix state with its prefix states
+  const PrefixFold pf{lse, out, out_dtype == PKV_F32 ? 1 : 0, st_m, st_l, st_acc,
+                      sl.chunk_groups};
   const int rc = decode_impl(fn, o_suffix, PKV_F32, q, k_pool, v_pool, kv_dtype, nullptr,
                              nullptr, block_tables + nb, max_blocks_per_seq, suffix_lens,
                              max_context_len - prefix_len, num_seqs, num_q_heads, num_kv_heads,
                              head_dim, block_size, num_blocks, scale, n, workspace, sl.decode,
-                             stream, lse, false);
+                             stream, &pf);
   if (rc != PKV_OK) return rc;
-  pkv::CombineParams cp{out, o_suffix, lse, st_m, st_l, st_acc, out_dtype == PKV_F32 ? 1 : 0,
-                        num_seqs, num_q_heads, num_kv_heads, sl.chunk_groups};
-  e = timed("prefix_combine", st,
-            [&] { return pkv::launch_prefix_combine(cp, kv_dtype, head_dim, st); });
-  if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "%s: combine kernel: %s", fn,
-                                   hipGetErrorString(e));
   return ok();
 }
 

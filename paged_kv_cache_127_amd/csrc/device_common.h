@@ -151,6 +151,15 @@ struct DecodeParams {
   // [S][H_q] log2-domain log-sum-exp of each output row, m + log2(l) (-inf for an empty
   // context), written beside the output when set (matrix-core kernel and merge only)
   float* lse;
+  // where the merge writes results: out / out_f32, except in shared-prefix mode (pst_m set),
+  // where out receives the decode's normalised fp32 rows and the merge folds every segment
+  // with the prefix states ([pst_groups][S * H_q] maxima and sums, [..][D] accumulators)
+  void* final_out;
+  int final_f32;
+  const float* pst_m;
+  const float* pst_l;
+  const float* pst_acc;
+  int pst_groups;
   int out_f32;         // 1: fp32 output, 0: output in the cache's 16-bit type
   int max_blocks;
   int max_context_len;   // lengths are clamped to [0, max_context_len]

@@ -49,7 +49,7 @@ hipError_t launch_splitk_reduce(const DecodeParams& p, int kv_dtype, int head_di
                                 hipStream_t st);
 
 // Shared-prefix decode (shared_prefix.hip): states of all sharers' query rows over the
-// prefix, then the merge of those states with the suffix decode's output.
+// prefix (the merge kernel folds them with the suffix decode's results).
 struct PrefixParams {
   const void* q;
   const void* k_pool;
@@ -69,27 +69,12 @@ struct PrefixParams {
   int steps_per_chunk;            // 32-token steps per wavefront
   float scale_log2;
 };
-struct CombineParams {
-  void* out;
-  const float* o_suffix;          // [S][Hq][D] normalised suffix output (may alias out)
-  const float* lse;               // [S][Hq]
-  const float* st_m;
-  const float* st_l;
-  const float* st_acc;
-  int out_f32;
-  int num_seqs;
-  int num_q_heads;
-  int num_kv_heads;
-  int chunk_groups;
-};
 // Chunk groups (workgroups per row group and KV head) and steps per wavefront of the prefix
-// pass: about one workgroup per CU, at most 16 groups, no empty group.
+// pass: about two workgroups per CU, at most 16 groups.
 void prefix_plan(int num_seqs, int group, int num_kv_heads, int prefix_len, int num_cus,
                  int* chunk_groups, int* steps_per_chunk);
 hipError_t launch_prefix_states(const PrefixParams& p, int kv_dtype, int head_dim,
                                 int block_size, hipStream_t st);
-hipError_t launch_prefix_combine(const CombineParams& p, int kv_dtype, int head_dim,
-                                 hipStream_t st);
 
 struct AppendParams {
   void* k_pool;

@@ -9,8 +9,8 @@
 //     tokens -- a dense [rows x tokens] attention block on the matrix cores, each key/value
 //     fragment loaded once per wavefront and used by RB row blocks of 16 rows;
 //   the decode kernel over each sequence's own suffix (tables and lengths past the prefix),
-//     writing its normalised output and the row's log-sum-exp;
-//   prefix_combine: per row, the suffix output and the prefix states merged into the result.
+//     writing normalised rows with their log-sum-exp, or partial states;
+//   the merge kernel, which folds every row's suffix state with its prefix states.
 //
 // prefix_states. Rows of KV head g are r = s * G + i (query head g * G + i of sequence s). A
 // workgroup of four wavefronts takes (g, row group of RB * 16 rows, chunk group); wavefront w
@@ -19,10 +19,11 @@
 // operand, so that the scores S^T[token][row] come out with lane l holding row l % 16 and
 // tokens 8 * (l / 16) + 4a + e -- the B-operand layout of the P.V product; value rows pass
 // through the wavefront's swizzled LDS tile and come back transposed as the A operand of
-// O^T[d][row] += V^T . P^T, with P split into a 16-bit high part and a remainder. At the end the
-// four wavefronts merge their states through LDS (the value tiles, no longer needed) and
-// wavefront 0 writes one state (m, l, acc) per row and chunk group: m in the log2 domain, acc
-// not normalised. The first workgroup also writes the suffix lengths max(L_s - P, 0).
+// O^T[d][row] += V^T . P^T, with P split into a 16-bit high part and a remainder. Block ids are
+// loaded two steps ahead, keys and values one step ahead. At the end the four wavefronts merge
+// their states through LDS (over the value tiles, no longer needed) and wavefront 0 writes one
+// state (m, l, acc) per row and chunk group: m in the log2 domain, acc not normalised. The first
+// workgroup also writes the suffix lengths max(L_s - P, 0).
 #include <algorithm>
 
 #include "device_common.h"
@@ -32,12 +33,13 @@
 
 namespace pkv {
 
-constexpr int kPrefixRB = 4;          // 16-row blocks per wavefront
+constexpr int kPrefixRB = 2;          // 16-row blocks per wavefront
 constexpr int kPrefixWaves = 4;       // chunks per workgroup
-constexpr int kCombineMaxGroups = 16; // chunk groups the combine kernel folds
+constexpr int kPrefixWGsPerCU = 2;    // resident workgroups per CU (two wavefronts per SIMD)
+constexpr int kMaxChunkGroups = 16;   // prefix states per row
 
 template <typename T, int D, int B, int RBK>
-__global__ __launch_bounds__(64 * kPrefixWaves) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(64 * kPrefixWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void prefix_states(PrefixParams p) {
   static_assert(B == 16 || B == 32, "block size");
   constexpr int NC = D / 32;
@@ -47,9 +49,11 @@ void prefix_states(PrefixParams p) {
   constexpr int VLPR = D / 8;            // lanes per value row (16 bytes each)
   constexpr int VTPI = 64 / VLPR;        // value rows per load instruction
   constexpr int TILE = 32 * ROWB;        // value tile per wavefront
-  static_assert(RBK * NF * 64 * 16 <= kPrefixWaves * TILE, "merge area");
-  __shared__ __attribute__((aligned(16))) char lds[kPrefixWaves * TILE];
-  __shared__ float lds_ml[2][RBK][64];
+  // value tiles during the steps; afterwards the states of wavefronts 1..3 for the merge
+  constexpr int STATE = RBK * NF * 64 * 16;
+  constexpr int LDS = kPrefixWaves * TILE > 3 * STATE ? kPrefixWaves * TILE : 3 * STATE;
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  __shared__ float lds_ml[3][2][RBK][64];
 
   const int lane = threadIdx.x & 63;
   const int wave = uni((int)(threadIdx.x >> 6));
@@ -155,17 +159,19 @@ void prefix_states(PrefixParams p) {
   };
 
   if (k0 < k1) {
-    int b0, b1;
+    int b0, b1, n0, n1;
     step_blocks(k0, b0, b1);
     load_k(b0, b1);
     load_v(b0, b1);
+    step_blocks(min(k0 + 1, k1 - 1), n0, n1);
 #pragma unroll 1
     for (int k = k0; k < k1; ++k) {
       const int nvalid = min(32, P - 32 * k);
       poison = poison || !valid_block(b0, p.num_blocks) || !valid_block(b1, p.num_blocks);
-      // next step's blocks (the last step re-reads its own: loads stay unconditional)
-      int n0, n1;
-      step_blocks(min(k + 1, k1 - 1), n0, n1);
+      // block ids two steps ahead, the data one step ahead (past the end: the last step again,
+      // so that every load stays unconditional)
+      int nn0, nn1;
+      step_blocks(min(k + 2, k1 - 1), nn0, nn1);
       f32x4 sacc[RBK][2];
 #pragma unroll
       for (int rb = 0; rb < RBK; ++rb)
@@ -239,6 +245,8 @@ void prefix_states(PrefixParams p) {
       }
       b0 = n0;
       b1 = n1;
+      n0 = nn0;
+      n1 = nn1;
     }
   }
   float l_tot[RBK];
@@ -248,41 +256,40 @@ void prefix_states(PrefixParams p) {
     if (poison) l_tot[rb] = __builtin_nanf("");
   }
 
-  // Merge the four wavefronts' states: wavefronts 3, 2, 1 in turn leave theirs in LDS (same
-  // lane -> (row, column) mapping in every wavefront, so each lane reads back its own slots) and
-  // the next lower one folds it in; wavefront 0 ends with the workgroup's state.
+  // Merge the four wavefronts' states: wavefronts 1..3 leave theirs in LDS (the same lane ->
+  // (row, column) mapping in every wavefront, so wavefront 0's lane reads its own slots), one
+  // barrier, and wavefront 0 folds them into its own.
   f32x4* mrg = reinterpret_cast<f32x4*>(lds);
   __syncthreads();   // every wavefront is done with its value tile
-#pragma unroll 1
-  for (int from = kPrefixWaves - 1; from >= 1; --from) {
-    if (wave == from) {
+  if (wave != 0) {
+    f32x4* dst = mrg + (size_t)(wave - 1) * RBK * NF * 64;
 #pragma unroll
-      for (int rb = 0; rb < RBK; ++rb) {
+    for (int rb = 0; rb < RBK; ++rb) {
 #pragma unroll
-        for (int f = 0; f < NF; ++f) mrg[(rb * NF + f) * 64 + lane] = oacc[rb][f];
-        lds_ml[0][rb][lane] = m_run[rb];
-        lds_ml[1][rb][lane] = l_tot[rb];
-      }
+      for (int f = 0; f < NF; ++f) dst[(rb * NF + f) * 64 + lane] = oacc[rb][f];
+      lds_ml[wave - 1][0][rb][lane] = m_run[rb];
+      lds_ml[wave - 1][1][rb][lane] = l_tot[rb];
     }
-    __syncthreads();
-    if (wave == from - 1) {
-#pragma unroll
-      for (int rb = 0; rb < RBK; ++rb) {
-        const float mo = lds_ml[0][rb][lane];
-        const float lo = lds_ml[1][rb][lane];
-        const float mn = fmaxf(m_run[rb], mo);
-        const float a_self = mn == kNegInf ? 0.f : fast_exp2(m_run[rb] - mn);
-        const float a_other = mn == kNegInf ? 0.f : fast_exp2(mo - mn);
-#pragma unroll
-        for (int f = 0; f < NF; ++f)
-          oacc[rb][f] = oacc[rb][f] * a_self + mrg[(rb * NF + f) * 64 + lane] * a_other;
-        l_tot[rb] = l_tot[rb] * a_self + lo * a_other;
-        m_run[rb] = mn;
-      }
-    }
-    __syncthreads();
   }
+  __syncthreads();
   if (wave != 0) return;
+#pragma unroll 1
+  for (int w = 0; w < kPrefixWaves - 1; ++w) {
+    const f32x4* src = mrg + (size_t)w * RBK * NF * 64;
+#pragma unroll
+    for (int rb = 0; rb < RBK; ++rb) {
+      const float mo = lds_ml[w][0][rb][lane];
+      const float lo = lds_ml[w][1][rb][lane];
+      const float mn = fmaxf(m_run[rb], mo);
+      const float a_self = mn == kNegInf ? 0.f : fast_exp2(m_run[rb] - mn);
+      const float a_other = mn == kNegInf ? 0.f : fast_exp2(mo - mn);
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        oacc[rb][f] = oacc[rb][f] * a_self + src[(rb * NF + f) * 64 + lane] * a_other;
+      l_tot[rb] = l_tot[rb] * a_self + lo * a_other;
+      m_run[rb] = mn;
+    }
+  }
 
   // state of chunk group cg: st_m / st_l [cgroups][S * Hq], st_acc [cgroups][S * Hq][D]
   const size_t SH = (size_t)S * Hq;
@@ -302,67 +309,15 @@ void prefix_states(PrefixParams p) {
   }
 }
 
-// prefix_combine: one wavefront per (sequence, KV head); lane l holds f32x4 chunks l, l + 64, ..
-// of the segment's G rows. Per row, with lse the suffix's log-sum-exp and (m_c, l_c, acc_c) the
-// prefix states: M = max(lse, m_c), o = (o_suffix 2^(lse - M) + sum_c acc_c 2^(m_c - M)) /
-// (2^(lse - M) + sum_c l_c 2^(m_c - M)). The output may alias o_suffix (fp32 output): each lane
-// reads its chunks before writing them.
-template <int D, typename T, int KMAX>
-__global__ __launch_bounds__(256) void prefix_combine(CombineParams p) {
-  const int lane = threadIdx.x & 63;
-  const int seg = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-  const int Hkv = p.num_kv_heads;
-  if (seg >= p.num_seqs * Hkv) return;
-  const int s = seg / Hkv;
-  const int g = seg - s * Hkv;
-  const int G = p.num_q_heads / Hkv;
-  const int n4 = G * D / 4;
-  const size_t SH = (size_t)p.num_seqs * p.num_q_heads;
-  const size_t row0 = (size_t)s * p.num_q_heads + (size_t)g * G;
-  const int C = p.chunk_groups;
-#pragma unroll
-  for (int k = 0; k < KMAX; ++k) {
-    const int e4 = lane + 64 * k;
-    if (e4 >= n4) continue;
-    const size_t row = row0 + (size_t)(4 * e4) / D;
-    const size_t off = row0 * D + 4 * (size_t)e4;
-    const float lse = p.lse[row];
-    const f32x4 os = *reinterpret_cast<const f32x4*>(p.o_suffix + off);
-    float M = lse;
-    for (int c = 0; c < C; ++c) M = fmaxf(M, p.st_m[c * SH + row]);
-    f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    if (M != kNegInf) {
-      const float ws = fast_exp2(lse - M);
-      num = os * ws;
-      den = ws;
-      for (int c = 0; c < C; ++c) {
-        const float a = fast_exp2(p.st_m[c * SH + row] - M);
-        num += *reinterpret_cast<const f32x4*>(p.st_acc + (c * SH + row0) * D + 4 * e4) * a;
-        den += p.st_l[c * SH + row] * a;
-      }
-    }
-    const float sc = den == 0.f ? 0.f : 1.0f / den;
-    if (p.out_f32) {
-      store_nt(reinterpret_cast<float*>(p.out) + off, num * sc);
-    } else {
-      const uint32_t w0 = (uint32_t)scaled_to_16<T>(num[0], sc) |
-                          ((uint32_t)scaled_to_16<T>(num[1], sc) << 16);
-      const uint32_t w1 = (uint32_t)scaled_to_16<T>(num[2], sc) |
-                          ((uint32_t)scaled_to_16<T>(num[3], sc) << 16);
-      store_nt(reinterpret_cast<uint16_t*>(p.out) + off, u32x2{w0, w1});
-    }
-  }
-}
-
 void prefix_plan(int num_seqs, int group, int num_kv_heads, int prefix_len, int num_cus,
                  int* chunk_groups, int* steps_per_chunk) {
   const int nsteps = (prefix_len + 31) / 32;
   const int64_t groups = ((int64_t)num_seqs * group + 16 * kPrefixRB - 1) / (16 * kPrefixRB);
   const int64_t base = (int64_t)num_kv_heads * groups;   // workgroups per chunk group
-  int64_t cg = base > 0 ? (std::max(num_cus, 1) + base - 1) / base : 1;
+  const int64_t target = (int64_t)std::max(num_cus, 1) * kPrefixWGsPerCU;
+  int64_t cg = base > 0 ? (target + base - 1) / base : 1;
   const int64_t cg_max = std::min<int64_t>((nsteps + kPrefixWaves - 1) / kPrefixWaves,
-                                           kCombineMaxGroups);
+                                           kMaxChunkGroups);
   cg = std::max<int64_t>(1, std::min(cg, cg_max));
   const int chunks = (int)cg * kPrefixWaves;
   *steps_per_chunk = std::max(1, (nsteps + chunks - 1) / chunks);
@@ -393,32 +348,6 @@ hipError_t launch_prefix_states(const PrefixParams& p, int kv_dtype, int head_di
   } else if (kv_dtype == 1) {
     if (head_dim == 128) launch_prefix_td<f16_t, 128>(p, block_size, st);
     else launch_prefix_td<f16_t, 64>(p, block_size, st);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <int D, typename T>
-static void launch_combine_t(const CombineParams& p, hipStream_t st) {
-  const int64_t segs = (int64_t)p.num_seqs * p.num_kv_heads;
-  const dim3 grid((unsigned)((segs + 3) / 4)), blk(256);
-  const int chunks = (p.num_q_heads / p.num_kv_heads * D / 4 + 63) / 64;
-  if (chunks <= 1) hipLaunchKernelGGL((prefix_combine<D, T, 1>), grid, blk, 0, st, p);
-  else if (chunks <= 2) hipLaunchKernelGGL((prefix_combine<D, T, 2>), grid, blk, 0, st, p);
-  else if (chunks <= 4) hipLaunchKernelGGL((prefix_combine<D, T, 4>), grid, blk, 0, st, p);
-  else hipLaunchKernelGGL((prefix_combine<D, T, 8>), grid, blk, 0, st, p);
-}
-
-hipError_t launch_prefix_combine(const CombineParams& p, int kv_dtype, int head_dim,
-                                 hipStream_t st) {
-  if (p.num_seqs <= 0) return hipSuccess;
-  if (kv_dtype == 2) {
-    if (head_dim == 128) launch_combine_t<128, bf16_t>(p, st);
-    else launch_combine_t<64, bf16_t>(p, st);
-  } else if (kv_dtype == 1) {
-    if (head_dim == 128) launch_combine_t<128, f16_t>(p, st);
-    else launch_combine_t<64, f16_t>(p, st);
   } else {
     return hipErrorInvalidValue;
   }

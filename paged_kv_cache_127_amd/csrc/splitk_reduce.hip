@@ -5,6 +5,10 @@
 // (m is kept in the log2 domain). Segments of empty sequences get a zero row here; segments
 // that one range finished were written by the decode kernel and are skipped. With p.lse set,
 // each merged row's log-sum-exp m* + log2(sum) is written too (-inf for an empty sequence).
+// Shared-prefix mode (p.pst_m set): every segment ends here. The suffix state -- the merged
+// partials, or the decode's normalised rows with their log-sum-exp for a segment one range
+// finished, or nothing for an empty suffix -- is folded with the rows' prefix states by the
+// same rule, and the result goes to p.final_out.
 //
 // WPS wavefronts per segment, four wavefronts per workgroup. The slots of a segment follow from
 // the schedule arithmetic alone, range by range, so the WPS wavefronts split the segment's
@@ -83,28 +87,74 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
     }
   };
 
-  // o * sc to the output (16-bit: the fp32 value rounded, see scaled_to_16)
+  // o * sc to the result (16-bit: the fp32 value rounded, see scaled_to_16)
   auto store = [&](int e4, f32x4 o, float sc) {
-    if (p.out_f32) {
-      store_nt(reinterpret_cast<float*>(p.out) + base + 4 * e4, o * sc);
+    if (p.final_f32) {
+      store_nt(reinterpret_cast<float*>(p.final_out) + base + 4 * e4, o * sc);
     } else {
       if constexpr (sizeof(T) == 2) {
         const uint32_t w0 = (uint32_t)scaled_to_16<T>(o[0], sc) |
                             ((uint32_t)scaled_to_16<T>(o[1], sc) << 16);
         const uint32_t w1 = (uint32_t)scaled_to_16<T>(o[2], sc) |
                             ((uint32_t)scaled_to_16<T>(o[3], sc) << 16);
-        store_nt(reinterpret_cast<uint16_t*>(p.out) + base + 4 * e4, u32x2{w0, w1});
+        store_nt(reinterpret_cast<uint16_t*>(p.final_out) + base + 4 * e4, u32x2{w0, w1});
       }
     }
   };
 
   // log-sum-exp of row (4 e4) / D, written by the lane holding the row's first chunk
+  const bool prefix_mode = p.pst_m != nullptr;     // uniform
   auto store_lse = [&](int e4, float m, float den) {
-    if (p.lse && e4 < n4 && (4 * e4) % D == 0)
+    if (p.lse && !prefix_mode && e4 < n4 && (4 * e4) % D == 0)
       p.lse[base / D + (4 * e4) / D] = den > 0.f ? m + __log2f(den) : kNegInf;
   };
 
-  if (ns == 0) {   // empty sequence: zero rows (and no new row: its length is 0)
+  // running (max, denominator, numerator) of this lane's chunks; fold(k, m, l, acc) merges one
+  // more state into chunk k's
+  float M[KMAX], den[KMAX];
+  f32x4 num[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    M[k] = kNegInf;
+    den[k] = 0.f;
+    num[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  auto fold = [&](int k, float m, float l, f32x4 a) {
+    const float m_new = fmaxf(M[k], m);
+    if (m_new == kNegInf) return;
+    const float a_old = fast_exp2(M[k] - m_new);
+    const float a_new = fast_exp2(m - m_new);
+    num[k] = num[k] * a_old + a * a_new;
+    den[k] = den[k] * a_old + l * a_new;
+    M[k] = m_new;
+  };
+  // Shared-prefix mode: the states of the rows over the shared prefix, one per chunk group
+  // ([groups][S * Hq] maxima and sums, [groups][S * Hq][D] accumulators).
+  auto fold_prefix = [&]() {
+    const size_t SHn = (size_t)S * p.num_q_heads;
+#pragma unroll 1
+    for (int c = 0; c < p.pst_groups; ++c) {
+      float mc[KMAX], lc[KMAX];
+      f32x4 ac[KMAX];
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) {
+        const int e4 = lane + 64 * k;
+        mc[k] = kNegInf;
+        lc[k] = 0.f;
+        ac[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (e4 < n4) {
+          const size_t row = base / D + (size_t)(4 * e4) / D;
+          mc[k] = p.pst_m[c * SHn + row];
+          lc[k] = p.pst_l[c * SHn + row];
+          ac[k] = *reinterpret_cast<const f32x4*>(p.pst_acc + c * SHn * D + base + 4 * e4);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) fold(k, mc[k], lc[k], ac[k]);
+    }
+  };
+
+  if (ns == 0 && !prefix_mode) {   // empty sequence: zero rows (and no new row: length 0)
     if (wave == 0) {
 #pragma unroll
       for (int k = 0; k < KMAX; ++k) {
@@ -119,11 +169,33 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
   const int64_t seg_w = kStepWeight * ns + line.pw;
   const int64_t ws0 = (int64_t)Hkv * wpre_s + g * seg_w;              // weighted segment start
   const int64_t first = ws0 + line.pw;                                 // weighted start of step 0
-  const int rf = line.owner(first);
-  const int rl = line.owner(first + kStepWeight * (ns - 1));
+  const int rf = ns > 0 ? line.owner(first) : 0;
+  int rl = ns > 0 ? line.owner(first + kStepWeight * (ns - 1)) : -1;   // no slots if empty
   if (rf == rl) {   // one range holds the whole segment: written by the decode kernel
-    append_store();
-    return;
+    if (!prefix_mode) {
+      append_store();
+      return;
+    }
+    // shared-prefix mode: the decode wrote the normalised rows (fp32, to out) and their
+    // log-sum-exp; they are the suffix state (lse, 1, o)
+    if (wave == 0) {
+      float lk[KMAX];
+      f32x4 ok[KMAX];
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) {
+        const int e4 = lane + 64 * k;
+        lk[k] = kNegInf;
+        ok[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (e4 < n4) {
+          lk[k] = p.lse[base / D + (4 * e4) / D];
+          ok[k] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.out) + base +
+                                                  4 * e4);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) fold(k, lk[k], 1.f, ok[k]);
+    }
+    rl = rf - 1;
   }
 
   // Slot of range r's piece of this segment, or -1 if r holds none of its steps. rf's piece is
@@ -137,14 +209,6 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
     return after > before ? 2 * (int64_t)r : -1;
   };
 
-  float M[KMAX], den[KMAX];
-  f32x4 num[KMAX];
-#pragma unroll
-  for (int k = 0; k < KMAX; ++k) {
-    M[k] = kNegInf;
-    den[k] = 0.f;
-    num[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
   const f32x4* acc4 = reinterpret_cast<const f32x4*>(p.ws_acc);
 #pragma unroll 1
   for (int r0 = rf + wave; r0 <= rl; r0 += WPS * kMergeBatch) {
@@ -174,17 +238,10 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j)
 #pragma unroll
-      for (int k = 0; k < KMAX; ++k) {
-        if (slot[j] < 0) continue;
-        const float m_new = fmaxf(M[k], mj[j][k]);
-        if (m_new == kNegInf) continue;
-        const float a_old = fast_exp2(M[k] - m_new);
-        const float a_new = fast_exp2(mj[j][k] - m_new);
-        num[k] = num[k] * a_old + aj[j][k] * a_new;
-        den[k] = den[k] * a_old + lj[j][k] * a_new;
-        M[k] = m_new;
-      }
+      for (int k = 0; k < KMAX; ++k)
+        if (slot[j] >= 0) fold(k, mj[j][k], lj[j][k], aj[j][k]);
   }
+  if (prefix_mode && wave == 0) fold_prefix();
   append_store();
   if constexpr (WPS == 1) {
 #pragma unroll
