@@ -190,39 +190,38 @@ def other_configs(pkv, W, torch, dev: str, workers: int, launches: int = 30):
     res["long8_bf16"]["step_with_table_upload_p50_us"] = round(step_up, 2)
     del t
     # shared prefix: 128 sequences over one 800-token prefix (logical bytes; the prefix blocks
-    # are re-read by every sharer, so caches serve most of them)
-    b = W.config4a()
-    t = stage(b)
-    dus, mus, aus, cus, step = _decode_timing(pkv, torch, lambda: decode_call(t), launches)
-    res["shared_prefix128"] = {
-        "workload": "shared prefix: 128 sequences, 800-token shared prefix + U{1..512} private "
-                    "tokens, 64/8 heads, head_dim 128, bf16, block size 16; decode + merge",
-        "logical_kv_bytes": b.kv_bytes, "decode_us": round(dus, 2), "merge_us": round(mus, 2),
-        "logical_gbs": round(b.kv_bytes / (dus * 1e-6) / 1e9, 1), "cache_assisted": True,
-        "step_p50_us": round(step, 2)}
-    # the same batch through the shared-prefix call: the 50 prefix blocks read once for all
-    # 128 sharers (prefix states), the decode over the suffixes, the per-row merge
-    P = 800
-    S, Hq, d = b.q.shape
-    pre = t["tab"][0, :P // b.block_size].contiguous()
-    ws_sp = pkv.shared_prefix_workspace(S, Hq, b.num_kv_heads, d, P, workers, dev)
+    # are re-read by every sharer, so caches serve most of them), plain decode and the
+    # shared-prefix call; then the same over a 4096-token prefix
+    for P, key in ((800, "shared_prefix128"), (4096, "shared_prefix128_p4096")):
+        b = W.config4a(prefix_len=P)
+        t = stage(b)
+        dus, mus, aus, cus, step = _decode_timing(pkv, torch, lambda: decode_call(t), launches)
+        S, Hq, d = b.q.shape
+        pre = t["tab"][0, :P // b.block_size].contiguous()
+        ws_sp = pkv.shared_prefix_workspace(S, Hq, b.num_kv_heads, d, P, workers, dev)
 
-    def sp_call():
-        pkv.paged_attn_decode_shared_prefix(t["out"], t["q"], t["kp"], t["vp"], pre, P, t["tab"],
-                                            t["lens"], t["mx"], num_workers=workers,
-                                            workspace=ws_sp)
-    kt, sp_step = _kernel_times(pkv, torch, sp_call, ("prefix_states", "decode_partial",
-                                                       "splitk_reduce", "prefix_combine"),
-                                launches)
-    unique = 2 * (P + int(b.lengths.sum()) - S * P) * b.num_kv_heads * d * 2
-    res["shared_prefix128"]["shared_prefix_call"] = {
-        "what": "paged_attn_decode_shared_prefix on the same batch (prefix read once)",
-        "kernel_us": {k: round(v, 2) for k, v in kt.items()},
-        "step_p50_us": round(sp_step, 2), "unique_kv_bytes": unique,
-        "unique_gbs": round(unique / (sp_step * 1e-6) / 1e9, 1),
-        "logical_gbs": round(b.kv_bytes / (sp_step * 1e-6) / 1e9, 1),
-        "speedup_vs_plain_step": round(step / sp_step, 3)}
-    del t, ws_sp
+        def sp_call():
+            pkv.paged_attn_decode_shared_prefix(t["out"], t["q"], t["kp"], t["vp"], pre, P,
+                                                t["tab"], t["lens"], t["mx"],
+                                                num_workers=workers, workspace=ws_sp)
+        kt, sp_step = _kernel_times(pkv, torch, sp_call, ("prefix_states", "decode_partial",
+                                                           "splitk_reduce"), launches)
+        unique = 2 * (P + int(b.lengths.sum()) - S * P) * b.num_kv_heads * d * 2
+        res[key] = {
+            "workload": f"shared prefix: 128 sequences, {P}-token shared prefix + U{{1..512}} "
+                        "private tokens, 64/8 heads, head_dim 128, bf16, block size 16",
+            "logical_kv_bytes": b.kv_bytes, "unique_kv_bytes": unique,
+            "decode_us": round(dus, 2), "merge_us": round(mus, 2),
+            "logical_gbs": round(b.kv_bytes / (dus * 1e-6) / 1e9, 1), "cache_assisted": True,
+            "step_p50_us": round(step, 2),
+            "shared_prefix_call": {
+                "what": "paged_attn_decode_shared_prefix on the same batch: prefix states of "
+                        "all sharers' rows (prefix read once), decode over the suffixes, merge",
+                "kernel_us": {k: round(v, 2) for k, v in kt.items()},
+                "step_p50_us": round(sp_step, 2),
+                "logical_gbs": round(b.kv_bytes / (sp_step * 1e-6) / 1e9, 1),
+                "speedup_vs_plain_step": round(step / sp_step, 3)}}
+        del t, ws_sp
     # copy-on-write pairs: copy 8 slots of each pair's shared partial block, append B's token,
     # decode all 128 sequences (the copy and append rewrite the same slots every call)
     b = W.config4b()

@@ -70,7 +70,7 @@ struct PrefixParams {
   float scale_log2;
 };
 // Chunk groups (workgroups per row group and KV head) and steps per wavefront of the prefix
-// pass: about two workgroups per CU, at most 16 groups.
+// pass: at least one workgroup per CU, at most 16 steps per wavefront and 16 groups.
 void prefix_plan(int num_seqs, int group, int num_kv_heads, int prefix_len, int num_cus,
                  int* chunk_groups, int* steps_per_chunk);
 hipError_t launch_prefix_states(const PrefixParams& p, int kv_dtype, int head_dim,

@@ -35,7 +35,7 @@ namespace pkv {
 
 constexpr int kPrefixRB = 2;          // 16-row blocks per wavefront
 constexpr int kPrefixWaves = 4;       // chunks per workgroup
-constexpr int kPrefixWGsPerCU = 2;    // resident workgroups per CU (two wavefronts per SIMD)
+constexpr int kMaxStepsPerWave = 16;  // 32-token steps of one wavefront (the prefix pass's depth)
 constexpr int kMaxChunkGroups = 16;   // prefix states per row
 
 template <typename T, int D, int B, int RBK>
@@ -127,10 +127,13 @@ void prefix_states(PrefixParams p) {
 
   // physical blocks of step k (B = 16: two blocks; a second block past the prefix repeats the
   // first and its slots are masked); out-of-range ids read block 0 and poison the state
+  // (scalar loads through the constant address space: their wait is not the vector-load
+  // counter that the key/value loads in flight use)
+  const ctable_t pblocks = (ctable_t)p.prefix_blocks;
   auto step_blocks = [&](int k, int& b0, int& b1) {
     const int j0 = B == 16 ? 2 * k : k;
-    b0 = p.prefix_blocks[j0];
-    b1 = (B == 16 && j0 + 1 < nb) ? p.prefix_blocks[j0 + 1] : b0;
+    b0 = pblocks[j0];
+    b1 = (B == 16 && j0 + 1 < nb) ? pblocks[j0 + 1] : b0;
   };
   u32x4 kr[2][NC], vr[NF];
   auto load_k = [&](int b0, int b1) {
@@ -314,11 +317,14 @@ void prefix_plan(int num_seqs, int group, int num_kv_heads, int prefix_len, int 
   const int nsteps = (prefix_len + 31) / 32;
   const int64_t groups = ((int64_t)num_seqs * group + 16 * kPrefixRB - 1) / (16 * kPrefixRB);
   const int64_t base = (int64_t)num_kv_heads * groups;   // workgroups per chunk group
-  const int64_t target = (int64_t)std::max(num_cus, 1) * kPrefixWGsPerCU;
-  int64_t cg = base > 0 ? (target + base - 1) / base : 1;
+  // at least one workgroup per CU, at most kMaxStepsPerWave steps per wavefront, at most
+  // kMaxChunkGroups states per row (each one more state for the merge to read)
+  const int64_t fill = base > 0 ? (std::max(num_cus, 1) + base - 1) / base : 1;
+  const int64_t depth = (nsteps + kPrefixWaves * kMaxStepsPerWave - 1) /
+                        (kPrefixWaves * kMaxStepsPerWave);
   const int64_t cg_max = std::min<int64_t>((nsteps + kPrefixWaves - 1) / kPrefixWaves,
                                            kMaxChunkGroups);
-  cg = std::max<int64_t>(1, std::min(cg, cg_max));
+  const int64_t cg = std::max<int64_t>(1, std::min(std::max(fill, depth), cg_max));
   const int chunks = (int)cg * kPrefixWaves;
   *steps_per_chunk = std::max(1, (nsteps + chunks - 1) / chunks);
   *chunk_groups = (int)cg;
