@@ -19,14 +19,14 @@ Every function here is pinned by ``tests/test_oracle_*.py`` to values the pages 
 closed forms, library routines or brute force, not to itself. No function is "parity
 unpinned".
 """
-from .attention import (attend, contiguous_decode, gather_kv, merge_states,
+from .attention import (attend, contiguous_decode, extend_attention, gather_kv, merge_states,
                         paged_decode, paged_decode_split, partial_state, shared_prefix_decode,
                         token_address)
 from .bookkeeping import (BlockPool, PagedKVModel, RefcountError, PoolExhausted,
                           blocks_for, copy_blocks, capacity_report, reserved_slots, shareable_prefix_blocks)
 
 __all__ = [
-    "attend", "contiguous_decode", "gather_kv", "merge_states",
+    "attend", "contiguous_decode", "extend_attention", "gather_kv", "merge_states",
     "paged_decode", "paged_decode_split", "partial_state", "shared_prefix_decode",
     "token_address", "BlockPool",
     "PagedKVModel", "RefcountError", "PoolExhausted", "blocks_for", "copy_blocks", "capacity_report",

@@ -214,6 +214,43 @@ def shared_prefix_decode(q, k_pool, v_pool, prefix_blocks, prefix_len: int, tabl
     return out
 
 
+def extend_attention(q, query_start, k_pool, v_pool, tables, lengths, block_size: int,
+                     scale=None):
+    """Output ``[T][H_q][d]`` (float64) of several new query tokens per sequence over the paged
+    cache (chunked prefill, or verification of speculated tokens): the pages' case of a request
+    whose cached prefix is reused and only the tokens past it get a fresh prefill pass
+    ("KV Cache Optimization and Management", section "RadixAttention: caching, not just
+    packing, the prefix"; "PagedAttention: Virtual Memory for the KV Cache", section "Sharing a
+    prefix and copying a partial block").
+
+    Reading: sequence s owns query rows ``query_start[s] .. query_start[s+1] - 1`` (n_s rows);
+    their keys and values are already stored, so its cache holds L_s = ``lengths[s]`` tokens,
+    the last n_s of them the new ones. New token t sits at position L_s - n_s + t and attends
+    to positions 0 .. L_s - n_s + t (causal), read through the block table. A row with no
+    position to attend (L_s < n_s - t) gives zeros."""
+    qf = _f64(q)
+    T, Hq, d = qf.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.zeros((T, Hq, d))
+    starts = [int(x) for x in query_start]
+    for s in range(len(starts) - 1):
+        n = starts[s + 1] - starts[s]
+        L = int(lengths[s])
+        for t in range(n):
+            upto = L - n + t + 1                 # positions 0 .. L - n + t
+            if upto <= 0:
+                continue
+            for g in range(Hkv):
+                K, V = gather_kv(k_pool, v_pool, tables[s], upto, g, block_size)
+                for i in range(G):
+                    out[starts[s] + t, g * G + i] = attend(qf[starts[s] + t, g * G + i], K, V,
+                                                            scale)
+    return out
+
+
 def contiguous_decode(q, k_logical, v_logical, scale=None):
     """The same output from the logical (never paged) per-sequence K/V ``[H_kv][L][d]``."""
     qf = _f64(q)

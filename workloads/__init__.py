@@ -29,7 +29,7 @@ import torch
 SEED_BASE = 127000
 
 # stream ids for numpy.random.default_rng([seed, stream])
-_LEN, _PLACE, _Q, _KV, _NEW, _SUFFIX = 0, 1, 2, 3, 4, 5
+_LEN, _PLACE, _Q, _KV, _NEW, _SUFFIX, _EXTQ = 0, 1, 2, 3, 4, 5, 6
 
 _DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -305,6 +305,18 @@ def shared_prefix_batch(suffix_lens, prefix_len: int, num_q_heads: int, num_kv_h
         v_log.append(torch.cat([vp, vs], dim=1))
     return Batch(dtype, B, num_q_heads, Hkv, d, lengths, tables, nblk, q, k_pool, v_pool, k_log,
                  v_log, seed, "shared_prefix")
+
+
+def extend_queries(batch: Batch, new_tokens, seed: int):
+    """Query rows for the last ``new_tokens[s]`` stored tokens of each sequence of ``batch``
+    (their keys and values are already in the cache): ``(q [T][H_q][d], query_start [S + 1])``
+    with T = sum of new_tokens, drawn N(0, 1) and rounded to the batch's dtype."""
+    n = np.asarray(new_tokens, dtype=np.int64)
+    start = np.zeros(len(n) + 1, dtype=np.int32)
+    start[1:] = np.cumsum(n)
+    q = normal(rng_for(seed, _EXTQ), (int(start[-1]), batch.num_q_heads, batch.head_dim),
+               batch.dtype)
+    return q, start
 
 
 def config4a_private(shared: Batch) -> Batch:
