@@ -178,6 +178,39 @@ int paged_attn_decode_shared_prefix(void* out, int out_dtype, const void* q, con
                                     void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Extend (multi-query) attention: several new query tokens per sequence -- a prefill chunk
+ * past a cached prefix, or speculated tokens to verify -- attend causally to the paged cache
+ * ([P3] "RadixAttention: caching, not just packing, the prefix": a request whose prefix is
+ * already cached runs a fresh prefill pass over its new tokens only; [P1] "Sharing a prefix
+ * and copying a partial block"). The new tokens' keys and values are already stored
+ * (kv_cache_append first). Sequence s owns query rows query_start[s] .. query_start[s+1] - 1
+ * (n_s rows); its cache holds context_lens[s] = L_s tokens, the last n_s of them the new ones,
+ * and new token t attends to positions 0 .. L_s - n_s + t:
+ *   out[query_start[s] + t][h] = softmax(q[..][h] . K_s[0 .. L_s - n_s + t]^T * scale) . V_s[..]
+ *   out, q         device [num_query_tokens][num_q_heads][head_dim]; q in kv_dtype, out fp32
+ *                  or kv_dtype
+ *   query_start    device int32 [num_seqs + 1], from 0 to num_query_tokens, nondecreasing
+ *   max_query_len  host: the largest n_s (sizes the launch and the workspace)
+ *   workspace      device, 256-byte aligned, pkv_extend_workspace_size(...) bytes for the same
+ *                  sizes
+ * Other arguments as for paged_attn_decode. 16-bit caches only (PKV_ERR_UNSUPPORTED otherwise).
+ * Each run of 32 query rows (32 / G new tokens of one KV head) reads its keys and values once,
+ * so the call suits short runs (speculative verification, small prefill chunks). Starts outside
+ * [0, num_query_tokens] are clamped (never read outside q or out); PAGEDKV_VALIDATE checks the
+ * starts, n_s <= max_query_len, n_s <= L_s and the table entries.
+ * --------------------------------------------------------------------------------------- */
+size_t pkv_extend_workspace_size(int num_seqs, int num_query_tokens, int num_q_heads,
+                                 int num_kv_heads, int head_dim, int max_query_len,
+                                 int max_context_len);
+int paged_attn_extend(void* out, int out_dtype, const void* q, const int32_t* query_start,
+                      int num_query_tokens, int max_query_len, const void* k_pool,
+                      const void* v_pool, int kv_dtype, const int32_t* block_tables,
+                      int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                      int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Append: store the keys and values of new tokens into their slots
  * ([P1] "Growing a request"; [P2] "KV Cache Fundamentals": the cache grows by one row per
  * head per generated token). For every i < num_tokens and KV head g:

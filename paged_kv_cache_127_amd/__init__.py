@@ -16,7 +16,7 @@ import torch  # loaded first: the library then binds to the HIP runtime torch al
 __all__ = [
     "PagedKVError", "paged_attn_decode", "paged_attn_decode_append", "kv_cache_append",
     "cow_block_copy", "kv_swap_out", "kv_swap_in", "paged_attn_decode_shared_prefix",
-    "shared_prefix_workspace", "pkv_decode_workspace_size", "decode_workspace",
+    "shared_prefix_workspace", "paged_attn_extend", "extend_workspace", "pkv_decode_workspace_size", "decode_workspace",
     "pkv_decode_auto_workers", "BlockPool", "timing_enable", "timing_query",
     "stream_read_probe", "set_validate", "library_path", "load_library", "PKV_F32", "PKV_F16",
     "PKV_BF16",
@@ -70,6 +70,10 @@ def _declare(L):
                                                     c_void, c_int, c_void, c_int, c_void, c_int,
                                                     c_int, c_int, c_int, c_int, c_int, c_int,
                                                     c_float, c_int, c_void, c_size, c_void]),
+        "pkv_extend_workspace_size": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
+        "paged_attn_extend": (c_int, [c_void, c_int, c_void, c_void, c_int, c_int, c_void, c_void,
+                                      c_int, c_void, c_int, c_void, c_int, c_int, c_int, c_int,
+                                      c_int, c_int, c_int, c_float, c_void, c_size, c_void]),
         "kv_swap_out": (c_int, [c_void, c_void, c_int, c_void, c_void, c_int, c_void, c_void,
                                 c_int, c_int, c_int, c_int, c_int, c_void]),
         "kv_swap_in": (c_int, [c_void, c_void, c_int, c_void, c_void, c_int, c_void, c_void,
@@ -235,6 +239,47 @@ def paged_attn_decode_shared_prefix(out: torch.Tensor, q: torch.Tensor, k_pool: 
         int(max_context_len), S, Hq, Hkv, d, B, N, float(scale), int(num_workers),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+    return out
+
+
+def extend_workspace(num_seqs, num_query_tokens, num_q_heads, num_kv_heads, head_dim,
+                     max_query_len, max_context_len, device="cuda") -> torch.Tensor:
+    """Allocate a workspace for paged_attn_extend with these sizes."""
+    n = int(load_library().pkv_extend_workspace_size(num_seqs, num_query_tokens, num_q_heads,
+                                                     num_kv_heads, head_dim, max_query_len,
+                                                     max_context_len))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def paged_attn_extend(out: torch.Tensor, q: torch.Tensor, query_start: torch.Tensor,
+                      max_query_len: int, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor,
+                      max_context_len: int, scale: float = 0.0,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Causal attention of each sequence's new query tokens (rows query_start[s] ..
+    query_start[s+1] - 1 of q, [T][H_q][d]) over its paged cache, whose last n_s tokens are the
+    new ones (C: ``paged_attn_extend``)."""
+    L = load_library()
+    kdt = _kv_dtype(k_pool)
+    if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape or out.shape != q.shape:
+        raise ValueError("bad tensor ranks or out shape; k_pool and v_pool must match")
+    T, Hq, d = q.shape
+    N, Hkv, B, d2 = k_pool.shape
+    S = int(context_lens.shape[0])
+    if d2 != d or tuple(query_start.shape) != (S + 1,) or block_tables.shape[0] != S:
+        raise ValueError("query_start must be [S + 1], block_tables [S][max_blocks]")
+    if out.dtype not in (torch.float32, k_pool.dtype):
+        raise TypeError("out must be float32 or the cache dtype")
+    if workspace is None:
+        workspace = extend_workspace(S, T, Hq, Hkv, d, max_query_len, max_context_len, q.device)
+    _check(L.paged_attn_extend(
+        _dev(out, "out"), _DT[out.dtype], _dev(q, "q", k_pool.dtype),
+        _dev(query_start, "query_start", torch.int32), T, int(max_query_len),
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype), kdt,
+        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+        _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, d, B,
+        N, float(scale), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

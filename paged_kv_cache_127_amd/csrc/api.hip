@@ -557,8 +557,8 @@ SpLayout sp_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim
                    int prefix_len) {
   const int G = num_q_heads / num_kv_heads;
   SpLayout L;
-  pkv::prefix_plan(num_seqs, G, num_kv_heads, prefix_len, cu_count(), &L.chunk_groups,
-                   &L.steps_per_chunk);
+  pkv::row_state_plan((int64_t)num_kv_heads * pkv::row_groups((int64_t)num_seqs * G), prefix_len,
+                      cu_count(), &L.chunk_groups, &L.steps_per_chunk);
   const size_t SH = (size_t)num_seqs * num_q_heads;
   L.decode = ws_layout(num_seqs, G, head_dim, n).total;
   L.suffix_lens = align256(L.decode);
@@ -669,11 +669,27 @@ int paged_attn_decode_shared_prefix(void* out, int out_dtype, const void* q, con
   float* st_l = reinterpret_cast<float*>(ws + sl.l);
   float* st_acc = reinterpret_cast<float*>(ws + sl.acc);
 
-  pkv::PrefixParams pp{q, k_pool, v_pool, prefix_blocks, context_lens, suffix_lens, st_m, st_l,
-                       st_acc, num_seqs, num_q_heads, num_kv_heads, num_blocks, prefix_len,
-                       sl.chunk_groups, sl.steps_per_chunk, sc * 1.4426950408889634f};
+  pkv::RowStateParams pp{};
+  pp.q = q;
+  pp.k_pool = k_pool;
+  pp.v_pool = v_pool;
+  pp.lens = context_lens;
+  pp.prefix_blocks = prefix_blocks;
+  pp.suffix_lens = suffix_lens;
+  pp.prefix_len = prefix_len;
+  pp.st_m = st_m;
+  pp.st_l = st_l;
+  pp.st_acc = st_acc;
+  pp.state_rows = (size_t)num_seqs * num_q_heads;
+  pp.num_seqs = num_seqs;
+  pp.num_q_heads = num_q_heads;
+  pp.num_kv_heads = num_kv_heads;
+  pp.num_blocks = num_blocks;
+  pp.chunk_groups = sl.chunk_groups;
+  pp.steps_per_chunk = sl.steps_per_chunk;
+  pp.scale_log2 = sc * 1.4426950408889634f;
   hipError_t e = timed("prefix_states", st, [&] {
-    return pkv::launch_prefix_states(pp, kv_dtype, head_dim, block_size, st);
+    return pkv::launch_row_states(pp, kv_dtype, head_dim, block_size, st);
   });
   if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "%s: prefix kernel: %s", fn,
                                    hipGetErrorString(e));
@@ -687,6 +703,151 @@ int paged_attn_decode_shared_prefix(void* out, int out_dtype, const void* q, con
                              head_dim, block_size, num_blocks, scale, n, workspace, sl.decode,
                              stream, &pf);
   if (rc != PKV_OK) return rc;
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of paged_attn_extend: the row states of every chunk group.
+struct ExtLayout {
+  size_t m, l, acc, total;
+  int chunk_groups, steps_per_chunk, max_row_groups;
+};
+
+ExtLayout ext_layout(int num_seqs, int num_query_tokens, int num_q_heads, int num_kv_heads,
+                     int head_dim, int max_query_len, int max_context_len) {
+  const int G = num_q_heads / num_kv_heads;
+  ExtLayout L;
+  L.max_row_groups = (int)pkv::row_groups((int64_t)max_query_len * G);
+  pkv::row_state_plan((int64_t)num_seqs * num_kv_heads * L.max_row_groups, max_context_len,
+                      cu_count(), &L.chunk_groups, &L.steps_per_chunk);
+  const size_t rows = (size_t)num_query_tokens * num_q_heads;
+  L.m = 0;
+  L.l = align256((size_t)L.chunk_groups * rows * sizeof(float));
+  L.acc = L.l + align256((size_t)L.chunk_groups * rows * sizeof(float));
+  L.total = L.acc + align256((size_t)L.chunk_groups * rows * head_dim * sizeof(float));
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pkv_extend_workspace_size(int num_seqs, int num_query_tokens, int num_q_heads,
+                                 int num_kv_heads, int head_dim, int max_query_len,
+                                 int max_context_len) {
+  if (num_seqs <= 0 || num_query_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || num_q_heads % num_kv_heads != 0 || max_query_len <= 0 ||
+      max_context_len <= 0)
+    return 0;
+  return ext_layout(num_seqs, num_query_tokens, num_q_heads, num_kv_heads, head_dim,
+                    max_query_len, max_context_len)
+      .total;
+}
+
+int paged_attn_extend(void* out, int out_dtype, const void* q, const int32_t* query_start,
+                      int num_query_tokens, int max_query_len, const void* k_pool,
+                      const void* v_pool, int kv_dtype, const int32_t* block_tables,
+                      int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                      int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  const char* fn = "paged_attn_extend";
+  if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "%s: negative or non-positive size", fn);
+  if (num_seqs == 0 || num_query_tokens == 0) return ok();
+  if (!out || !q || !query_start || !k_pool || !v_pool || !block_tables || !context_lens)
+    return fail(PKV_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (kv_dtype != PKV_F16 && kv_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: kv_dtype %d (fp16 or bf16 caches)", fn, kv_dtype);
+  if (!(out_dtype == PKV_F32 || out_dtype == kv_dtype))
+    return fail(PKV_ERR_UNSUPPORTED, "%s: out_dtype %d with kv_dtype %d", fn, out_dtype,
+                kv_dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128)", fn, head_dim);
+  if (block_size != 16 && block_size != 32)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: block_size %d (16 or 32)", fn, block_size);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "%s: %d query heads not a multiple of %d KV heads", fn,
+                num_q_heads, num_kv_heads);
+  if (max_query_len == 0 || max_query_len > num_query_tokens || max_context_len == 0)
+    return fail(PKV_ERR_INVALID_ARG, "%s: max_query_len %d (1 to %d), max_context_len %d", fn,
+                max_query_len, num_query_tokens, max_context_len);
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PKV_ERR_INVALID_ARG, "%s: max_context_len %d exceeds table capacity %d x %d",
+                fn, max_context_len, max_blocks_per_seq, block_size);
+  const ExtLayout el = ext_layout(num_seqs, num_query_tokens, num_q_heads, num_kv_heads,
+                                  head_dim, max_query_len, max_context_len);
+  if (!workspace || workspace_bytes < el.total)
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", fn,
+                workspace_bytes, el.total);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(PKV_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+  if (validate_mode()) {
+    std::vector<int32_t> qs, lens, tabs;
+    if (!copy_ints(qs, query_start, (size_t)num_seqs + 1, st) ||
+        !copy_ints(lens, context_lens, num_seqs, st) ||
+        !copy_ints(tabs, block_tables, (size_t)num_seqs * max_blocks_per_seq, st))
+      return fail(PKV_ERR_LAUNCH, "%s: validation copy failed", fn);
+    if (qs[0] != 0 || qs[num_seqs] != num_query_tokens)
+      return fail(PKV_ERR_VALIDATION, "query_start must run from 0 to %d", num_query_tokens);
+    for (int s = 0; s < num_seqs; ++s) {
+      const int n = qs[s + 1] - qs[s];
+      if (n < 0 || n > max_query_len)
+        return fail(PKV_ERR_VALIDATION, "sequence %d: %d query tokens (0 to %d)", s, n,
+                    max_query_len);
+      if (lens[s] < n || lens[s] > max_context_len)
+        return fail(PKV_ERR_VALIDATION, "context_lens[%d] = %d outside [%d, %d]", s, lens[s], n,
+                    max_context_len);
+      const int nbs = (lens[s] + block_size - 1) / block_size;
+      for (int j = 0; j < nbs; ++j) {
+        const int b = tabs[(size_t)s * max_blocks_per_seq + j];
+        if (b < 0 || b >= num_blocks)
+          return fail(PKV_ERR_VALIDATION, "block_tables[%d][%d] = %d outside [0, %d)", s, j, b,
+                      num_blocks);
+      }
+    }
+  }
+
+  char* ws = reinterpret_cast<char*>(workspace);
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim);
+  pkv::RowStateParams rp{};
+  rp.q = q;
+  rp.k_pool = k_pool;
+  rp.v_pool = v_pool;
+  rp.lens = context_lens;
+  rp.query_start = query_start;
+  rp.tables = block_tables;
+  rp.max_blocks = max_blocks_per_seq;
+  rp.max_row_groups = el.max_row_groups;
+  rp.num_query_tokens = num_query_tokens;
+  rp.st_m = reinterpret_cast<float*>(ws + el.m);
+  rp.st_l = reinterpret_cast<float*>(ws + el.l);
+  rp.st_acc = reinterpret_cast<float*>(ws + el.acc);
+  rp.state_rows = (size_t)num_query_tokens * num_q_heads;
+  rp.num_seqs = num_seqs;
+  rp.num_q_heads = num_q_heads;
+  rp.num_kv_heads = num_kv_heads;
+  rp.num_blocks = num_blocks;
+  rp.chunk_groups = el.chunk_groups;
+  rp.steps_per_chunk = el.steps_per_chunk;
+  rp.scale_log2 = sc * 1.4426950408889634f;
+  hipError_t e = timed("extend_states", st, [&] {
+    return pkv::launch_row_states(rp, kv_dtype, head_dim, block_size, st);
+  });
+  if (e != hipSuccess)
+    return fail(PKV_ERR_LAUNCH, "%s: states kernel: %s", fn, hipGetErrorString(e));
+  pkv::ExtendFinishParams fp{out, rp.st_m, rp.st_l, rp.st_acc, rp.state_rows, el.chunk_groups,
+                             out_dtype == PKV_F32 ? 1 : 0};
+  e = timed("extend_finish", st,
+            [&] { return pkv::launch_extend_finish(fp, kv_dtype, head_dim, st); });
+  if (e != hipSuccess)
+    return fail(PKV_ERR_LAUNCH, "%s: finish kernel: %s", fn, hipGetErrorString(e));
   return ok();
 }
 

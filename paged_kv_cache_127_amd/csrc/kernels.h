@@ -48,33 +48,56 @@ int decode_valu_resident_waves(int kv_dtype, int head_dim, int block_size, int g
 hipError_t launch_splitk_reduce(const DecodeParams& p, int kv_dtype, int head_dim,
                                 hipStream_t st);
 
-// Shared-prefix decode (shared_prefix.hip): states of all sharers' query rows over the
-// prefix (the merge kernel folds them with the suffix decode's results).
-struct PrefixParams {
+// Softmax states of many query rows over one block list (row_states.hip): the shared-prefix
+// pass (all sharers' rows over the shared blocks; the merge kernel folds them with the suffix
+// decode's results) and extend attention (each sequence's new-token rows over its own blocks,
+// causal; extend_finish folds and normalises).
+struct RowStateParams {
   const void* q;
   const void* k_pool;
   const void* v_pool;
-  const int32_t* prefix_blocks;   // [prefix_len / block_size]
   const int32_t* lens;            // [S] context lengths
+  // prefix mode (query_start null)
+  const int32_t* prefix_blocks;   // [prefix_len / block_size]
   int32_t* suffix_lens;           // [S] out: max(lens - prefix_len, 0)
-  float* st_m;                    // [chunk_groups][S * Hq]
-  float* st_l;                    // [chunk_groups][S * Hq]
-  float* st_acc;                  // [chunk_groups][S * Hq][D]
+  int prefix_len;                 // tokens, a multiple of the block size
+  // extend mode (query_start set)
+  const int32_t* query_start;     // [S + 1] first query row of each sequence
+  const int32_t* tables;          // [S][max_blocks]
+  int max_blocks;
+  int max_row_groups;             // row groups of the longest query run
+  int num_query_tokens;           // T
+  float* st_m;                    // [chunk_groups][state_rows]
+  float* st_l;                    // [chunk_groups][state_rows]
+  float* st_acc;                  // [chunk_groups][state_rows][D]
+  size_t state_rows;              // S * Hq (prefix mode) or T * Hq (extend mode)
   int num_seqs;
   int num_q_heads;
   int num_kv_heads;
   int num_blocks;
-  int prefix_len;                 // tokens, a multiple of the block size
   int chunk_groups;
   int steps_per_chunk;            // 32-token steps per wavefront
   float scale_log2;
 };
-// Chunk groups (workgroups per row group and KV head) and steps per wavefront of the prefix
-// pass: at least one workgroup per CU, at most 16 steps per wavefront and 16 groups.
-void prefix_plan(int num_seqs, int group, int num_kv_heads, int prefix_len, int num_cus,
-                 int* chunk_groups, int* steps_per_chunk);
-hipError_t launch_prefix_states(const PrefixParams& p, int kv_dtype, int head_dim,
-                                int block_size, hipStream_t st);
+struct ExtendFinishParams {
+  void* out;                      // [rows][D], fp32 or the cache's 16-bit type
+  const float* st_m;
+  const float* st_l;
+  const float* st_acc;
+  size_t rows;                    // T * Hq
+  int chunk_groups;
+  int out_f32;
+};
+// Chunk groups and steps per wavefront for `base_workgroups` workgroups per chunk group over
+// up to max_tokens tokens: at least one workgroup per CU, at most 16 steps per wavefront and
+// 16 groups.
+void row_state_plan(int64_t base_workgroups, int max_tokens, int num_cus, int* chunk_groups,
+                    int* steps_per_chunk);
+int64_t row_groups(int64_t rows);   // row groups (of one wavefront's rows) covering `rows`
+hipError_t launch_row_states(const RowStateParams& p, int kv_dtype, int head_dim,
+                             int block_size, hipStream_t st);
+hipError_t launch_extend_finish(const ExtendFinishParams& p, int kv_dtype, int head_dim,
+                                hipStream_t st);
 
 struct AppendParams {
   void* k_pool;

@@ -1,0 +1,481 @@
+// Softmax states of many query rows over the tokens of one block list, on the matrix cores.
+// Two users:
+//
+// Shared-prefix decode. Sequences that begin with the same whole blocks ("PagedAttention:
+// Virtual Memory for the KV Cache", section "Sharing a prefix and copying a partial block":
+// sharers' tables point at the same physical blocks) need those blocks' keys and values only
+// once per step. The softmax state over a token range merges with the state over the rest by
+// the log-sum-exp rule ("Paged Attention and vLLM", section "Paged Attention CUDA Kernel"), so
+// the work splits exactly: the states of the S * G query rows of every KV head over the prefix
+// (here); the decode kernel over each sequence's own suffix, writing normalised rows with their
+// log-sum-exp or partial states; the merge kernel, which folds every row's suffix state with
+// its prefix states.
+//
+// Extend (multi-query) attention. The new tokens of a sequence -- a prefill chunk past a
+// cached prefix, or speculated tokens to verify ("KV Cache Optimization and Management",
+// section "RadixAttention: caching, not just packing, the prefix": only the tokens past the
+// shared part need a fresh prefill pass) -- are already stored; new token t of n attends to
+// positions 0 .. L - n + t of its sequence (causal). Its n * G rows of a KV head attend to the
+// sequence's own blocks with a per-row token limit; extend_finish folds each row's states and
+// normalises.
+//
+// row_states. A workgroup of four wavefronts takes (row group of RB * 16 rows of one KV head,
+// chunk group); wavefront w runs chunk 4 * cg + w, a run of 32-token steps. Per step the MFMA
+// operands are laid out as in the decode kernel: key rows tau(a, i) = 8 * (i / 4) + 4a + i % 4
+// as the A operand, so that the scores S^T[token][row] come out with lane l holding row l % 16
+// and tokens 8 * (l / 16) + 4a + e -- the B-operand layout of the P.V product; value rows pass
+// through the wavefront's swizzled LDS tile and come back transposed as the A operand of
+// O^T[d][row] += V^T . P^T, with P split into a 16-bit high part and a remainder. Each
+// key/value fragment a wavefront loads serves its RB row blocks; two wavefronts per SIMD, so
+// that one computes while the other waits for memory. Block ids are scalar loads two steps
+// ahead, keys and values one step ahead. At the end the four wavefronts merge their states
+// through LDS (over the value tiles, no longer needed) and wavefront 0 writes one state
+// (m, l, acc) per row and chunk group: m in the log2 domain, acc not normalised. In prefix mode
+// the first workgroup also writes the suffix lengths max(L_s - P, 0).
+#include <algorithm>
+
+#include "device_common.h"
+#include "kernels.h"
+#include "mfma_common.h"
+#include "schedule.h"
+
+namespace pkv {
+
+constexpr int kRowsRB = 2;            // 16-row blocks per wavefront
+constexpr int kRowWaves = 4;          // chunks per workgroup
+constexpr int kMaxStepsPerWave = 16;  // 32-token steps of one wavefront
+constexpr int kMaxChunkGroups = 16;   // states per row
+
+template <typename T, int D, int B, int RBK>
+__global__ __launch_bounds__(64 * kRowWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void row_states(RowStateParams p) {
+  static_assert(B == 16 || B == 32, "block size");
+  constexpr int NC = D / 32;
+  constexpr int NF = D / 16;
+  constexpr int ES = 2;
+  constexpr int ROWB = D * ES;           // bytes per key / value row
+  constexpr int VLPR = D / 8;            // lanes per value row (16 bytes each)
+  constexpr int VTPI = 64 / VLPR;        // value rows per load instruction
+  constexpr int TILE = 32 * ROWB;        // value tile per wavefront
+  // value tiles during the steps; afterwards the states of wavefronts 1..3 for the merge
+  constexpr int STATE = RBK * NF * 64 * 16;
+  constexpr int LDS = kRowWaves * TILE > 3 * STATE ? kRowWaves * TILE : 3 * STATE;
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  __shared__ float lds_ml[3][2][RBK][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uni((int)(threadIdx.x >> 6));
+  const int r16 = lane & 15;
+  const int jg = lane >> 4;
+  const int S = p.num_seqs, Hq = p.num_q_heads, Hkv = p.num_kv_heads;
+  const int G = Hq / Hkv;
+  const bool extend = p.query_start != nullptr;   // uniform
+  const int cgroups = p.chunk_groups;
+  const int cg = blockIdx.x % cgroups;
+  int g, rg, R, tok_end, qs = 0, n = 0, L = 0;
+  ctable_t blocks;
+  if (!extend) {
+    // prefix mode: rows r = s * G + i of all S sequences, the shared blocks, P tokens for all
+    const int P = p.prefix_len;
+    if (blockIdx.x == 0)
+      for (int s = threadIdx.x; s < S; s += blockDim.x)
+        p.suffix_lens[s] = max(p.lens[s] - P, 0);
+    R = S * G;
+    const int groups = ceil_div(R, 16 * RBK);
+    rg = (blockIdx.x / cgroups) % groups;
+    g = blockIdx.x / (cgroups * groups);           // grid = Hkv * groups * cgroups
+    tok_end = P;
+    blocks = (ctable_t)p.prefix_blocks;
+  } else {
+    // extend mode: rows r = t * G + i of sequence s's n new tokens, its own blocks, tokens up
+    // to the group's last row's limit (grid = S * Hkv * max_row_groups * cgroups)
+    const int mg = p.max_row_groups;
+    rg = (blockIdx.x / cgroups) % mg;
+    const int sg = blockIdx.x / (cgroups * mg);
+    g = sg % Hkv;
+    const int s = sg / Hkv;
+    // out-of-contract starts are clamped into [0, T]: rows are never read or written outside
+    qs = min(max(p.query_start[s], 0), p.num_query_tokens);
+    n = min(max(p.query_start[s + 1] - qs, 0), p.num_query_tokens - qs);
+    L = clamp_len(p.lens[s], p.max_blocks * B);
+    R = n * G;
+    if (rg * 16 * RBK >= R) return;                // the whole workgroup: no barrier yet
+    const int t_last = (min((rg + 1) * 16 * RBK, R) - 1) / G;
+    tok_end = min(max(L - n + t_last + 1, 0), L);
+    blocks = (ctable_t)p.tables + (size_t)s * p.max_blocks;
+  }
+  const int nsteps = ceil_div(tok_end, 32);
+  const int chunk = cg * kRowWaves + wave;
+  const int k0 = min(chunk * p.steps_per_chunk, nsteps);
+  const int k1 = min(k0 + p.steps_per_chunk, nsteps);
+  const int nb = ceil_div(tok_end, B);             // blocks holding the tokens
+
+  const char* kbase = reinterpret_cast<const char*>(p.k_pool);
+  const char* vbase = reinterpret_cast<const char*>(p.v_pool);
+  const size_t tile_stride = (size_t)B * D * ES;   // bytes per (block, head)
+  const int tokA0 = 8 * (r16 >> 2) + (r16 & 3);
+  const int kofs0 = ((tokA0 & (B - 1)) * D + 8 * jg) * ES;
+  const int kofs1 = (((tokA0 + 4) & (B - 1)) * D + 8 * jg) * ES;
+  const int vrow = lane / VLPR;
+  const int vch = lane % VLPR;
+  const int vtok = 8 * jg;
+
+  // query rows of the RB row blocks (padding rows repeat the last row and are never stored),
+  // each row's output / state index and its token limit
+  u32x4 q[RBK][NC];
+  size_t qrow[RBK];
+  int lim[RBK];
+#pragma unroll
+  for (int rb = 0; rb < RBK; ++rb) {
+    const int r = min((rg * RBK + rb) * 16 + r16, R - 1);
+    const int a = r / G;                           // sequence (prefix) or new token (extend)
+    const int i = r - a * G;
+    qrow[rb] = ((size_t)(extend ? qs + a : a)) * Hq + (size_t)g * G + i;
+    lim[rb] = extend ? min(max(L - n + a + 1, 0), L) : tok_end;
+    const char* qp = reinterpret_cast<const char*>(p.q) + (qrow[rb] * D + 8 * jg) * ES;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) q[rb][c] = load16(qp + 32 * c * ES);
+  }
+
+  char* vstage = lds + wave * TILE;
+  int vw_ofs[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int t = VTPI * f + vrow;
+    vw_ofs[f] = t * ROWB + (((vch >> 1) ^ piece_swizzle<D>(t)) << 5) + 16 * (vch & 1);
+  }
+  int vr_ofs[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int t = 8 * jg + 4 * hh + (r16 >> 2);
+    vr_ofs[hh] = t * ROWB + (piece_swizzle<D>(t) << 5) + 8 * (r16 & 3);
+  }
+
+  float m_run[RBK], l_run[RBK];
+  f32x4 oacc[RBK][NF];
+#pragma unroll
+  for (int rb = 0; rb < RBK; ++rb) {
+    m_run[rb] = kNegInf;
+    l_run[rb] = 0.f;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) oacc[rb][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bool poison = false;
+
+  // physical blocks of step k (B = 16: two blocks; a second block past the prefix repeats the
+  // first and its slots are masked); out-of-range ids read block 0 and poison the state
+  // (scalar loads through the constant address space: their wait is not the vector-load
+  // counter that the key/value loads in flight use)
+  auto step_blocks = [&](int k, int& b0, int& b1) {
+    const int j0 = B == 16 ? 2 * k : k;
+    b0 = blocks[j0];
+    b1 = (B == 16 && j0 + 1 < nb) ? blocks[j0 + 1] : b0;
+  };
+  u32x4 kr[2][NC], vr[NF];
+  auto load_k = [&](int b0, int b1) {
+    b0 = valid_block(b0, p.num_blocks) ? b0 : 0;
+    b1 = valid_block(b1, p.num_blocks) ? b1 : 0;
+    const char* t0 = kbase + ((size_t)b0 * Hkv + g) * tile_stride;
+    const char* t1 = kbase + ((size_t)b1 * Hkv + g) * tile_stride;
+    const char* ka = ((B == 16 && tokA0 >= 16) ? t1 : t0) + kofs0;
+    const char* kb = ((B == 16 && tokA0 + 4 >= 16) ? t1 : t0) + kofs1;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kr[0][c] = load16(ka + 32 * c * ES);
+      kr[1][c] = load16(kb + 32 * c * ES);
+    }
+  };
+  auto load_v = [&](int b0, int b1) {
+    b0 = valid_block(b0, p.num_blocks) ? b0 : 0;
+    b1 = valid_block(b1, p.num_blocks) ? b1 : 0;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int t = VTPI * f + vrow;
+      const int blk = (B == 16 && t >= 16) ? b1 : b0;
+      vr[f] = load16(vbase + ((size_t)blk * Hkv + g) * tile_stride + (size_t)(t & (B - 1)) * ROWB +
+                     16 * vch);
+    }
+  };
+
+  if (k0 < k1) {
+    int b0, b1, n0, n1;
+    step_blocks(k0, b0, b1);
+    load_k(b0, b1);
+    load_v(b0, b1);
+    step_blocks(min(k0 + 1, k1 - 1), n0, n1);
+#pragma unroll 1
+    for (int k = k0; k < k1; ++k) {
+      const int nvalid = min(32, tok_end - 32 * k);
+      poison = poison || !valid_block(b0, p.num_blocks) || !valid_block(b1, p.num_blocks);
+      // block ids two steps ahead, the data one step ahead (past the end: the last step again,
+      // so that every load stays unconditional)
+      int nn0, nn1;
+      step_blocks(min(k + 2, k1 - 1), nn0, nn1);
+      f32x4 sacc[RBK][2];
+#pragma unroll
+      for (int rb = 0; rb < RBK; ++rb)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          sacc[rb][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < NC; ++c) sacc[rb][a] = mfma16x16x32<T>(kr[a][c], q[rb][c], sacc[rb][a]);
+        }
+      load_k(n0, n1);
+      wave_lds_sync();
+#pragma unroll
+      for (int f = 0; f < NF; ++f) *reinterpret_cast<u32x4*>(vstage + vw_ofs[f]) = vr[f];
+      load_v(n0, n1);
+      wave_lds_sync();
+      u32x4 va[NF];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const uint2 lo = lds_read_tr16(vstage + (vr_ofs[0] ^ (f << 5)));
+        const uint2 hi = lds_read_tr16(vstage + (vr_ofs[1] ^ (f << 5)));
+        va[f] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+      if (nvalid < 32) {
+        const int nv = nvalid - vtok;
+        u32x4 msk;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          msk[u] = (2 * u < nv ? 0xffffu : 0u) | (2 * u + 1 < nv ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) va[f] &= msk;
+      }
+#pragma unroll
+      for (int rb = 0; rb < RBK; ++rb) {
+        float z[8];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int tok = vtok + 4 * a + e;
+            z[4 * a + e] = (tok < nvalid && 32 * k + tok < lim[rb]) ? sacc[rb][a][e] * p.scale_log2
+                                                                     : kNegInf;
+          }
+        float mx = z[0];
+#pragma unroll
+        for (int t = 1; t < 8; ++t) mx = fmaxf(mx, z[t]);
+        mx = cross_max<16>(mx);
+        const float m_new = fmaxf(m_run[rb], mx);
+        // a row with nothing to attend yet (causal limit) keeps (-inf, 0, 0): exponents
+        // against 0 instead of -inf, so that no -inf - -inf appears
+        const float m_ref = m_new == kNegInf ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run[rb] - m_ref);
+        float pr[8];
+        float ps = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          pr[t] = fast_exp2(z[t] - m_ref);
+          ps += pr[t];
+        }
+        l_run[rb] = l_run[rb] * alpha + ps;
+        m_run[rb] = m_new;
+        u32x4 phi, plo;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          uint32_t h, l;
+          split_pair<T>(pr[2 * u], pr[2 * u + 1], h, l);
+          phi[u] = h;
+          plo[u] = l;
+        }
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          oacc[rb][f] *= alpha;
+          oacc[rb][f] = mfma16x16x32<T>(va[f], phi, oacc[rb][f]);
+          oacc[rb][f] = mfma16x16x32<T>(va[f], plo, oacc[rb][f]);
+        }
+      }
+      b0 = n0;
+      b1 = n1;
+      n0 = nn0;
+      n1 = nn1;
+    }
+  }
+  float l_tot[RBK];
+#pragma unroll
+  for (int rb = 0; rb < RBK; ++rb) {
+    l_tot[rb] = cross_sum<16>(l_run[rb]);
+    if (poison) l_tot[rb] = __builtin_nanf("");
+  }
+
+  // Merge the four wavefronts' states: wavefronts 1..3 leave theirs in LDS (the same lane ->
+  // (row, column) mapping in every wavefront, so wavefront 0's lane reads its own slots), one
+  // barrier, and wavefront 0 folds them into its own.
+  f32x4* mrg = reinterpret_cast<f32x4*>(lds);
+  __syncthreads();   // every wavefront is done with its value tile
+  if (wave != 0) {
+    f32x4* dst = mrg + (size_t)(wave - 1) * RBK * NF * 64;
+#pragma unroll
+    for (int rb = 0; rb < RBK; ++rb) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f) dst[(rb * NF + f) * 64 + lane] = oacc[rb][f];
+      lds_ml[wave - 1][0][rb][lane] = m_run[rb];
+      lds_ml[wave - 1][1][rb][lane] = l_tot[rb];
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll 1
+  for (int w = 0; w < kRowWaves - 1; ++w) {
+    const f32x4* src = mrg + (size_t)w * RBK * NF * 64;
+#pragma unroll
+    for (int rb = 0; rb < RBK; ++rb) {
+      const float mo = lds_ml[w][0][rb][lane];
+      const float lo = lds_ml[w][1][rb][lane];
+      const float mn = fmaxf(m_run[rb], mo);
+      const float a_self = mn == kNegInf ? 0.f : fast_exp2(m_run[rb] - mn);
+      const float a_other = mn == kNegInf ? 0.f : fast_exp2(mo - mn);
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        oacc[rb][f] = oacc[rb][f] * a_self + src[(rb * NF + f) * 64 + lane] * a_other;
+      l_tot[rb] = l_tot[rb] * a_self + lo * a_other;
+      m_run[rb] = mn;
+    }
+  }
+
+  // state of chunk group cg: st_m / st_l [cgroups][state_rows], st_acc [..][state_rows][D]
+#pragma unroll
+  for (int rb = 0; rb < RBK; ++rb) {
+    const int r = (rg * RBK + rb) * 16 + r16;
+    if (r >= R) continue;
+    const size_t row = (size_t)cg * p.state_rows + qrow[rb];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) store_nt(p.st_acc + row * D + 16 * f + 4 * jg, oacc[rb][f]);
+    if (jg == 0) {
+      store_nt(p.st_m + row, m_run[rb]);
+      store_nt(p.st_l + row, l_tot[rb]);
+    }
+  }
+}
+
+// extend_finish: one thread per f32x4 chunk of the output rows; the row's states of every chunk
+// group fold by the log-sum-exp rule and the sum is normalised. CM >= chunk_groups.
+template <int D, typename T, int CM>
+__global__ __launch_bounds__(256) void extend_finish(ExtendFinishParams p) {
+  constexpr int Q = D / 4;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= p.rows * Q) return;
+  const size_t row = idx / Q;
+  const size_t off = 4 * idx;                    // = row * D + 4 * (idx % Q)
+  float m[CM], l[CM];
+  f32x4 a[CM];
+#pragma unroll
+  for (int c = 0; c < CM; ++c) {
+    if (c < p.chunk_groups) {
+      m[c] = p.st_m[c * p.rows + row];
+      l[c] = p.st_l[c * p.rows + row];
+      a[c] = *reinterpret_cast<const f32x4*>(p.st_acc + c * p.rows * D + off);
+    } else {
+      m[c] = kNegInf;
+      l[c] = 0.f;
+      a[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  float M = kNegInf;
+#pragma unroll
+  for (int c = 0; c < CM; ++c) M = fmaxf(M, m[c]);
+  f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (M != kNegInf) {
+#pragma unroll
+    for (int c = 0; c < CM; ++c) {
+      const float w = fast_exp2(m[c] - M);
+      num += a[c] * w;
+      den += l[c] * w;
+    }
+  }
+  const float sc = den == 0.f ? 0.f : 1.0f / den;
+  if (p.out_f32) {
+    store_nt(reinterpret_cast<float*>(p.out) + off, num * sc);
+  } else {
+    const uint32_t w0 = (uint32_t)scaled_to_16<T>(num[0], sc) |
+                        ((uint32_t)scaled_to_16<T>(num[1], sc) << 16);
+    const uint32_t w1 = (uint32_t)scaled_to_16<T>(num[2], sc) |
+                        ((uint32_t)scaled_to_16<T>(num[3], sc) << 16);
+    store_nt(reinterpret_cast<uint16_t*>(p.out) + off, u32x2{w0, w1});
+  }
+}
+
+void row_state_plan(int64_t base_workgroups, int max_tokens, int num_cus, int* chunk_groups,
+                    int* steps_per_chunk) {
+  const int nsteps = (max_tokens + 31) / 32;
+  // at least one workgroup per CU, at most kMaxStepsPerWave steps per wavefront, at most
+  // kMaxChunkGroups states per row (each one more state for the merge to read)
+  const int64_t base = std::max<int64_t>(base_workgroups, 1);
+  const int64_t fill = (std::max(num_cus, 1) + base - 1) / base;
+  const int64_t depth = (nsteps + kRowWaves * kMaxStepsPerWave - 1) /
+                        (kRowWaves * kMaxStepsPerWave);
+  const int64_t cg_max = std::max<int64_t>(
+      1, std::min<int64_t>((nsteps + kRowWaves - 1) / kRowWaves, kMaxChunkGroups));
+  const int64_t cg = std::max<int64_t>(1, std::min(std::max(fill, depth), cg_max));
+  const int chunks = (int)cg * kRowWaves;
+  *steps_per_chunk = std::max(1, (nsteps + chunks - 1) / chunks);
+  *chunk_groups = (int)cg;
+}
+
+int64_t row_groups(int64_t rows) { return (rows + 16 * kRowsRB - 1) / (16 * kRowsRB); }
+
+template <typename T, int D, int B>
+static void launch_rows_tdb(const RowStateParams& p, int64_t grid, hipStream_t st) {
+  hipLaunchKernelGGL((row_states<T, D, B, kRowsRB>), dim3((unsigned)grid), dim3(64 * kRowWaves),
+                     0, st, p);
+}
+
+template <typename T, int D>
+static void launch_rows_td(const RowStateParams& p, int64_t grid, int block_size,
+                           hipStream_t st) {
+  if (block_size == 16) launch_rows_tdb<T, D, 16>(p, grid, st);
+  else launch_rows_tdb<T, D, 32>(p, grid, st);
+}
+
+hipError_t launch_row_states(const RowStateParams& p, int kv_dtype, int head_dim,
+                             int block_size, hipStream_t st) {
+  if (p.num_seqs <= 0) return hipSuccess;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int64_t grid =
+      p.query_start ? (int64_t)p.num_seqs * p.num_kv_heads * p.max_row_groups * p.chunk_groups
+                    : (int64_t)p.num_kv_heads * row_groups((int64_t)p.num_seqs * G) *
+                          p.chunk_groups;
+  if (grid <= 0) return hipSuccess;
+  if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if (kv_dtype == 2) {
+    if (head_dim == 128) launch_rows_td<bf16_t, 128>(p, grid, block_size, st);
+    else launch_rows_td<bf16_t, 64>(p, grid, block_size, st);
+  } else if (kv_dtype == 1) {
+    if (head_dim == 128) launch_rows_td<f16_t, 128>(p, grid, block_size, st);
+    else launch_rows_td<f16_t, 64>(p, grid, block_size, st);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int D, typename T>
+static void launch_finish_t(const ExtendFinishParams& p, hipStream_t st) {
+  const int64_t chunks = (int64_t)p.rows * (D / 4);
+  const dim3 grid((unsigned)((chunks + 255) / 256)), blk(256);
+  const int C = p.chunk_groups;
+  if (C <= 1) hipLaunchKernelGGL((extend_finish<D, T, 1>), grid, blk, 0, st, p);
+  else if (C <= 2) hipLaunchKernelGGL((extend_finish<D, T, 2>), grid, blk, 0, st, p);
+  else if (C <= 4) hipLaunchKernelGGL((extend_finish<D, T, 4>), grid, blk, 0, st, p);
+  else if (C <= 8) hipLaunchKernelGGL((extend_finish<D, T, 8>), grid, blk, 0, st, p);
+  else hipLaunchKernelGGL((extend_finish<D, T, 16>), grid, blk, 0, st, p);
+}
+
+hipError_t launch_extend_finish(const ExtendFinishParams& p, int kv_dtype, int head_dim,
+                                hipStream_t st) {
+  if (p.rows == 0) return hipSuccess;
+  if (kv_dtype == 2) {
+    if (head_dim == 128) launch_finish_t<128, bf16_t>(p, st);
+    else launch_finish_t<64, bf16_t>(p, st);
+  } else if (kv_dtype == 1) {
+    if (head_dim == 128) launch_finish_t<128, f16_t>(p, st);
+    else launch_finish_t<64, f16_t>(p, st);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -200,3 +200,26 @@ def test_shared_prefix_argument_checks():
     assert L.pkv_shared_prefix_workspace_size(2, 16, 2, 128, 0, 0) == 0
     assert L.pkv_shared_prefix_workspace_size(2, 16, 2, 128, 0, 32) > \
         L.pkv_decode_workspace_size(2, 16, 2, 128, 0)
+
+
+def test_extend_argument_checks():
+    """Host-side rejections of paged_attn_extend (no kernel launched)."""
+    L = pkv.load_library()
+    base = dict(out=0x1000, out_dtype=0, q=0x1000, qs=0x1000, T=8, maxq=4, k=0x1000, v=0x1000,
+                kv_dtype=2, tables=0x1000, max_blocks=8, lens=0x1000, max_ctx=128, S=2, Hq=16,
+                Hkv=2, d=128, B=16, N=16, scale=0.0, ws=None, ws_bytes=0, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.paged_attn_extend(*a.values())
+
+    assert call(S=0) == 0 and call(T=0) == 0
+    assert call(qs=None) == -1
+    assert call(kv_dtype=0) == -2                 # fp32 cache
+    assert call(maxq=0) == -1 and call(maxq=9) == -1
+    assert call(max_ctx=129) == -1                # beyond the table capacity
+    assert call(d=96) == -2 and call(B=8) == -2
+    assert call() == -3                           # no workspace
+    assert L.pkv_extend_workspace_size(2, 8, 16, 2, 128, 4, 128) > 0
+    assert L.pkv_extend_workspace_size(2, 8, 16, 3, 128, 4, 128) == 0
