@@ -369,6 +369,57 @@ def swap_figures(pkv, W, torch, dev: str, preempt: int = 32, launches: int = 10)
     return res
 
 
+def extend_figures(pkv, W, torch, dev: str, launches: int = 20):
+    """Extend (multi-query, causal) attention: (1) speculative verification on the GQA batch --
+    each sequence's last 4 stored tokens are the new ones -- against the plain decode of the
+    same batch; (2) a prefill chunk: 8 sequences of 1024..4096 tokens whose last 256 are new.
+    Kernel durations from hipEvents around every launch, call p50 from torch events."""
+    import numpy as np
+    res = {}
+
+    def run(b, new, seed, key, desc):
+        q, start = W.extend_queries(b, new, seed=seed)
+        qd, sd = q.to(dev), torch.from_numpy(start).to(dev)
+        kp, vp = b.k_pool.to(dev), b.v_pool.to(dev)
+        tab, lens = torch.from_numpy(b.tables).to(dev), torch.from_numpy(b.lengths).to(dev)
+        mx, maxq = int(b.lengths.max()), int(np.max(new))
+        out = torch.empty(qd.shape, dtype=torch.float32, device=dev)
+        ws = pkv.extend_workspace(b.num_seqs, qd.shape[0], b.num_q_heads, b.num_kv_heads,
+                                  b.head_dim, maxq, mx, dev)
+
+        def call():
+            pkv.paged_attn_extend(out, qd, sd, maxq, kp, vp, tab, lens, mx, workspace=ws)
+        kt, step = _kernel_times(pkv, torch, call, ("extend_states", "extend_finish"), launches)
+        # causal work: row (s, t, h) attends L_s - n_s + t + 1 positions
+        att = sum(int(n) * (2 * int(L) - int(n) + 1) // 2 for L, n in zip(b.lengths, new))
+        flops = 4 * att * b.num_q_heads * b.head_dim
+        r = {"workload": desc, "query_tokens": int(np.sum(new)), "kv_bytes": b.kv_bytes,
+             "kernel_us": {k: round(v, 2) for k, v in kt.items()},
+             "step_p50_us": round(step, 2),
+             "kv_gbs": round(b.kv_bytes / (step * 1e-6) / 1e9, 1),
+             "tflops": round(flops / (step * 1e-6) / 1e12, 2)}
+        del kp, vp, out, ws
+        return r
+
+    b = W.config3(16)
+    new = np.minimum(4, b.lengths)
+    res["spec_verify4_gqa256"] = run(b, new, 71, "spec", "speculative verification: the GQA "
+                                     "decode batch (256 sequences, 64/8 heads, d 128, bf16, B "
+                                     "16), the last 4 stored tokens of each sequence as new "
+                                     "query tokens (1,024 rows per KV head)")
+    b = W.small_batch(W.rng_for(W.SEED_BASE + 9, 0).integers(1024, 4096, size=8, endpoint=True),
+                      64, 8, 128, 16, torch.bfloat16, seed=W.SEED_BASE + 9)
+    new = np.full(8, 256)
+    res["prefill_chunk256_x8"] = run(b, new, 72, "prefill", "prefill chunk: 8 sequences of "
+                                     "1024..4096 stored tokens (64/8 heads, d 128, bf16, B 16), "
+                                     "the last 256 of each new (2,048 query tokens)")
+    torch.cuda.empty_cache()
+    for k, v in res.items():
+        print(f"bench: {k} step p50 {v['step_p50_us']} us, {v['tflops']} TFLOP/s",
+              file=sys.stderr, flush=True)
+    return res
+
+
 def stream_probe(pkv, torch, dev: str, gib: int = 2, launches: int = 20):
     """Plain streaming-read bandwidth of this device (the library's probe kernel)."""
     buf = torch.ones((gib << 30) // 4, dtype=torch.float32, device=dev)
@@ -621,6 +672,7 @@ def main():
         result["read_probe"] = probe
         result["other_configs"] = other_configs(pkv, W, torch, dev, args.workers)
         result["swap"] = swap_figures(pkv, W, torch, dev)
+        result["extend"] = extend_figures(pkv, W, torch, dev)
     if not args.no_cpu_baseline:
         print("bench: oracle on one core", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(b, args.cpu_steps)
