@@ -13,7 +13,8 @@ Sources (web pages; cited by title and section):
     per-block partial softmax and its log-sum-exp merge, the copy-on-write rule, block swap of
     a preempted sequence to CPU memory and back.
   * "KV Cache Optimization and Management" -- reference counting, release at count zero,
-    worked capacity examples.
+    worked capacity examples, the prefix index (match, insert, least-recently-used eviction of
+    unreferenced leaves) in ``oracle.prefix_index``.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` to values the pages print,
 closed forms, library routines or brute force, not to itself. No function is "parity
