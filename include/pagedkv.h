@@ -287,6 +287,40 @@ int pkv_pool_decref(pkv_pool* pool, int32_t block, int* freed);  /* -1; *freed =
 int pkv_pool_refcount(const pkv_pool* pool, int32_t block);      /* count, or <0 on error   */
 int pkv_pool_num_free(const pkv_pool* pool);
 
+/* ---------------------------------------------------------------------------------------
+ * Host prefix index over a pkv_pool: a radix tree of cached token sequences whose edges own
+ * runs of whole blocks ([P3] "RadixAttention: caching, not just packing, the prefix": requests
+ * that share a prefix share its path; a new request reuses every matched token's blocks and
+ * prefills only the rest; the least recently used leaves are trimmed first and a branch still
+ * referenced by a running request is never evicted). Sharing is by whole blocks of block_size
+ * tokens. The index holds one pool reference per cached block. No device memory; not
+ * thread-safe; destroy the index before its pool.
+ *
+ * pkv_prefix_index_match: the physical blocks of the longest cached whole-block prefix of
+ *   tokens[0, num_tokens) (at most max_blocks of them) into out_blocks, their count into
+ *   *matched_blocks; each gets one pool reference for the caller, which releases it with the
+ *   sequence (pkv_seq_release / pkv_pool_decref). Marks the matched path as just used.
+ * pkv_prefix_index_insert: cache the whole blocks of a computed sequence; blocks[j] holds its
+ *   tokens [j * block_size, (j + 1) * block_size) and must be live in the pool
+ *   (PKV_ERR_REFCOUNT otherwise, nothing changed). A prefix that is already cached keeps its
+ *   cached block. *inserted_blocks = blocks that became cached (one index reference each).
+ * pkv_prefix_index_evict: free up to max_blocks blocks, one at a time, each the least recently
+ *   used last block of a leaf that only the index references (ties: lower id); their ids go
+ *   to freed_ids (may be NULL) in that order, their count to *freed_blocks.
+ * pkv_prefix_index_size: blocks the index holds.
+ * --------------------------------------------------------------------------------------- */
+typedef struct pkv_prefix_index pkv_prefix_index;
+
+pkv_prefix_index* pkv_prefix_index_create(pkv_pool* pool, int block_size);  /* NULL on error */
+void pkv_prefix_index_destroy(pkv_prefix_index* index);      /* drops the index's references */
+int pkv_prefix_index_match(pkv_prefix_index* index, const int32_t* tokens, int num_tokens,
+                           int32_t* out_blocks, int max_blocks, int* matched_blocks);
+int pkv_prefix_index_insert(pkv_prefix_index* index, const int32_t* tokens, int num_tokens,
+                            const int32_t* blocks, int* inserted_blocks);
+int pkv_prefix_index_evict(pkv_prefix_index* index, int max_blocks, int32_t* freed_ids,
+                           int* freed_blocks);
+int pkv_prefix_index_size(const pkv_prefix_index* index);
+
 /* Table helpers on one host table row (int32 [max_blocks]) of a sequence that currently
  * holds `length` tokens.
  *

@@ -19,7 +19,7 @@ __all__ = [
     "shared_prefix_workspace", "paged_attn_extend", "extend_workspace", "pkv_decode_workspace_size", "decode_workspace",
     "pkv_decode_auto_workers", "BlockPool", "timing_enable", "timing_query",
     "stream_read_probe", "set_validate", "library_path", "load_library", "PKV_F32", "PKV_F16",
-    "PKV_BF16",
+    "PKV_BF16", "PrefixIndex",
 ]
 
 PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
@@ -78,6 +78,12 @@ def _declare(L):
                                 c_int, c_int, c_int, c_int, c_int, c_void]),
         "kv_swap_in": (c_int, [c_void, c_void, c_int, c_void, c_void, c_int, c_void, c_void,
                                c_int, c_int, c_int, c_int, c_int, c_void]),
+        "pkv_prefix_index_create": (c_void, [c_void, c_int]),
+        "pkv_prefix_index_destroy": (None, [c_void]),
+        "pkv_prefix_index_match": (c_int, [c_void, i32p, c_int, i32p, c_int, P(c_int)]),
+        "pkv_prefix_index_insert": (c_int, [c_void, i32p, c_int, i32p, P(c_int)]),
+        "pkv_prefix_index_evict": (c_int, [c_void, c_int, i32p, P(c_int)]),
+        "pkv_prefix_index_size": (c_int, [c_void]),
         "pkv_pool_create": (c_void, [c_int]),
         "pkv_pool_destroy": (None, [c_void]),
         "pkv_pool_alloc": (c_int, [c_void, i32p]),
@@ -497,3 +503,54 @@ class BlockPool:
         if rc < 0:
             raise PagedKVError(rc, "pkv_seq_release")
         return rc
+
+
+class PrefixIndex:
+    """Host prefix index over a BlockPool (C: ``pkv_prefix_index_*``): match the longest cached
+    whole-block prefix of a token sequence, insert a computed sequence's blocks, evict least
+    recently used unreferenced leaves."""
+
+    def __init__(self, pool: "BlockPool", block_size: int):
+        L = load_library()
+        self._L = L
+        self._pool = pool                     # kept alive: the index holds pool references
+        self._x = L.pkv_prefix_index_create(pool._p, int(block_size))
+        if not self._x:
+            raise PagedKVError(-1, "pkv_prefix_index_create failed")
+        self.block_size = int(block_size)
+
+    def __del__(self):
+        x = getattr(self, "_x", None)
+        if x:
+            self._L.pkv_prefix_index_destroy(x)
+            self._x = None
+
+    @staticmethod
+    def _ints(values):
+        import numpy as np
+        a = np.ascontiguousarray(values, dtype=np.int32)
+        return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+    def match(self, tokens) -> list:
+        t, tp = self._ints(tokens)
+        cap = max(1, len(t) // self.block_size)
+        out, op = self._ints([0] * cap)
+        n = ctypes.c_int()
+        _check(self._L.pkv_prefix_index_match(self._x, tp, len(t), op, cap, ctypes.byref(n)))
+        return out[:n.value].tolist()
+
+    def insert(self, tokens, blocks) -> int:
+        t, tp = self._ints(tokens)
+        b, bp = self._ints(blocks if len(blocks) else [0])
+        n = ctypes.c_int()
+        _check(self._L.pkv_prefix_index_insert(self._x, tp, len(t), bp, ctypes.byref(n)))
+        return n.value
+
+    def evict(self, max_blocks: int) -> list:
+        out, op = self._ints([0] * max(1, int(max_blocks)))
+        n = ctypes.c_int()
+        _check(self._L.pkv_prefix_index_evict(self._x, int(max_blocks), op, ctypes.byref(n)))
+        return out[:n.value].tolist()
+
+    def size(self) -> int:
+        return int(self._L.pkv_prefix_index_size(self._x))

@@ -31,7 +31,7 @@ CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-I", INCLUDE]
 
 HIP_SOURCES = ["api.hip", "decode_mfma.hip", "decode_valu.hip", "splitk_reduce.hip",
                "append_cow.hip", "swap.hip", "row_states.hip", "probe.hip"]
-CXX_SOURCES = ["pool.cpp"]
+CXX_SOURCES = ["pool.cpp", "prefix_index.cpp"]
 
 
 def _run(cmd):
