@@ -46,6 +46,22 @@ constexpr int kRowWaves = 4;          // chunks per workgroup
 constexpr int kMaxStepsPerWave = 16;  // 32-token steps of one wavefront
 constexpr int kMaxChunkGroups = 16;   // states per row
 
+// Two fp32 probabilities (in [0, 1]) as packed 16-bit high parts and remainders. bf16: the high
+// part is the fp32 value truncated to its upper half (one AND), so the remainder p - hi is exact
+// and is rounded once; |hi + lo - p| <= 2^-17 p. fp16 keeps the rounding split.
+template <typename T>
+__device__ __forceinline__ void split_hi_lo(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  if constexpr (__is_same(T, bf16_t)) {
+    const uint32_t u0 = __float_as_uint(p0) & 0xffff0000u;
+    const uint32_t u1 = __float_as_uint(p1) & 0xffff0000u;
+    hi = (u0 >> 16) | u1;
+    lo = (uint32_t)Elem<T>::from_f32(p0 - __uint_as_float(u0)) |
+         ((uint32_t)Elem<T>::from_f32(p1 - __uint_as_float(u1)) << 16);
+  } else {
+    split_pair<T>(p0, p1, hi, lo);
+  }
+}
+
 template <typename T, int D, int B, int RBK>
 __global__ __launch_bounds__(64 * kRowWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void row_states(RowStateParams p) {
@@ -151,6 +167,12 @@ void row_states(RowStateParams p) {
     vr_ofs[hh] = t * ROWB + (piece_swizzle<D>(t) << 5) + 8 * (r16 & 3);
   }
 
+  // the smallest token limit of the wavefront's rows: steps below it need no masking
+  int lim_min = lim[0];
+#pragma unroll
+  for (int rb = 1; rb < RBK; ++rb) lim_min = min(lim_min, lim[rb]);
+  lim_min = uni((int)-cross_max<1>(-(float)lim_min));
+
   float m_run[RBK], l_run[RBK];
   f32x4 oacc[RBK][NF];
 #pragma unroll
@@ -245,14 +267,22 @@ void row_states(RowStateParams p) {
 #pragma unroll
       for (int rb = 0; rb < RBK; ++rb) {
         float z[8];
+        if (32 * k + 32 <= lim_min) {   // every token of the step counts for every row
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+          for (int a = 0; a < 2; ++a)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int tok = vtok + 4 * a + e;
-            z[4 * a + e] = (tok < nvalid && 32 * k + tok < lim[rb]) ? sacc[rb][a][e] * p.scale_log2
-                                                                     : kNegInf;
-          }
+            for (int e = 0; e < 4; ++e) z[4 * a + e] = sacc[rb][a][e] * p.scale_log2;
+        } else {
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int tok = vtok + 4 * a + e;
+              z[4 * a + e] = (tok < nvalid && 32 * k + tok < lim[rb])
+                                 ? sacc[rb][a][e] * p.scale_log2
+                                 : kNegInf;
+            }
+        }
         float mx = z[0];
 #pragma unroll
         for (int t = 1; t < 8; ++t) mx = fmaxf(mx, z[t]);
@@ -270,18 +300,24 @@ void row_states(RowStateParams p) {
           ps += pr[t];
         }
         l_run[rb] = l_run[rb] * alpha + ps;
+        // the accumulators need rescaling only when some row's maximum moved (alpha is then
+        // exactly 1 everywhere else, and most steps move no maximum)
+        const bool moved = __builtin_amdgcn_ballot_w64(m_new != m_run[rb]) != 0;
         m_run[rb] = m_new;
         u32x4 phi, plo;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           uint32_t h, l;
-          split_pair<T>(pr[2 * u], pr[2 * u + 1], h, l);
+          split_hi_lo<T>(pr[2 * u], pr[2 * u + 1], h, l);
           phi[u] = h;
           plo[u] = l;
         }
+        if (moved) {
+#pragma unroll
+          for (int f = 0; f < NF; ++f) oacc[rb][f] *= alpha;
+        }
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-          oacc[rb][f] *= alpha;
           oacc[rb][f] = mfma16x16x32<T>(va[f], phi, oacc[rb][f]);
           oacc[rb][f] = mfma16x16x32<T>(va[f], plo, oacc[rb][f]);
         }

@@ -129,28 +129,34 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
     M[k] = m_new;
   };
   // Shared-prefix mode: the states of the rows over the shared prefix, one per chunk group
-  // ([groups][S * Hq] maxima and sums, [groups][S * Hq][D] accumulators).
+  // ([groups][S * Hq] maxima and sums, [groups][S * Hq][D] accumulators). Wavefront 0 loads
+  // group c's into registers; group 0's are requested right here, before the schedule work,
+  // so that their latency overlaps it.
+  const size_t SHn = (size_t)S * p.num_q_heads;
+  float pm[KMAX], pl[KMAX];
+  f32x4 pa[KMAX];
+  auto load_prefix = [&](int c) {
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const int e4 = lane + 64 * k;
+      pm[k] = kNegInf;
+      pl[k] = 0.f;
+      pa[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (e4 < n4) {
+        const size_t row = base / D + (size_t)(4 * e4) / D;
+        pm[k] = p.pst_m[c * SHn + row];
+        pl[k] = p.pst_l[c * SHn + row];
+        pa[k] = *reinterpret_cast<const f32x4*>(p.pst_acc + c * SHn * D + base + 4 * e4);
+      }
+    }
+  };
+  if (prefix_mode && wave == 0) load_prefix(0);
   auto fold_prefix = [&]() {
-    const size_t SHn = (size_t)S * p.num_q_heads;
 #pragma unroll 1
     for (int c = 0; c < p.pst_groups; ++c) {
-      float mc[KMAX], lc[KMAX];
-      f32x4 ac[KMAX];
+      if (c > 0) load_prefix(c);
 #pragma unroll
-      for (int k = 0; k < KMAX; ++k) {
-        const int e4 = lane + 64 * k;
-        mc[k] = kNegInf;
-        lc[k] = 0.f;
-        ac[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (e4 < n4) {
-          const size_t row = base / D + (size_t)(4 * e4) / D;
-          mc[k] = p.pst_m[c * SHn + row];
-          lc[k] = p.pst_l[c * SHn + row];
-          ac[k] = *reinterpret_cast<const f32x4*>(p.pst_acc + c * SHn * D + base + 4 * e4);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < KMAX; ++k) fold(k, mc[k], lc[k], ac[k]);
+      for (int k = 0; k < KMAX; ++k) fold(k, pm[k], pl[k], pa[k]);
     }
   };
 
