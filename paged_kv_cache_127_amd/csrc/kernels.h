@@ -76,7 +76,8 @@ struct RowStateParams {
   int num_kv_heads;
   int num_blocks;
   int chunk_groups;
-  int steps_per_chunk;            // 32-token steps per wavefront
+  int steps_per_chunk;            // planned 32-token steps per wavefront (the kernel splits each
+                                  // row group's own steps evenly)
   float scale_log2;
 };
 struct ExtendFinishParams {

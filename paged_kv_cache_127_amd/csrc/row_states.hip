@@ -120,10 +120,13 @@ void row_states(RowStateParams p) {
     tok_end = min(max(L - n + t_last + 1, 0), L);
     blocks = (ctable_t)p.tables + (size_t)s * p.max_blocks;
   }
+  // this row group's steps, split evenly over the chunk groups' wavefronts (a short sequence
+  // gets short chunks rather than idle wavefronts)
   const int nsteps = ceil_div(tok_end, 32);
   const int chunk = cg * kRowWaves + wave;
-  const int k0 = min(chunk * p.steps_per_chunk, nsteps);
-  const int k1 = min(k0 + p.steps_per_chunk, nsteps);
+  const int spc = ceil_div(nsteps, cgroups * kRowWaves);
+  const int k0 = min(chunk * spc, nsteps);
+  const int k1 = min(k0 + spc, nsteps);
   const int nb = ceil_div(tok_end, B);             // blocks holding the tokens
 
   const char* kbase = reinterpret_cast<const char*>(p.k_pool);
