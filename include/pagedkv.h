@@ -4,7 +4,10 @@
  * Single-query decode attention over a KV cache that lives in fixed-size physical blocks and
  * is addressed through a per-sequence block table, plus the two calls that mutate the cache
  * (append of new tokens, copy-on-write of a shared block) and a host-side refcounted block
- * pool.
+ * pool. Around that path: decode of sequences that share a prefix (the shared blocks read once
+ * for all sharers), extend attention (several new query tokens per sequence, causal), block
+ * swap between the pools and pinned host memory, and a host prefix index (radix tree with
+ * least-recently-used eviction) over the block pool.
  *
  * Sources, cited by page title and section:
  *   [P1] "PagedAttention: Virtual Memory for the KV Cache"
