@@ -141,3 +141,46 @@ def test_rejections_and_validation():
         pkv.set_validate(False)
     ref = oracle.extend_attention(q, start, b.k_pool, b.v_pool, b.tables, b.lengths, 16)
     assert float(np.abs(out.cpu().double().numpy() - ref).max()) <= 2e-3
+
+
+def test_shared_prefix_and_extend_replay_in_a_hip_graph():
+    """Both calls allocate nothing, launch only on the caller's stream and record no memset:
+    captured together in a HIP graph, three replays (with eager work and synchronisations
+    between them) reproduce the eager results bit for bit."""
+    b = W.shared_prefix_batch([9, 120, 3, 300], 96, 16, 2, 128, 16, torch.bfloat16, seed=81,
+                              poison=True)
+    db = DeviceBatch(b)
+    q, start = W.extend_queries(b, [5, 9, 3, 12], seed=82)
+    qd, sd = q.cuda(), torch.from_numpy(start).cuda()
+    pre = db.tables[0, :6].contiguous()
+    out_sp = torch.empty(db.q.shape, dtype=torch.float32, device="cuda")
+    out_ex = torch.empty(qd.shape, dtype=torch.bfloat16, device="cuda")
+    ws_sp = pkv.shared_prefix_workspace(b.num_seqs, 16, 2, 128, 96)
+    ws_ex = pkv.extend_workspace(b.num_seqs, qd.shape[0], 16, 2, 128, 12, db.max_ctx)
+
+    def step():
+        pkv.paged_attn_decode_shared_prefix(out_sp, db.q, db.k_pool, db.v_pool, pre, 96,
+                                            db.tables, db.lens, db.max_ctx, workspace=ws_sp)
+        pkv.paged_attn_extend(out_ex, qd, sd, 12, db.k_pool, db.v_pool, db.tables, db.lens,
+                              db.max_ctx, workspace=ws_ex)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref_sp, ref_ex = out_sp.clone(), out_ex.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        out_sp.fill_(float("nan"))
+        out_ex.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(out_sp.cpu()), bits(ref_sp.cpu()))
+        assert torch.equal(bits(out_ex.cpu()), bits(ref_ex.cpu()))
+    assert max_err(ref_sp.cpu(), oracle.shared_prefix_decode(
+        b.q, b.k_pool, b.v_pool, b.tables[0][:6], 96, b.tables, b.lengths, 16)) <= 2e-3
