@@ -456,6 +456,28 @@ def prefix_index_figures(pkv, requests: int = 500):
             "host_us_per_request_match_and_insert": round(us, 2)}
 
 
+def mfma_probe(pkv, torch, dev: str, iters: int = 2000, launches: int = 5):
+    """What 16x16x32 bf16 MFMAs sustain here (the library's probe), with one and with two
+    wavefronts per SIMD (1 and 2 workgroups of 4 wavefronts per CU)."""
+    props = torch.cuda.get_device_properties(dev)
+    cus = props.multi_processor_count
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    res = {}
+    for per_cu in (1, 2):
+        wgs = cus * per_cu
+        pkv.mfma_rate_probe(wgs, 10, sink)
+        torch.cuda.synchronize()
+        pkv.timing_enable(True, every=1)
+        for _ in range(launches):
+            pkv.mfma_rate_probe(wgs, iters, sink)
+        torch.cuda.synchronize()
+        ms, n = pkv.timing_query("mfma_rate")
+        pkv.timing_enable(False)
+        flops = wgs * 4 * iters * 8 * 16384
+        res[f"waves_per_simd_{per_cu}_tflops"] = round(flops / (ms / n * 1e-3) / 1e12, 1)
+    return res
+
+
 def stream_probe(pkv, torch, dev: str, gib: int = 2, launches: int = 20):
     """Plain streaming-read bandwidth of this device (the library's probe kernel)."""
     buf = torch.ones((gib << 30) // 4, dtype=torch.float32, device=dev)
@@ -706,6 +728,7 @@ def main():
         probe = stream_probe(pkv, torch, dev)
         probe["decode_frac_of_probe"] = round(achieved / probe["gbs"], 4)
         result["read_probe"] = probe
+        result["mfma_probe"] = mfma_probe(pkv, torch, dev)
         result["other_configs"] = other_configs(pkv, W, torch, dev, args.workers)
         result["swap"] = swap_figures(pkv, W, torch, dev)
         result["extend"] = extend_figures(pkv, W, torch, dev)

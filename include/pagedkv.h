@@ -365,6 +365,14 @@ int pkv_timing_query(const char* name, double* total_ms, int64_t* launches);
  * PKV_ERR_INVALID_ARG for null pointers, misalignment or a bad size. */
 int pkv_stream_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
+/* Matrix-core probe (measurement only): `workgroups` workgroups of 4 wavefronts, each issuing
+ * `iters` rounds of 8 independent 16x16x32 bf16 MFMAs (16,384 flops each, no memory traffic),
+ * so that a benchmark can compare MFMA-bound kernels with what the matrix cores sustain.
+ *   sink   device float, written only in a case that does not occur
+ * Asynchronous on `stream`; time it with pkv_timing_query("mfma_rate").
+ * PKV_ERR_INVALID_ARG for a null sink or non-positive counts. */
+int pkv_mfma_rate_probe(int workgroups, int iters, float* sink, void* stream);
+
 /* Contract validation on (1) or off (0) for this process, overriding PAGEDKV_VALIDATE. */
 int pkv_set_validate(int on);
 

@@ -18,7 +18,7 @@ __all__ = [
     "cow_block_copy", "kv_swap_out", "kv_swap_in", "paged_attn_decode_shared_prefix",
     "shared_prefix_workspace", "paged_attn_extend", "extend_workspace", "pkv_decode_workspace_size", "decode_workspace",
     "pkv_decode_auto_workers", "BlockPool", "timing_enable", "timing_query",
-    "stream_read_probe", "set_validate", "library_path", "load_library", "PKV_F32", "PKV_F16",
+    "stream_read_probe", "mfma_rate_probe", "set_validate", "library_path", "load_library", "PKV_F32", "PKV_F16",
     "PKV_BF16", "PrefixIndex",
 ]
 
@@ -100,6 +100,7 @@ def _declare(L):
         "pkv_set_validate": (c_int, [c_int]),
         "pkv_timing_query": (c_int, [ctypes.c_char_p, P(ctypes.c_double), P(ctypes.c_int64)]),
         "pkv_stream_read_probe": (c_int, [c_void, c_size, c_void, c_void]),
+        "pkv_mfma_rate_probe": (c_int, [c_int, c_int, c_void, c_void]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -402,6 +403,13 @@ def stream_read_probe(src: torch.Tensor, sink: torch.Tensor, stream=None):
     nbytes = src.numel() * src.element_size()
     _check(load_library().pkv_stream_read_probe(_dev(src, "src"), nbytes,
                                                 _dev(sink, "sink", torch.int32), _stream(stream)))
+
+
+def mfma_rate_probe(workgroups: int, iters: int, sink: torch.Tensor, stream=None):
+    """workgroups x 4 wavefronts, each iters x 8 independent 16x16x32 bf16 MFMAs (C:
+    ``pkv_mfma_rate_probe``)."""
+    _check(load_library().pkv_mfma_rate_probe(int(workgroups), int(iters),
+                                              _dev(sink, "sink", torch.float32), _stream(stream)))
 
 
 def set_validate(on: bool = True):

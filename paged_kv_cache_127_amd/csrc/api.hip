@@ -907,6 +907,18 @@ int pkv_timing_query(const char* name, double* total_ms, int64_t* launches) {
   return ok();
 }
 
+int pkv_mfma_rate_probe(int workgroups, int iters, float* sink, void* stream) {
+  if (!sink) return fail(PKV_ERR_INVALID_ARG, "pkv_mfma_rate_probe: null pointer");
+  if (workgroups <= 0 || iters <= 0 || workgroups > (1 << 20))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_mfma_rate_probe: %d workgroups, %d rounds",
+                workgroups, iters);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = timed("mfma_rate", st,
+                       [&] { return pkv::launch_mfma_rate(workgroups, iters, sink, st); });
+  if (e != hipSuccess) return launch_error(e, "pkv_mfma_rate_probe");
+  return ok();
+}
+
 int pkv_stream_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
   if (!src || !sink) return fail(PKV_ERR_INVALID_ARG, "pkv_stream_read_probe: null pointer");
   if (bytes == 0 || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(src) & 15))

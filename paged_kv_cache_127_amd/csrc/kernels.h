@@ -152,5 +152,8 @@ hipError_t launch_block_copy(const SwapParams& p, int num_cus, hipStream_t st);
 // Streaming-read probe (probe.hip): reads `bytes` (multiple of 16) of src once.
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int num_cus,
                               hipStream_t st);
+// Matrix-core probe (probe.hip): 4 wavefronts per workgroup, each `iters` x 8 independent
+// 16x16x32 bf16 MFMAs (16,384 flops each).
+hipError_t launch_mfma_rate(int workgroups, int iters, float* sink, hipStream_t st);
 
 }  // namespace pkv

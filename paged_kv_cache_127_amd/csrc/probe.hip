@@ -4,8 +4,13 @@
 // thread (the fastest of the plain-read shapes measured on MI355X: grid-stride loops and
 // fewer loads in flight read 2-15 % slower), and folds the data into a value that is stored
 // only if it equals a magic constant, so the loads cannot be dropped.
+//
+// Matrix-core probe: the reference point for kernels bound by the MFMA pipe. Each wavefront
+// issues `iters` rounds of 8 independent v_mfma_f32_16x16x32_bf16 (distinct accumulators, no
+// memory traffic) and stores the accumulators only if their sum equals a magic constant.
 #include "device_common.h"
 #include "kernels.h"
+#include "mfma_common.h"
 
 namespace pkv {
 
@@ -39,6 +44,32 @@ hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int
   const int blocks = (num_cus > 0 ? num_cus : 256) * 32;
   hipLaunchKernelGGL(stream_read, dim3(blocks), dim3(256), 0, st,
                      reinterpret_cast<const u32x4*>(src), n16, sink);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void mfma_rate(int iters, float* sink) {
+  u32x4 a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = 0x3f803f80u + threadIdx.x;   // bf16 pairs near 1
+    b[i] = 0x3f003f00u + i;             // bf16 pairs near 0.5
+  }
+  f32x4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = mfma16x16x32<bf16_t>(a, b, acc[j]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  if (s == 1234.5f) sink[0] = s;
+}
+
+hipError_t launch_mfma_rate(int workgroups, int iters, float* sink, hipStream_t st) {
+  if (workgroups <= 0 || iters <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mfma_rate, dim3(workgroups), dim3(256), 0, st, iters, sink);
   return hipGetLastError();
 }
 

@@ -444,6 +444,14 @@ def test_stream_read_probe_runs():
     assert int(sink.item()) == 0
 
 
+def test_mfma_rate_probe_runs():
+    """The matrix-core probe runs to completion and leaves the sink alone."""
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    pkv.mfma_rate_probe(8, 50, sink)
+    torch.cuda.synchronize()
+    assert float(sink.item()) == 0.0
+
+
 # ---- decode with the step's append fused in ----------------------------------------------
 @pytest.mark.parametrize("case", [("bf16", 16, 2, 128, 16), ("bf16", 64, 8, 128, 32),
                                   ("f16", 4, 4, 128, 16), ("f32", 8, 2, 64, 16),

@@ -223,3 +223,10 @@ def test_extend_argument_checks():
     assert call() == -3                           # no workspace
     assert L.pkv_extend_workspace_size(2, 8, 16, 2, 128, 4, 128) > 0
     assert L.pkv_extend_workspace_size(2, 8, 16, 3, 128, 4, 128) == 0
+
+
+def test_mfma_probe_argument_checks():
+    L = pkv.load_library()
+    assert L.pkv_mfma_rate_probe(4, 10, None, None) == -1
+    assert L.pkv_mfma_rate_probe(0, 10, 0x1000, None) == -1
+    assert L.pkv_mfma_rate_probe(4, 0, 0x1000, None) == -1
