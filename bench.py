@@ -456,14 +456,14 @@ def prefix_index_figures(pkv, requests: int = 500):
             "host_us_per_request_match_and_insert": round(us, 2)}
 
 
-def mfma_probe(pkv, torch, dev: str, iters: int = 2000, launches: int = 5):
-    """What 16x16x32 bf16 MFMAs sustain here (the library's probe), with one and with two
-    wavefronts per SIMD (1 and 2 workgroups of 4 wavefronts per CU)."""
+def mfma_probe(pkv, torch, dev: str, iters: int = 4000, launches: int = 5):
+    """What 16x16x32 bf16 MFMAs sustain here (the library's probe), with one, two and four
+    wavefronts per SIMD (1, 2 and 4 workgroups of 4 wavefronts per CU)."""
     props = torch.cuda.get_device_properties(dev)
     cus = props.multi_processor_count
     sink = torch.zeros(1, dtype=torch.float32, device=dev)
     res = {}
-    for per_cu in (1, 2):
+    for per_cu in (1, 2, 4):
         wgs = cus * per_cu
         pkv.mfma_rate_probe(wgs, 10, sink)
         torch.cuda.synchronize()

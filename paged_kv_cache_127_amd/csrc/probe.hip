@@ -54,9 +54,12 @@ __global__ __launch_bounds__(256) void mfma_rate(int iters, float* sink) {
     a[i] = 0x3f803f80u + threadIdx.x;   // bf16 pairs near 1
     b[i] = 0x3f003f00u + i;             // bf16 pairs near 0.5
   }
+  // Distinct starting values keep every accumulator in registers of its own: started from
+  // identical zeros, the compiler moved them between registers each round, and the MFMAs
+  // then waited on the moves (and so on each other's results).
   f32x4 acc[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{(float)(threadIdx.x + j), 0.f, 0.f, 0.f};
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = mfma16x16x32<bf16_t>(a, b, acc[j]);
