@@ -62,6 +62,20 @@ __device__ __forceinline__ void split_hi_lo(float p0, float p1, uint32_t& hi, ui
   }
 }
 
+// Max over the lanes that differ in lane bits 4 and 5 (the four 16-lane rows of the wavefront),
+// with the gfx950 lane-swap instructions: v_permlane16_swap exchanges the odd rows of its first
+// operand with the even rows of its second, v_permlane32_swap the upper half of the first with
+// the lower half of the second; given the same value twice, each returns every lane's value and
+// that of its partner row (half). No LDS round trip, unlike a shuffle through ds_bpermute.
+__device__ __forceinline__ float rows_max(float v) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
 template <typename T, int D, int B, int RBK>
 __global__ __launch_bounds__(64 * kRowWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void row_states(RowStateParams p) {
@@ -289,7 +303,7 @@ void row_states(RowStateParams p) {
         float mx = z[0];
 #pragma unroll
         for (int t = 1; t < 8; ++t) mx = fmaxf(mx, z[t]);
-        mx = cross_max<16>(mx);
+        mx = rows_max(mx);
         const float m_new = fmaxf(m_run[rb], mx);
         // a row with nothing to attend yet (causal limit) keeps (-inf, 0, 0): exponents
         // against 0 instead of -inf, so that no -inf - -inf appears
