@@ -90,7 +90,7 @@ struct ExtendFinishParams {
   int out_f32;
 };
 // Chunk groups and steps per wavefront for `base_workgroups` workgroups per chunk group over
-// up to max_tokens tokens: at least one workgroup per CU, at most 16 steps per wavefront and
+// up to max_tokens tokens: at least one workgroup per CU, at most 32 steps per wavefront and
 // 16 groups.
 void row_state_plan(int64_t base_workgroups, int max_tokens, int num_cus, int* chunk_groups,
                     int* steps_per_chunk);

@@ -43,8 +43,9 @@ namespace pkv {
 
 constexpr int kRowsRB = 2;            // 16-row blocks per wavefront
 constexpr int kRowWaves = 4;          // chunks per workgroup
-constexpr int kMaxStepsPerWave = 16;  // 32-token steps of one wavefront
+constexpr int kMaxStepsPerWave = 32;  // planned 32-token steps of one wavefront
 constexpr int kMaxChunkGroups = 16;   // states per row
+constexpr int kMinExtendSteps = 8;    // extend mode: fewest 32-token steps a wavefront is given
 
 // Two fp32 probabilities (in [0, 1]) as packed 16-bit high parts and remainders. bf16: the high
 // part is the fp32 value truncated to its upper half (one AND), so the remainder p - hi is exact
@@ -134,11 +135,15 @@ void row_states(RowStateParams p) {
     tok_end = min(max(L - n + t_last + 1, 0), L);
     blocks = (ctable_t)p.tables + (size_t)s * p.max_blocks;
   }
-  // this row group's steps, split evenly over the chunk groups' wavefronts (a short sequence
-  // gets short chunks rather than idle wavefronts)
+  // this row group's steps, split evenly over the chunk groups' wavefronts. In extend mode a
+  // wavefront gets at least kMinExtendSteps of them: every wavefront pays a fixed start (the
+  // dependent loads of its sequence's limits, block ids, queries and first keys and values)
+  // and end (the merge and the state stores), so a short sequence is better served by a few
+  // wavefronts than by short chunks on all of them; the others are left empty.
   const int nsteps = ceil_div(tok_end, 32);
   const int chunk = cg * kRowWaves + wave;
-  const int spc = ceil_div(nsteps, cgroups * kRowWaves);
+  int spc = ceil_div(nsteps, cgroups * kRowWaves);
+  if (extend) spc = max(spc, kMinExtendSteps);
   const int k0 = min(chunk * spc, nsteps);
   const int k1 = min(k0 + spc, nsteps);
   const int nb = ceil_div(tok_end, B);             // blocks holding the tokens
@@ -155,7 +160,6 @@ void row_states(RowStateParams p) {
 
   // query rows of the RB row blocks (padding rows repeat the last row and are never stored),
   // each row's output / state index and its token limit
-  u32x4 q[RBK][NC];
   size_t qrow[RBK];
   int lim[RBK];
 #pragma unroll
@@ -165,6 +169,32 @@ void row_states(RowStateParams p) {
     const int i = r - a * G;
     qrow[rb] = ((size_t)(extend ? qs + a : a)) * Hq + (size_t)g * G + i;
     lim[rb] = extend ? min(max(L - n + a + 1, 0), L) : tok_end;
+  }
+
+  // a workgroup none of whose chunks holds a step writes the empty state (-inf, 0, 0) of its
+  // rows for this chunk group -- what the merge below would produce -- and leaves (uniform
+  // over the workgroup, before any barrier)
+  if (cg * kRowWaves * spc >= nsteps) {
+    if (wave != 0) return;
+#pragma unroll
+    for (int rb = 0; rb < RBK; ++rb) {
+      const int r = (rg * RBK + rb) * 16 + r16;
+      if (r >= R) continue;
+      const size_t row = (size_t)cg * p.state_rows + qrow[rb];
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        store_nt(p.st_acc + row * D + 16 * f + 4 * jg, f32x4{0.f, 0.f, 0.f, 0.f});
+      if (jg == 0) {
+        store_nt(p.st_m + row, kNegInf);
+        store_nt(p.st_l + row, 0.f);
+      }
+    }
+    return;
+  }
+
+  u32x4 q[RBK][NC];
+#pragma unroll
+  for (int rb = 0; rb < RBK; ++rb) {
     const char* qp = reinterpret_cast<const char*>(p.q) + (qrow[rb] * D + 8 * jg) * ES;
 #pragma unroll
     for (int c = 0; c < NC; ++c) q[rb][c] = load16(qp + 32 * c * ES);

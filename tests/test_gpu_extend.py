@@ -88,6 +88,29 @@ def test_result_does_not_depend_on_workspace_contents():
     assert torch.equal(bits(_run(db, q, start, ws_fill=0)), bits(_run(db, q, start, ws_fill=255)))
 
 
+@pytest.mark.parametrize("lens,new,hq,hkv,d,B,dt", [
+    ([3000, 40], [3, 5], 8, 1, 128, 16, "bf16"),
+    ([2500], [4], 16, 2, 64, 32, "f16"),
+    ([4000, 1, 700], [2, 1, 9], 32, 4, 128, 16, "bf16"),
+])
+def test_few_workgroups_long_contexts(lens, new, hq, hkv, d, B, dt):
+    """Few row groups over long contexts: the plan spreads them over many chunk groups, each
+    wavefront still gets at least 8 steps, so most chunk groups of the short rows (and the far
+    ones of the long rows) have no step at all and write the empty state without loading
+    anything. Against the oracle, with the workspace NaN-filled and zero-filled."""
+    seed = zlib.crc32(repr((lens, new, hq)).encode()) % 10000
+    b = W.small_batch(lens, hq, hkv, d, B, DT[dt], seed=seed, poison=True)
+    q, start = W.extend_queries(b, new, seed=seed + 1)
+    db = DeviceBatch(b)
+    got = _run(db, q, start)
+    ref = oracle.extend_attention(q, start, b.k_pool, b.v_pool, b.tables, b.lengths, B)
+    err = float(np.abs(got.double().numpy() - ref).max())
+    print(f"{lens} {new} max-abs {err:.3g}")
+    assert np.isfinite(got.numpy()).all()
+    assert err <= TOL[DT[dt]], err
+    assert torch.equal(bits(got), bits(_run(db, q, start, ws_fill=0)))
+
+
 def test_speculative_verification_at_gqa_shape():
     """The GQA decode workload (256 sequences, 64/8 heads, bf16, B 16, log-normal lengths), its
     last 4 stored tokens of each sequence taken as the new ones; 24 sequences against the
