@@ -29,9 +29,10 @@
 // key/value fragment a wavefront loads serves its RB row blocks; two wavefronts per SIMD, so
 // that one computes while the other waits for memory. Block ids are scalar loads two steps
 // ahead, keys and values one step ahead. At the end the four wavefronts merge their states
-// through LDS (over the value tiles, no longer needed) and wavefront 0 writes one state
-// (m, l, acc) per row and chunk group: m in the log2 domain, acc not normalised. In prefix mode
-// the first workgroup also writes the suffix lengths max(L_s - P, 0).
+// through LDS (over the value tiles, no longer needed), each folding and storing a quarter of
+// the columns: one state (m, l, acc) per row and chunk group, m in the log2 domain, acc not
+// normalised. In prefix mode the first workgroup also writes the suffix lengths
+// max(L_s - P, 0).
 #include <algorithm>
 
 #include "device_common.h"
@@ -88,11 +89,12 @@ void row_states(RowStateParams p) {
   constexpr int VLPR = D / 8;            // lanes per value row (16 bytes each)
   constexpr int VTPI = 64 / VLPR;        // value rows per load instruction
   constexpr int TILE = 32 * ROWB;        // value tile per wavefront
-  // value tiles during the steps; afterwards the states of wavefronts 1..3 for the merge
+  // value tiles during the steps; afterwards the four wavefronts' states for the merge
   constexpr int STATE = RBK * NF * 64 * 16;
-  constexpr int LDS = kRowWaves * TILE > 3 * STATE ? kRowWaves * TILE : 3 * STATE;
+  constexpr int LDS = TILE > STATE ? kRowWaves * TILE : kRowWaves * STATE;
+  static_assert(NF % kRowWaves == 0, "column tiles per merging wavefront");
   __shared__ __attribute__((aligned(16))) char lds[LDS];
-  __shared__ float lds_ml[3][2][RBK][64];
+  __shared__ float lds_ml[kRowWaves][2][RBK][64];
 
   const int lane = threadIdx.x & 63;
   const int wave = uni((int)(threadIdx.x >> 6));
@@ -382,52 +384,55 @@ void row_states(RowStateParams p) {
     if (poison) l_tot[rb] = __builtin_nanf("");
   }
 
-  // Merge the four wavefronts' states: wavefronts 1..3 leave theirs in LDS (the same lane ->
-  // (row, column) mapping in every wavefront, so wavefront 0's lane reads its own slots), one
-  // barrier, and wavefront 0 folds them into its own.
+  // Merge the four wavefronts' states: each leaves its (m, l, acc) in LDS (the same lane ->
+  // (row, column) mapping in every wavefront), one barrier, then wavefront w folds the four
+  // states of column tiles w, w + 4, ... and stores them; wavefront 0 also stores m and l.
   f32x4* mrg = reinterpret_cast<f32x4*>(lds);
   __syncthreads();   // every wavefront is done with its value tile
-  if (wave != 0) {
-    f32x4* dst = mrg + (size_t)(wave - 1) * RBK * NF * 64;
+  {
+    f32x4* dst = mrg + (size_t)wave * RBK * NF * 64;
 #pragma unroll
     for (int rb = 0; rb < RBK; ++rb) {
 #pragma unroll
       for (int f = 0; f < NF; ++f) dst[(rb * NF + f) * 64 + lane] = oacc[rb][f];
-      lds_ml[wave - 1][0][rb][lane] = m_run[rb];
-      lds_ml[wave - 1][1][rb][lane] = l_tot[rb];
+      lds_ml[wave][0][rb][lane] = m_run[rb];
+      lds_ml[wave][1][rb][lane] = l_tot[rb];
     }
   }
   __syncthreads();
-  if (wave != 0) return;
-#pragma unroll 1
-  for (int w = 0; w < kRowWaves - 1; ++w) {
-    const f32x4* src = mrg + (size_t)w * RBK * NF * 64;
-#pragma unroll
-    for (int rb = 0; rb < RBK; ++rb) {
-      const float mo = lds_ml[w][0][rb][lane];
-      const float lo = lds_ml[w][1][rb][lane];
-      const float mn = fmaxf(m_run[rb], mo);
-      const float a_self = mn == kNegInf ? 0.f : fast_exp2(m_run[rb] - mn);
-      const float a_other = mn == kNegInf ? 0.f : fast_exp2(mo - mn);
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-        oacc[rb][f] = oacc[rb][f] * a_self + src[(rb * NF + f) * 64 + lane] * a_other;
-      l_tot[rb] = l_tot[rb] * a_self + lo * a_other;
-      m_run[rb] = mn;
-    }
-  }
 
   // state of chunk group cg: st_m / st_l [cgroups][state_rows], st_acc [..][state_rows][D]
 #pragma unroll
   for (int rb = 0; rb < RBK; ++rb) {
+    float mw[kRowWaves];
+    float mx = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) {
+      mw[w] = lds_ml[w][0][rb][lane];
+      mx = fmaxf(mx, mw[w]);
+    }
+    float wgt[kRowWaves];
+    float lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) {
+      wgt[w] = mx == kNegInf ? 0.f : fast_exp2(mw[w] - mx);
+      lsum += lds_ml[w][1][rb][lane] * wgt[w];
+    }
     const int r = (rg * RBK + rb) * 16 + r16;
     if (r >= R) continue;
     const size_t row = (size_t)cg * p.state_rows + qrow[rb];
 #pragma unroll
-    for (int f = 0; f < NF; ++f) store_nt(p.st_acc + row * D + 16 * f + 4 * jg, oacc[rb][f]);
-    if (jg == 0) {
-      store_nt(p.st_m + row, m_run[rb]);
-      store_nt(p.st_l + row, l_tot[rb]);
+    for (int j = 0; j < NF / kRowWaves; ++j) {
+      const int f = wave + kRowWaves * j;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kRowWaves; ++w)
+        acc += mrg[((size_t)w * RBK * NF + rb * NF + f) * 64 + lane] * wgt[w];
+      store_nt(p.st_acc + row * D + 16 * f + 4 * jg, acc);
+    }
+    if (wave == 0 && jg == 0) {
+      store_nt(p.st_m + row, mx);
+      store_nt(p.st_l + row, lsum);
     }
   }
 }
