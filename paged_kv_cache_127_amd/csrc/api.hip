@@ -837,11 +837,17 @@ int paged_attn_extend(void* out, int out_dtype, const void* q, const int32_t* qu
   rp.chunk_groups = el.chunk_groups;
   rp.steps_per_chunk = el.steps_per_chunk;
   rp.scale_log2 = sc * 1.4426950408889634f;
+  // one chunk group: each workgroup's merged state is its rows' whole softmax, normalised and
+  // written straight to `out` (no finish kernel)
+  const bool direct = el.chunk_groups == 1;
+  rp.out = direct ? out : nullptr;
+  rp.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
   hipError_t e = timed("extend_states", st, [&] {
     return pkv::launch_row_states(rp, kv_dtype, head_dim, block_size, st);
   });
   if (e != hipSuccess)
     return fail(PKV_ERR_LAUNCH, "%s: states kernel: %s", fn, hipGetErrorString(e));
+  if (direct) return ok();
   pkv::ExtendFinishParams fp{out, rp.st_m, rp.st_l, rp.st_acc, rp.state_rows, el.chunk_groups,
                              out_dtype == PKV_F32 ? 1 : 0};
   e = timed("extend_finish", st,

@@ -70,6 +70,9 @@ struct RowStateParams {
   float* st_m;                    // [chunk_groups][state_rows]
   float* st_l;                    // [chunk_groups][state_rows]
   float* st_acc;                  // [chunk_groups][state_rows][D]
+  void* out;                      // extend mode with one chunk group: the normalised rows
+                                  // [T * Hq][D] go here directly (states unused); else null
+  int out_f32;                    // out is fp32 (else the cache's 16-bit type)
   size_t state_rows;              // S * Hq (prefix mode) or T * Hq (extend mode)
   int num_seqs;
   int num_q_heads;

@@ -78,6 +78,21 @@ __device__ __forceinline__ float rows_max(float v) {
   return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
+// Four normalised output values (x * s) at element `off` of the output rows, fp32 or the
+// cache's 16-bit type (rounded once from the fp32 product).
+template <typename T>
+__device__ __forceinline__ void store_row4(const RowStateParams& p, size_t off, f32x4 x, float s) {
+  if (p.out_f32) {
+    store_nt(reinterpret_cast<float*>(p.out) + off, x * s);
+  } else {
+    const uint32_t w0 =
+        (uint32_t)scaled_to_16<T>(x[0], s) | ((uint32_t)scaled_to_16<T>(x[1], s) << 16);
+    const uint32_t w1 =
+        (uint32_t)scaled_to_16<T>(x[2], s) | ((uint32_t)scaled_to_16<T>(x[3], s) << 16);
+    store_nt(reinterpret_cast<uint16_t*>(p.out) + off, u32x2{w0, w1});
+  }
+}
+
 template <typename T, int D, int B, int RBK>
 __global__ __launch_bounds__(64 * kRowWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void row_states(RowStateParams p) {
@@ -182,6 +197,12 @@ void row_states(RowStateParams p) {
     for (int rb = 0; rb < RBK; ++rb) {
       const int r = (rg * RBK + rb) * 16 + r16;
       if (r >= R) continue;
+      if (p.out) {                                 // nothing to attend: a zero row
+#pragma unroll
+        for (int f = 0; f < NF; ++f) store_row4<T>(p, qrow[rb] * D + 16 * f + 4 * jg,
+                                                    f32x4{0.f, 0.f, 0.f, 0.f}, 0.f);
+        continue;
+      }
       const size_t row = (size_t)cg * p.state_rows + qrow[rb];
 #pragma unroll
       for (int f = 0; f < NF; ++f)
@@ -421,6 +442,9 @@ void row_states(RowStateParams p) {
     const int r = (rg * RBK + rb) * 16 + r16;
     if (r >= R) continue;
     const size_t row = (size_t)cg * p.state_rows + qrow[rb];
+    // one chunk group: this state is the row's whole softmax, normalised here exactly as the
+    // finish kernel would (weight 1, den = l; 0 for a row with nothing to attend)
+    const float sc = (mx == kNegInf || lsum == 0.f) ? 0.f : 1.0f / lsum;
 #pragma unroll
     for (int j = 0; j < NF / kRowWaves; ++j) {
       const int f = wave + kRowWaves * j;
@@ -428,9 +452,10 @@ void row_states(RowStateParams p) {
 #pragma unroll
       for (int w = 0; w < kRowWaves; ++w)
         acc += mrg[((size_t)w * RBK * NF + rb * NF + f) * 64 + lane] * wgt[w];
-      store_nt(p.st_acc + row * D + 16 * f + 4 * jg, acc);
+      if (p.out) store_row4<T>(p, qrow[rb] * D + 16 * f + 4 * jg, acc, sc);
+      else store_nt(p.st_acc + row * D + 16 * f + 4 * jg, acc);
     }
-    if (wave == 0 && jg == 0) {
+    if (!p.out && wave == 0 && jg == 0) {
       store_nt(p.st_m + row, mx);
       store_nt(p.st_l + row, lsum);
     }

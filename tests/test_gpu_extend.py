@@ -111,6 +111,36 @@ def test_few_workgroups_long_contexts(lens, new, hq, hkv, d, B, dt):
     assert torch.equal(bits(got), bits(_run(db, q, start, ws_fill=0)))
 
 
+def test_one_chunk_group_writes_the_output_directly():
+    """When the row groups alone fill the CUs (96 sequences x 4 KV heads, at most 24 rows each)
+    and no row group is long, the plan uses one chunk group and the states kernel writes the
+    normalised rows itself: no finish launch (the library's own launch timing shows none),
+    parity with the oracle, 16-bit output = RNE of the fp32 output, sequences with no new
+    token untouched."""
+    rng = np.random.default_rng(31)
+    lens = [int(x) for x in rng.integers(20, 600, size=96)]
+    new = [int(x) for x in rng.integers(0, 7, size=96)]
+    b = W.small_batch(lens, 16, 4, 128, 16, torch.bfloat16, seed=32, poison=True)
+    q, start = W.extend_queries(b, new, seed=33)
+    db = DeviceBatch(b)
+    pkv.timing_enable(True, every=1)
+    try:
+        f32 = _run(db, q, start)
+        torch.cuda.synchronize()
+        _, n_states = pkv.timing_query("extend_states")
+        _, n_finish = pkv.timing_query("extend_finish")
+    finally:
+        pkv.timing_enable(False)
+    assert n_states >= 1 and n_finish == 0, (n_states, n_finish)
+    ref = oracle.extend_attention(q, start, b.k_pool, b.v_pool, b.tables, b.lengths, 16)
+    err = float(np.abs(f32.double().numpy() - ref).max())
+    print(f"one chunk group, {int(start[-1])} query tokens: max-abs {err:.3g}")
+    assert np.isfinite(f32.numpy()).all()
+    assert err <= 2e-3, err
+    b16 = _run(db, q, start, out_dtype=torch.bfloat16)
+    assert torch.equal(bits(b16), bits(f32.to(torch.bfloat16)))
+
+
 def test_speculative_verification_at_gqa_shape():
     """The GQA decode workload (256 sequences, 64/8 heads, bf16, B 16, log-normal lengths), its
     last 4 stored tokens of each sequence taken as the new ones; 24 sequences against the
