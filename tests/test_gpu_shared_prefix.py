@@ -86,16 +86,18 @@ def test_16bit_output_is_rounded_fp32_output():
     assert torch.equal(bits(b16), bits(f32.to(torch.bfloat16)))
 
 
-def test_shared_prefix_workload_full_size():
-    """128 sequences over an 800-token prefix with U{1..512}-token suffixes (64/8 heads,
-    head_dim 128, bf16, block size 16), in the launch configuration the benchmark times;
+@pytest.mark.parametrize("prefix_len", [800, 4096, 8192])
+def test_shared_prefix_workload_full_size(prefix_len):
+    """128 sequences over an 800-, 4096- or 8192-token prefix with U{1..512}-token suffixes
+    (64/8 heads, head_dim 128, bf16, block size 16), in the launch configuration the benchmark
+    times (800 and 4096: one chunk group of up to 32 steps per wavefront; 8192: two groups);
     16 sequences checked against the oracle, all against the plain decode."""
-    b = W.config4a()
+    b = W.config4a(prefix_len=prefix_len)
     db = DeviceBatch(b)
-    got = _run(db, 800)
+    got = _run(db, prefix_len)
     seqs = list(range(0, 128, 8))
-    err = float(np.abs(got.double().numpy()[seqs] - _ref(b, 800, seqs)).max())
-    print(f"shared-prefix workload: max-abs {err:.3g} on {len(seqs)} sequences")
+    err = float(np.abs(got.double().numpy()[seqs] - _ref(b, prefix_len, seqs)).max())
+    print(f"shared-prefix workload, prefix {prefix_len}: max-abs {err:.3g} on {len(seqs)} sequences")
     assert err <= 2e-3, err
     plain = db.decode()
     assert float((plain - got).abs().max()) <= 4e-3
