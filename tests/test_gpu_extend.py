@@ -162,6 +162,28 @@ def test_speculative_verification_at_gqa_shape():
     assert np.isfinite(got.numpy()).all()
 
 
+def test_prefill_chunk_at_bench_shape():
+    """The prefill chunk the benchmark times: 8 sequences of 1024..4096 stored tokens (64/8
+    heads, d 128, bf16, B 16), the last 256 of each new. The last 16 new tokens of the longest,
+    the shortest and one middle sequence against the oracle (the last m tokens of a run attend
+    exactly as a run of m new tokens would)."""
+    b = W.small_batch(W.rng_for(W.SEED_BASE + 9, 0).integers(1024, 4096, size=8, endpoint=True),
+                      64, 8, 128, 16, torch.bfloat16, seed=W.SEED_BASE + 9)
+    new = np.full(8, 256)
+    q, start = W.extend_queries(b, new, seed=72)
+    got = _run(DeviceBatch(b), q, start)
+    m = 16
+    sel = np.array([int(np.argmax(b.lengths)), int(np.argmin(b.lengths)), 3])
+    rows = np.concatenate([np.arange(start[s + 1] - m, start[s + 1]) for s in sel])
+    sub = np.arange(len(sel) + 1, dtype=np.int32) * m
+    ref = oracle.extend_attention(q[torch.from_numpy(rows)], sub, b.k_pool, b.v_pool,
+                                  b.tables[sel], b.lengths[sel], 16)
+    err = float(np.abs(got.double().numpy()[rows] - ref).max())
+    print(f"prefill chunk: max-abs {err:.3g} over {len(rows)} rows")
+    assert err <= 2e-3, err
+    assert np.isfinite(got.numpy()).all()
+
+
 def test_rejections_and_validation():
     b = W.small_batch([40, 20], 16, 2, 128, 16, torch.bfloat16, seed=18)
     q, start = W.extend_queries(b, [4, 3], seed=19)
