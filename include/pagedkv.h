@@ -104,8 +104,10 @@ const char* pkv_last_error(void);
  *   num_seqs      at most 4096 per call
  *   scale         softmax scale; <= 0 selects 1/sqrt(head_dim)
  *   num_workers   0 = automatic (as many wavefronts as the chosen kernel keeps resident on
- *                 the current device, at most 8 per compute unit), else 1 .. 2^20 (any
- *                 count gives the same result up to rounding)
+ *                 the current device, at most 8 per compute unit, and no more than
+ *                 num_kv_heads * num_seqs * ceil(max_context_len / 32), the most 32-token
+ *                 steps the call can have), else 1 .. 2^20 (any count gives the same result
+ *                 up to rounding)
  *   workspace     device scratch, 256-byte aligned, of at least
  *                 pkv_decode_workspace_size(...) bytes for the same num_workers; no contents
  *                 are assumed between calls. Calls that overlap in time need separate
@@ -114,7 +116,8 @@ const char* pkv_last_error(void);
 size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                  int num_workers);
 
-/* The worker count that num_workers = 0 selects on the current device. */
+/* The worker count that num_workers = 0 selects on the current device for a call with at
+ * least that many 32-token steps (an upper bound on what it uses; it sizes the workspace). */
 int pkv_decode_auto_workers(void);
 
 int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_pool,

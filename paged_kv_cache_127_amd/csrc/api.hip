@@ -261,6 +261,11 @@ int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const v
     if (per_cu <= 0 || per_cu > kWorkersPerCU) per_cu = kWorkersPerCU;
     const int cus = cu_count();
     n = (cus > 0 ? cus : 256) * per_cu;
+    // no more workers than the line can have steps: a worker past them would only pay the
+    // schedule prologue, and every extra range boundary is one more partial to merge
+    const int64_t max_steps = (int64_t)num_kv_heads * num_seqs *
+                              ((max_context_len + pkv::kStepTokens - 1) / pkv::kStepTokens);
+    if (max_steps < n) n = (int)std::max<int64_t>(max_steps, 1);
   }
   const int pw = piece_weight();
   {
