@@ -16,8 +16,9 @@
 // section "RadixAttention: caching, not just packing, the prefix": only the tokens past the
 // shared part need a fresh prefill pass) -- are already stored; new token t of n attends to
 // positions 0 .. L - n + t of its sequence (causal). Its n * G rows of a KV head attend to the
-// sequence's own blocks with a per-row token limit; extend_finish folds each row's states and
-// normalises.
+// sequence's own blocks with a per-row token limit. With one chunk group a workgroup's merged
+// state is its rows' whole softmax and is normalised into the output right here; with several,
+// extend_finish folds each row's states and normalises.
 //
 // row_states. A workgroup of four wavefronts takes (row group of RB * 16 rows of one KV head,
 // chunk group); wavefront w runs chunk 4 * cg + w, a run of 32-token steps. Per step the MFMA
@@ -31,7 +32,7 @@
 // ahead, keys and values one step ahead. At the end the four wavefronts merge their states
 // through LDS (over the value tiles, no longer needed), each folding and storing a quarter of
 // the columns: one state (m, l, acc) per row and chunk group, m in the log2 domain, acc not
-// normalised. In prefix mode the first workgroup also writes the suffix lengths
+// normalised (or, extend mode with one chunk group, the normalised rows). In prefix mode the first workgroup also writes the suffix lengths
 // max(L_s - P, 0).
 #include <algorithm>
 
