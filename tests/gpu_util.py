@@ -56,10 +56,18 @@ class DeviceBatch:
         return out.cpu()
 
 
+def widened(pool):
+    """A cache pool as a float32 NumPy array: exact for fp16, bf16 and fp32 values, and the
+    oracle's gathers run several times faster on it than on 16-bit torch tensors."""
+    if isinstance(pool, torch.Tensor):
+        return pool.detach().cpu().float().numpy()
+    return pool
+
+
 def oracle_decode(b, q=None, seqs=None, k_pool=None, v_pool=None, tables=None, lengths=None):
     return oracle.paged_decode(b.q if q is None else q,
-                               b.k_pool if k_pool is None else k_pool,
-                               b.v_pool if v_pool is None else v_pool,
+                               widened(b.k_pool if k_pool is None else k_pool),
+                               widened(b.v_pool if v_pool is None else v_pool),
                                b.tables if tables is None else tables,
                                b.lengths if lengths is None else lengths, b.block_size,
                                seqs=seqs)

@@ -142,9 +142,8 @@ def test_most_sequences_per_call(case):
     lens[:3] = (0, 1, 47)
     b = W.small_batch(lens, hq, hkv, d, B, DT[dt], seed=71, poison=True)
     got = DeviceBatch(b).decode()
-    seqs = sorted(set(range(0, 4096, 61)) | {0, 1, 2, 4095})
-    err = max_err(got, oracle_decode(b, seqs=seqs), seqs)
-    print(f"4096 sequences {case} max-abs (sampled) {err:.3g}")
+    err = max_err(got, oracle_decode(b))
+    print(f"4096 sequences {case} max-abs {err:.3g}")
     assert err <= 2e-3
     assert torch.equal(got[0].cpu(), torch.zeros_like(got[0].cpu()))   # empty context
     assert not torch.isnan(got).any()
@@ -240,9 +239,8 @@ def test_config4a_shared_prefix():
     a = DeviceBatch(shared).decode()
     c = DeviceBatch(private).decode()
     assert torch.equal(bits(a), bits(c))              # sharing changes nothing
-    seqs = list(range(0, 128, 8))
-    err = max_err(a, oracle_decode(shared, seqs=seqs), seqs)
-    print(f"config4a max-abs (16 sampled sequences) {err:.3g}")
+    err = max_err(a, oracle_decode(shared))
+    print(f"config4a max-abs (all 128 sequences) {err:.3g}")
     assert err <= 2e-3
 
 
