@@ -3,17 +3,19 @@
 Workload (one "step" = one pass of the whole decode path over one batch): the GQA decode
 batch -- 256 sequences, 64 query / 8 KV heads, head_dim 128, bf16 cache, 16-token blocks at
 seeded random physical placement, context lengths log-normal (median 512, sigma 1) clipped to
-[16, 4096]. Each step stores one new token per sequence with ``kv_cache_append`` (it rewrites
-the current token's slot, so the batch shape is the same every step) and then runs
-``paged_attn_decode`` (partition kernel + split-K merge). Inputs are resident in HBM before
-timing starts.
+[16, 4096]. Each step stores one new token per sequence and decodes all sequences with
+``paged_attn_decode_append`` (the append fused into the decode). Inputs are resident in HBM
+before timing starts. ``--workload mha`` / ``long`` put the multi-head fp16 batch or the
+long-context batch in the headline loop instead (for profiling those configs on their own).
 
-Prints ONE JSON line. ``value`` is KV bytes per step (2 * sum(L) * H_kv * d * 2 B, each KV head
-once) divided by the measured step time. ``roofline`` reports the decode partition kernel: the
-same KV bytes divided by that kernel's average duration (hipEvents the library records on the
-launch stream around every 8th launch of each kernel in the timed region), against the 8 TB/s
-HBM peak. ``cpu_baseline`` times
-the CPU oracle (fp64, one thread) on the same batch.
+Prints ONE JSON line. ``value`` is KV bytes per step (2 * sum(L) * H_kv * d * sizeof, each KV
+head once) divided by the measured step time: K steps launched back to back, wall clock
+around them, the library's own timing off (the same step captured in a HIP graph and replayed
+is reported under ``graph_replay``). ``roofline`` reports the decode kernel: the same KV bytes
+divided by that kernel's average duration, from hipEvents the library records on the launch
+stream around every launch of a dedicated loop of ``--kernel-launches`` steps (100 by
+default, whatever ``--steps`` is), against the 8 TB/s HBM peak. ``cpu_baseline`` times the CPU oracle (fp64, one
+thread) on the same batch.
 """
 from __future__ import annotations
 
@@ -29,7 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-TIMING_EVERY = 8
+KERNEL_LAUNCHES = 100
 METRIC = "paged decode attention KV GB/s (fraction of HBM peak) and seq-steps/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_mfma_gqa256_b16_traffic.json")
 KERNEL_SOURCES = ["paged_kv_cache_127_amd/csrc/decode_mfma.hip",
@@ -116,6 +118,24 @@ def _decode_timing(pkv, torch, launch, launches: int):
     names = ("decode_partial", "splitk_reduce", "append", "cow")
     kt, step = _kernel_times(pkv, torch, launch, names, launches)
     return [kt[n] for n in names] + [step]
+
+
+def kernel_loop(pkv, torch, launch, names, launches: int):
+    """{kernel name: (mean us, launches timed)} over `launches` calls of `launch`, from the
+    hipEvents the library records on the launch stream around every launch of each kernel."""
+    for _ in range(3):
+        launch()
+    torch.cuda.synchronize()
+    pkv.timing_enable(True, every=1)
+    for _ in range(launches):
+        launch()
+    torch.cuda.synchronize()
+    out = {}
+    for name in names:
+        ms, n = pkv.timing_query(name)
+        out[name] = (ms / n * 1e3 if n else 0.0, n)
+    pkv.timing_enable(False)
+    return out
 
 
 def other_configs(pkv, W, torch, dev: str, workers: int, launches: int = 30):
@@ -555,18 +575,57 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def headline_workload(name, block_size, W, torch, dev):
+    """The batch, the step and its description for the workload the JSON line reports.
+
+    gqa (default): the GQA decode batch at ``block_size``; a step appends one new token per
+    sequence (it rewrites the current token's slot, so the batch is the same every step) and
+    decodes all sequences with ``paged_attn_decode_append``. mha: the multi-head fp16 batch,
+    a plain decode per step. long: the long-context batch, one appended token per sequence
+    fused into the decode. The last two exist so that each HBM-bound config can be profiled
+    on its own; the default line is the GQA batch."""
+    if name == "gqa":
+        b = W.config3(block_size)
+        desc = (f"GQA decode batch: {b.num_seqs} sequences, {b.num_q_heads} query / "
+                f"{b.num_kv_heads} KV heads, head_dim {b.head_dim}, bf16 cache, block size "
+                f"{block_size}, log-normal context lengths (median 512, sigma 1, clipped to "
+                "[16, 4096]), seeded random block placement in a 1.25x pool; one appended "
+                "token per sequence per step (paged_attn_decode_append: append fused into the "
+                "decode kernel)")
+        append = True
+    elif name == "mha":
+        b = W.config2()
+        desc = ("MHA decode batch: 64 sequences, 32 query / 32 KV heads, head_dim 128, fp16 "
+                "cache, block size 16, context lengths uniform in [128, 2048], seeded random "
+                "block placement in a 1.25x pool; one decode per step (paged_attn_decode)")
+        append = False
+    else:
+        b = W.config5(steps=1)
+        desc = ("long contexts: 8 sequences, 64 query / 8 KV heads, head_dim 128, bf16 cache, "
+                "block size 16, context lengths uniform in [16384, 32768]; one appended token "
+                "per sequence per step (paged_attn_decode_append)")
+        append = True
+    return b, desc, append
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gqa", choices=("gqa", "mha", "long"),
+                    help="batch of the headline line (gqa is the graded one)")
     ap.add_argument("--block-size", type=int, default=16, choices=(16, 32))
     ap.add_argument("--workers", type=int, default=0, help="decode wavefronts (0 = automatic)")
+    ap.add_argument("--kernel-launches", type=int, default=KERNEL_LAUNCHES,
+                    help="launches in the dedicated kernel-timing loop")
     ap.add_argument("--cpu-steps", type=int, default=15,
                     help="decode steps of the CPU oracle (about 0.7 s each on one core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the figures on the other batch configs and the read probe")
+    ap.add_argument("--no-graph-replay", action="store_true",
+                    help="skip the HIP-graph replay comparison (counter runs)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -584,7 +643,7 @@ def main():
 
     dev = "cuda:0"
     t_gen = time.perf_counter()
-    b = W.config3(args.block_size)
+    b, desc, fused_append = headline_workload(args.workload, args.block_size, W, torch, dev)
     S, Hq, Hkv, d = b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim
     q = b.q.to(dev)
     k_pool = b.k_pool.to(dev)
@@ -598,6 +657,7 @@ def main():
     seq_ids = torch.arange(S, dtype=torch.int32, device=dev)
     positions = (lens - 1).to(torch.int32)
     gen_s = time.perf_counter() - t_gen
+    dtype_name = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[b.dtype]
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -608,56 +668,70 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # One decode step: every sequence appends its newest token (position L - 1; the same slot
-    # each step, so the batch stays the same) and all sequences decode. The timed step is the
-    # fused call; the same work as two calls (kv_cache_append, then paged_attn_decode) is
-    # timed afterwards for comparison.
+    # One decode step over the whole batch (see headline_workload). The same work as two calls
+    # (kv_cache_append, then paged_attn_decode) is timed afterwards for comparison.
     def step():
-        pkv.paged_attn_decode_append(out, q, k_pool, v_pool, k_new, v_new, tables, lens, max_ctx,
-                                     num_workers=args.workers, workspace=ws)
+        if fused_append:
+            pkv.paged_attn_decode_append(out, q, k_pool, v_pool, k_new, v_new, tables, lens,
+                                         max_ctx, num_workers=args.workers, workspace=ws)
+        else:
+            pkv.paged_attn_decode(out, q, k_pool, v_pool, tables, lens, max_ctx,
+                                  num_workers=args.workers, workspace=ws)
 
     def step_two_calls():
         pkv.kv_cache_append(k_pool, v_pool, k_new, v_new, seq_ids, positions, tables)
         pkv.paged_attn_decode(out, q, k_pool, v_pool, tables, lens, max_ctx,
                               num_workers=args.workers, workspace=ws)
 
+    pkv.timing_enable(False)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # kernel durations: hipEvents around every TIMING_EVERY-th launch of each kernel (events
-    # between all launches would add their own cost to the step time)
-    pkv.timing_enable(True, every=TIMING_EVERY)
-    torch.cuda.synchronize()
+    # headline: K steps back to back, launched eagerly through the Python binding, the
+    # library's own timing off, wall clock around them
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kernel_ms, kernel_n = pkv.timing_query("decode_partial")
-    reduce_ms, reduce_n = pkv.timing_query("splitk_reduce")
-    pkv.timing_enable(False)
-
-    # the same step as two calls
-    for _ in range(args.warmup):
-        step_two_calls()
-    torch.cuda.synchronize()
-    pkv.timing_enable(True, every=TIMING_EVERY)
-    t2 = time.perf_counter()
-    for _ in range(args.steps):
-        step_two_calls()
-    torch.cuda.synchronize()
-    two_ms = (time.perf_counter() - t2) * 1e3 / args.steps
-    append_ms, append_n = pkv.timing_query("append")
-    dec2_ms, dec2_n = pkv.timing_query("decode_partial")
-    pkv.timing_enable(False)
-
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # the same step captured once in a HIP graph and replayed K times (for comparison: on this
+    # ROCm release graph replays of this step run slower than eager launches)
+    graph_ms = None
+    if not args.no_graph_replay:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        del graph
+
+    # kernel durations: a dedicated loop of its own (independent of --steps), hipEvents the
+    # library records on the launch stream around every launch of each kernel
+    kt = kernel_loop(pkv, torch, step, ("decode_partial", "splitk_reduce"), args.kernel_launches)
+    kern_avg_us, kernel_n = kt["decode_partial"]
+    reduce_us, _ = kt["splitk_reduce"]
+
     kv_bytes = b.kv_bytes
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    kern_avg_ms = kernel_ms / max(kernel_n, 1)
-    achieved = kv_bytes / (kern_avg_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.block_size, args.workers)
+    achieved = kv_bytes / (kern_avg_us * 1e-6) / 1e9
+    is_valu = Hq == Hkv or b.dtype == torch.float32
+    kname = "decode_partial_valu" if is_valu else "decode_partial_mfma"
+    traffic = measured_traffic(args.block_size, args.workers) if args.workload == "gqa" else None
 
     result = {
         "metric": METRIC,
@@ -670,47 +744,57 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": dtype_name,
         "data": "synthetic",
         "config": {
-            "workload": (f"GQA decode batch: {S} sequences, {Hq} query / {Hkv} KV heads, "
-                         f"head_dim {d}, bf16 cache, block size {args.block_size}, log-normal "
-                         "context lengths (median 512, sigma 1, clipped to [16, 4096]), seeded "
-                         "random block placement in a 1.25x pool; one appended token per "
-                         "sequence per step (paged_attn_decode_append: append fused into the "
-                         "decode kernel)"),
+            "workload": desc,
             "num_seqs": S,
             "sum_context_tokens": int(b.lengths.sum()),
-            "block_size": args.block_size,
+            "block_size": b.block_size,
             "num_workers": args.workers or "auto",
             "kv_bytes_per_step": kv_bytes,
         },
+        "step_launch": "eager calls through the Python binding, back to back",
+        "graph_replay": None if graph_ms is None else {
+            "what": "the same step captured in a HIP graph, K replays back to back",
+            "ms_per_step": round(graph_ms, 5),
+            "value": round(kv_bytes / (graph_ms * 1e-3) / 1e9, 2)},
         "seq_steps_per_s": round(S / (ms_per_step * 1e-3), 1),
         "hbm_fraction_of_step": round(value / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_partial_mfma",
+            "kernel": kname,
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "avg_kernel_us": round(kern_avg_ms * 1e3, 3),
+            "avg_kernel_us": round(kern_avg_us, 3),
             "timed_launches": kernel_n,
-            "timing": f"hipEvents around every {TIMING_EVERY}th launch in the timed region",
+            "timing": (f"hipEvents around each of {kernel_n} launches in a dedicated loop after "
+                       "the timed steps; the headline steps ran with the library's timing off"),
         },
-        "other_kernels_avg_us": {
-            "splitk_reduce": round(reduce_ms / max(reduce_n, 1) * 1e3, 3),
-        },
-        "two_calls": {
+        "other_kernels_avg_us": {"splitk_reduce": round(reduce_us, 3)},
+        "setup_s": round(gen_s, 2),
+    }
+    if args.workload == "gqa":
+        for _ in range(args.warmup):
+            step_two_calls()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(args.steps):
+            step_two_calls()
+        torch.cuda.synchronize()
+        two_ms = (time.perf_counter() - t2) * 1e3 / args.steps
+        kt2 = kernel_loop(pkv, torch, step_two_calls, ("decode_partial", "append"),
+                          max(20, args.kernel_launches // 4))
+        result["two_calls"] = {
             "what": "the same step as kv_cache_append + paged_attn_decode",
             "ms_per_step": round(two_ms, 5),
             "value": round(kv_bytes / (two_ms * 1e-3) / 1e9, 2),
-            "decode_kernel_us": round(dec2_ms / max(dec2_n, 1) * 1e3, 3),
-            "append_kernel_us": round(append_ms / max(append_n, 1) * 1e3, 3),
-        },
-        "setup_s": round(gen_s, 2),
-    }
+            "decode_kernel_us": round(kt2["decode_partial"][0], 3),
+            "append_kernel_us": round(kt2["append"][0], 3),
+        }
     # step-time spread: torch events around every step (on the stream the library launches on)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(100)]
@@ -721,8 +805,11 @@ def main():
     torch.cuda.synchronize()
     st_us = sorted(a.elapsed_time(e) * 1e3 for a, e in ev)
     result["step_us_percentiles"] = {"p10": round(st_us[10], 2), "p50": round(st_us[50], 2),
-                                     "p90": round(st_us[90], 2), "steps": len(st_us)}
-    if not args.no_other_configs:
+                                     "p90": round(st_us[90], 2), "steps": len(st_us),
+                                     "what": "torch events around each of 100 eager steps"}
+    print(f"bench: step {ms_per_step * 1e3:.1f} us, decode kernel {kern_avg_us:.1f} us "
+          f"({achieved / HBM_PEAK_GBS:.3f} of peak)", file=sys.stderr, flush=True)
+    if not args.no_other_configs and args.workload == "gqa":
         del k_pool, v_pool, q, out, ws
         torch.cuda.empty_cache()
         probe = stream_probe(pkv, torch, dev)
@@ -733,7 +820,7 @@ def main():
         result["swap"] = swap_figures(pkv, W, torch, dev)
         result["extend"] = extend_figures(pkv, W, torch, dev)
         result["prefix_index"] = prefix_index_figures(pkv)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == "gqa":
         print("bench: oracle on one core", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(b, args.cpu_steps)
         print("bench: oracle on a process pool", file=sys.stderr, flush=True)

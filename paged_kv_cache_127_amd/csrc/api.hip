@@ -133,17 +133,53 @@ int cu_count() {
   return v;
 }
 
+// Resident wavefronts per CU of a decode kernel configuration (the occupancy query costs
+// tens of microseconds of host time, so each configuration is asked once per device).
+int resident_waves_cached(bool mfma, int kv_dtype, int head_dim, int block_size, int G,
+                          int waves, int num_seqs) {
+  struct Key {
+    int dev, mfma, dt, d, b, g, w, s;
+    bool operator==(const Key& o) const {
+      return dev == o.dev && mfma == o.mfma && dt == o.dt && d == o.d && b == o.b && g == o.g &&
+             w == o.w && s == o.s;
+    }
+  };
+  static std::mutex mu;
+  static std::vector<std::pair<Key, int>> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const Key k{dev, mfma ? 1 : 0, kv_dtype, head_dim, block_size, G, waves, num_seqs};
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    for (auto& e : cache)
+      if (e.first == k) return e.second;
+  }
+  const int v = mfma ? pkv::decode_mfma_resident_waves(kv_dtype, head_dim, block_size, G, waves,
+                                                       num_seqs)
+                     : pkv::decode_valu_resident_waves(kv_dtype, head_dim, block_size, G, waves,
+                                                       num_seqs);
+  std::lock_guard<std::mutex> lk(mu);
+  if (cache.size() < 4096) cache.push_back({k, v});
+  return v;
+}
+
 int choose_workers(int num_workers) {
   return num_workers > 0 ? num_workers : pkv_decode_auto_workers();
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Schedule weight of a segment start relative to a step's 4 (a piece start costs about one
-// step of streaming time on gfx950); PAGEDKV_PIECE_WEIGHT overrides it for measurements.
+// Schedule weight of a segment start relative to a step's 4. With streaming (non-temporal)
+// key/value loads a piece start costs about a quarter of a step on gfx950: per-wavefront
+// timestamps on the GQA batch put a step at about 2 us and a piece start at no measurable
+// extra time, and of the weights 4, 2, 1 and 0, weight 1 gave the shortest decode at both
+// block sizes. PAGEDKV_PIECE_WEIGHT overrides it for measurements (read once per process).
 int piece_weight() {
-  const int v = env_int("PAGEDKV_PIECE_WEIGHT", 4);
-  return v < 0 ? 0 : (v > 64 ? 64 : v);
+  static const int v = [] {
+    const int x = env_int("PAGEDKV_PIECE_WEIGHT", 1);
+    return x < 0 ? 0 : (x > 64 ? 64 : x);
+  }();
+  return v;
 }
 
 struct WsLayout {
@@ -248,16 +284,14 @@ int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const v
                 num_seqs, pkv::kMaxSeqsPerCall);
   if (num_workers < 0 || num_workers > (1 << 20))
     return fail(PKV_ERR_INVALID_ARG, "%s: num_workers %d", fn, num_workers);
-  const int waves_env = env_int("PAGEDKV_DECODE_WAVES", 4);
+  static const int waves_env = env_int("PAGEDKV_DECODE_WAVES", 4);
   const int waves = (waves_env == 1 || waves_env == 2 || waves_env == 4) ? waves_env : 4;
   int n = num_workers;
   if (n == 0) {
     // every worker resident at once: the resident wavefronts per CU of the chosen kernel,
     // capped by the per-CU count the automatic workspace size assumes
-    int per_cu = use_mfma ? pkv::decode_mfma_resident_waves(kv_dtype, head_dim, block_size, G,
-                                                            waves, num_seqs)
-                          : pkv::decode_valu_resident_waves(kv_dtype, head_dim, block_size, G,
-                                                            waves, num_seqs);
+    int per_cu = resident_waves_cached(use_mfma, kv_dtype, head_dim, block_size, G, waves,
+                                       num_seqs);
     if (per_cu <= 0 || per_cu > kWorkersPerCU) per_cu = kWorkersPerCU;
     const int cus = cu_count();
     n = (cus > 0 ? cus : 256) * per_cu;

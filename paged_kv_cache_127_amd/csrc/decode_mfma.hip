@@ -156,13 +156,17 @@ void decode_mfma(DecodeParams p) {
   // piece's first step); the padding columns of the 16-wide tile repeat head G-1 and are never
   // stored.
   const int qrow = r16 < G ? r16 : G - 1;
+  // A step described past the end of the range is never computed: its lanes load the lane's
+  // own query row instead, a line the same step loads anyway, so no HBM bytes are spent on it.
+  // (Pointing the masked rows past a real step's valid tokens there as well made the 16-token
+  // block kernel slower on the GQA batch, 169 -> 174 us, so those rows are read as they are.)
+  auto qrow_addr = [&](const StepInfo& si) {
+    return qbase + (((size_t)si.s * p.num_q_heads + (size_t)si.g * G + qrow) * D + 8 * jg) * ES;
+  };
   auto load_kq = [&](StepRegs<D>& r, const StepInfo& si) {
-    {
-      const char* qp = qbase + (((size_t)si.s * p.num_q_heads + (size_t)si.g * G + qrow) * D +
-                                8 * jg) * ES;
+    const char* qp = qrow_addr(si);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) r.q[c] = load16(qp + 32 * c * ES);
-    }
+    for (int c = 0; c < NC; ++c) r.q[c] = load16(qp + 32 * c * ES);
     const int b0 = valid_block(si.b0, p.num_blocks) ? si.b0 : 0;   // out-of-range: block 0,
     const int b1 = valid_block(si.b1, p.num_blocks) ? si.b1 : 0;   // then poison
     const char* t0 = kbase + ((size_t)b0 * Hkv + si.g) * kv_block_stride;
@@ -176,10 +180,14 @@ void decode_mfma(DecodeParams p) {
       if (tokA0 == tn) ka = kn;
       if (tokA0 + 4 == tn) kb = kn;
     }
+    if (si.past) {
+      ka = qp;
+      kb = qp;
+    }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      r.k[0][c] = load16(ka + 32 * c * ES);
-      r.k[1][c] = load16(kb + 32 * c * ES);
+      r.k[0][c] = load16_stream(ka + 32 * c * ES);
+      r.k[1][c] = load16_stream(kb + 32 * c * ES);
     }
   };
   auto load_v = [&](StepRegs<D>& r, const StepInfo& si) {
@@ -187,6 +195,7 @@ void decode_mfma(DecodeParams p) {
     const int b1 = valid_block(si.b1, p.num_blocks) ? si.b1 : 0;
     const bool sub = p.k_new && si.k == si.ns - 1;   // fused append (see load_kq)
     const int tn = si.L - 1 - 32 * si.k;
+    const char* qp = qrow_addr(si);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int t = VTPI * f + vrow;
@@ -195,7 +204,8 @@ void decode_mfma(DecodeParams p) {
                       (size_t)(t & (B - 1)) * RB + 16 * vch;
       if (sub && t == tn)
         a = reinterpret_cast<const char*>(p.v_new) + ((size_t)si.s * Hkv + si.g) * RB + 16 * vch;
-      r.v[f] = load16(a);
+      if (si.past) a = qp;
+      r.v[f] = load16_stream(a);
     }
   };
 
@@ -370,10 +380,10 @@ void decode_mfma(DecodeParams p) {
   // Software pipeline over two register buffers: while step i computes, the loads of step
   // i + 1 are in flight and those of step i + 2 are issued into the parts of step i's buffer
   // that are consumed (inside compute_step); the block ids of the step after that are being
-  // fetched (scalar loads). Past
-  // the last step the stream repeats it (cache hits), which keeps every vector load
-  // unconditional. The loop runs over pairs of steps with its only exit at the bottom, so the
-  // compiler's wait counts stay exact; an odd last step is finished after it.
+  // fetched (scalar loads). Past the last step the stream repeats it, flagged past (its loads
+  // hit cached query lines), which keeps every vector load unconditional. The loop runs over
+  // pairs of steps with its only exit at the bottom, so the compiler's wait counts stay exact;
+  // an odd last step is finished after it.
   StepRegs<D> BA, BB;
   StepInfo sa = ss.next();
   StepInfo sb = ss.next();
@@ -395,7 +405,9 @@ void decode_mfma(DecodeParams p) {
   }
   if (nsteps & 1) {
     begin_step(sa);
-    compute_step(BA, sa, sa);   // its loads repeat this step's lines (cache hits, unused)
+    StepInfo none = sa;         // loads issued for no step: cached lines, never used
+    none.past = true;
+    compute_step(BA, sa, none);
   }
   flush(false);
 }

@@ -104,6 +104,12 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
     const bool sub = p.k_new && si.k == si.ns - 1;
     const int tn = si.L - 1 - 32 * si.k;
     const size_t nofs = ((size_t)si.s * Hkv + si.g) * D * ES + (size_t)ch * 16;
+    // rows at or past the step's valid tokens (every row of a step described past the end of
+    // the range) are masked out, so their lanes load the first query row's line, which this
+    // step loads anyway: no HBM bytes are spent on them
+    const int nvalid = si.past ? 0 : si.L - 32 * si.k;
+    const char* q0 = qbase + (((size_t)si.s * p.num_q_heads + (size_t)si.g * G) * D +
+                              (size_t)ch * EPC) * ES;
 #pragma unroll
     for (int c = 0; c < NI; ++c) {
       const int tt = TPI * c + row;
@@ -111,8 +117,11 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
       const size_t ofs = ((size_t)blk * Hkv + si.g) * blk_stride +
                          (size_t)(tt & (B - 1)) * D * ES + (size_t)ch * 16;
       const bool nw = sub && tt == tn;
-      r.k[c] = load16(nw ? reinterpret_cast<const char*>(p.k_new) + nofs : kbase + ofs);
-      r.v[c] = load16(nw ? reinterpret_cast<const char*>(p.v_new) + nofs : vbase + ofs);
+      const bool dead = tt >= nvalid;
+      const char* ka = nw ? reinterpret_cast<const char*>(p.k_new) + nofs : kbase + ofs;
+      const char* va = nw ? reinterpret_cast<const char*>(p.v_new) + nofs : vbase + ofs;
+      r.k[c] = load16_stream(dead ? q0 : ka);
+      r.v[c] = load16_stream(dead ? q0 : va);
     }
   };
 
@@ -249,9 +258,10 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
   // Software pipeline over two register buffers: while step i computes, the loads of step
   // i + 1 are in flight; the loads of step i + 2 are issued into the buffer step i has just
   // consumed, and the block ids of the step after that are being fetched (scalar loads). Past
-  // the last step the stream repeats it (cache hits), which keeps every vector load
-  // unconditional. The loop runs over pairs of steps with its only exit at the bottom, so the
-  // compiler's wait counts stay exact; an odd last step is finished after it.
+  // the last step the stream repeats it, flagged past (its loads hit cached query lines), which
+  // keeps every vector load unconditional. The loop runs over pairs of steps with its only exit
+  // at the bottom, so the compiler's wait counts stay exact; an odd last step is finished after
+  // it.
   Regs RA, RB;
   StepInfo sa = ss.next();
   StepInfo sb = ss.next();

@@ -207,6 +207,7 @@ struct StepInfo {
   int range;        // the worker (its partial slots are 2*range, 2*range+1)
   bool rfirst;      // first step of the worker's range
   bool rlast;       // last step of the worker's range
+  bool past;        // described past the end of the range (its loads are never used)
 };
 
 // Wave-uniform position in the step line: segment (s, g), step k of ns, sequence length L.
@@ -251,9 +252,9 @@ __device__ __forceinline__ bool valid_block(int b, int num_blocks) {
 // Describes the steps of one worker's range [b0, end) in order. next() returns the current
 // step's description -- with its physical block ids fetched by scalar loads from the table row
 // (raw: they are checked where they are used, so the loads' latency is hidden) -- and moves the
-// cursor on; past the end of the range it keeps describing the last step. A step whose tokens
-// all sit in its first block (block size 16) gets that block for its second half too: the
-// masked loads then re-read lines the first half fetches.
+// cursor on; past the end of the range it keeps describing the last step, flagged `past` (the
+// kernels point such a step's key/value loads at cached lines). A step whose tokens all sit in
+// its first block (block size 16) gets that block for its second half too.
 template <int B>
 struct StepStream {
   const int64_t* sm_prefix;
@@ -289,6 +290,7 @@ struct StepStream {
     si.range = w;
     si.rfirst = j == b0;
     si.rlast = j == end - 1;
+    si.past = j >= end;
     ++j;
     if (j < end) cursor_next(c, sm_prefix, sm_len, S, Hkv);
     return si;
