@@ -128,6 +128,28 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * paged_attn_decode without a caller workspace, for callers that cannot allocate device
+ * memory at the call site: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. The same kernels and the same result, bit for bit, as paged_attn_decode
+ * with the same arguments and num_workers; the decode's scratch (schedule prefixes and split
+ * partial states) lives in a static device array of the library, PKV_DECODE_STATIC_SCRATCH
+ * bytes on each GPU, held from the first call on that GPU until the process ends. The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine). A call whose
+ * scratch need, pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+ * num_workers), exceeds that size fails with PKV_ERR_WORKSPACE_TOO_SMALL before enqueuing
+ * anything. Every call on one GPU shares that GPU's array and leaves its contents behind:
+ * calls that overlap in time on one GPU (other streams, other host threads) race and must be
+ * serialized by the caller.
+ * --------------------------------------------------------------------------------------- */
+#define PKV_DECODE_STATIC_SCRATCH ((size_t)32 << 20)
+int paged_attn_decode_noalloc(void* out, int out_dtype, const void* q, const void* k_pool,
+                              const void* v_pool, int kv_dtype, const int32_t* block_tables,
+                              int max_blocks_per_seq, const int32_t* context_lens,
+                              int max_context_len, int num_seqs, int num_q_heads,
+                              int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                              float scale, int num_workers, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Decode step with the step's append fused in: the same result, in the pools and in `out`,
  * as kv_cache_append of one token per sequence -- k_new[s] / v_new[s] at position
  * context_lens[s] - 1, for every s with context_lens[s] >= 1 -- followed by

@@ -16,7 +16,8 @@ import torch  # loaded first: the library then binds to the HIP runtime torch al
 __all__ = [
     "PagedKVError", "paged_attn_decode", "paged_attn_decode_append", "kv_cache_append",
     "cow_block_copy", "kv_swap_out", "kv_swap_in", "paged_attn_decode_shared_prefix",
-    "shared_prefix_workspace", "paged_attn_extend", "extend_workspace", "pkv_decode_workspace_size", "decode_workspace",
+    "shared_prefix_workspace", "paged_attn_extend", "paged_attn_decode_noalloc",
+    "DECODE_STATIC_SCRATCH", "extend_workspace", "pkv_decode_workspace_size", "decode_workspace",
     "pkv_decode_auto_workers", "BlockPool", "timing_enable", "timing_query",
     "stream_read_probe", "mfma_rate_probe", "set_validate", "library_path", "load_library", "PKV_F32", "PKV_F16",
     "PKV_BF16", "PrefixIndex",
@@ -57,6 +58,9 @@ def _declare(L):
         "paged_attn_decode": (c_int, [c_void, c_int, c_void, c_void, c_void, c_int, c_void, c_int,
                                       c_void, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                       c_float, c_int, c_void, c_size, c_void]),
+        "paged_attn_decode_noalloc": (c_int, [c_void, c_int, c_void, c_void, c_void, c_int,
+                                              c_void, c_int, c_void, c_int, c_int, c_int, c_int,
+                                              c_int, c_int, c_int, c_float, c_int, c_void]),
         "paged_attn_decode_append": (c_int, [c_void, c_int, c_void, c_void, c_void, c_int, c_void,
                                              c_void, c_void, c_int, c_void, c_int, c_int, c_int,
                                              c_int, c_int, c_int, c_int, c_float, c_int, c_void,
@@ -287,6 +291,37 @@ def paged_attn_extend(out: torch.Tensor, q: torch.Tensor, query_start: torch.Ten
         _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, d, B,
         N, float(scale), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+DECODE_STATIC_SCRATCH = 32 << 20   # bytes of the library's static decode scratch per GPU
+
+
+def paged_attn_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
+                              v_pool: torch.Tensor, block_tables: torch.Tensor,
+                              context_lens: torch.Tensor, max_context_len: int,
+                              scale: float = 0.0, num_workers: int = 0,
+                              stream=None) -> torch.Tensor:
+    """paged_attn_decode with the library's static scratch in place of a workspace (C:
+    ``paged_attn_decode_noalloc``): nothing is allocated. Calls that overlap on one GPU race."""
+    L = load_library()
+    kdt = _kv_dtype(k_pool)
+    if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape or out.shape != q.shape:
+        raise ValueError("bad tensor ranks or out shape; k_pool and v_pool must match")
+    S, Hq, d = q.shape
+    N, Hkv, B, d2 = k_pool.shape
+    if d2 != d:
+        raise ValueError("q and the pools disagree on head_dim")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+        raise ValueError("block_tables must be [S][max_blocks] and context_lens [S]")
+    if out.dtype not in (torch.float32, k_pool.dtype):
+        raise TypeError("out must be float32 or the cache dtype")
+    _check(L.paged_attn_decode_noalloc(
+        _dev(out, "out"), _DT[out.dtype], _dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool", k_pool.dtype), kdt, _dev(block_tables, "block_tables", torch.int32),
+        int(block_tables.shape[1]), _dev(context_lens, "context_lens", torch.int32),
+        int(max_context_len), S, Hq, Hkv, d, B, N, float(scale), int(num_workers),
+        _stream(stream)))
     return out
 
 

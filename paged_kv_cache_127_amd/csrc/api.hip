@@ -413,6 +413,69 @@ int paged_attn_decode(void* out, int out_dtype, const void* q, const void* k_poo
                      num_workers, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+// Scratch of paged_attn_decode_noalloc: a static device array (one copy per GPU, zero at
+// load, held until the process ends). Host code never uses the array's name as an address:
+// its device address is looked up once per device, with that device current, and kept.
+static __device__ __align__(256) unsigned char scratch[PKV_DECODE_STATIC_SCRATCH];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, or nullptr (error message set).
+void* scratch_address(const char* fn) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    fail(PKV_ERR_LAUNCH, "%s: no usable current device", fn);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      fail(PKV_ERR_LAUNCH, "%s: hipGetSymbolAddress of the static scratch: %s", fn,
+           hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode_noalloc(void* out, int out_dtype, const void* q, const void* k_pool,
+                              const void* v_pool, int kv_dtype, const int32_t* block_tables,
+                              int max_blocks_per_seq, const int32_t* context_lens,
+                              int max_context_len, int num_seqs, int num_q_heads,
+                              int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                              float scale, int num_workers, void* stream) {
+  const char* fn = "paged_attn_decode_noalloc";
+  if (num_seqs == 0) return ok();
+  if (num_seqs > 0 && num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 &&
+      head_dim > 0 && num_workers >= 0) {
+    const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                  num_workers);
+    if (need > PKV_DECODE_STATIC_SCRATCH)
+      return fail(PKV_ERR_WORKSPACE_TOO_SMALL,
+                  "%s: the call needs %zu bytes of scratch, the static array holds %zu", fn,
+                  need, (size_t)PKV_DECODE_STATIC_SCRATCH);
+  }
+  void* ws = scratch_address(fn);
+  if (!ws) return PKV_ERR_LAUNCH;
+  return decode_impl(fn, out, out_dtype, q, k_pool, v_pool, kv_dtype, nullptr, nullptr,
+                     block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                     num_workers, ws, PKV_DECODE_STATIC_SCRATCH, stream);
+}
+
 int paged_attn_decode_append(void* out, int out_dtype, const void* q, void* k_pool, void* v_pool,
                              int kv_dtype, const void* k_new, const void* v_new,
                              const int32_t* block_tables, int max_blocks_per_seq,

@@ -230,3 +230,16 @@ def test_mfma_probe_argument_checks():
     assert L.pkv_mfma_rate_probe(4, 10, None, None) == -1
     assert L.pkv_mfma_rate_probe(0, 10, 0x1000, None) == -1
     assert L.pkv_mfma_rate_probe(4, 0, 0x1000, None) == -1
+
+
+def test_noalloc_rejects_calls_beyond_the_static_scratch():
+    """A call whose scratch need exceeds the static array fails before anything is enqueued
+    (host-side check; no device is touched)."""
+    L = pkv.load_library()
+    need = L.pkv_decode_workspace_size(64, 64, 8, 128, 1 << 20)
+    assert need > pkv.DECODE_STATIC_SCRATCH
+    fake = 1 << 40
+    rc = L.paged_attn_decode_noalloc(fake, 0, fake, fake, fake, 2, fake, 8, fake, 128, 64, 64, 8,
+                                     128, 16, 100, 0.0, 1 << 20, None)
+    assert rc == -3
+    assert b"static array" in L.pkv_last_error()
