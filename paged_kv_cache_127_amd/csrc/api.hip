@@ -359,6 +359,9 @@ int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const v
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim);
   p.scale_log2 = sc * 1.4426950408889634f;
   p.piece_weight = pw;
+  // streaming key/value loads for a decode that reads its blocks once; the suffix decode of the
+  // shared-prefix call (short segments right after the prefix pass) runs faster with plain ones
+  p.stream_loads = (pf && use_mfma && waves == 4) ? 0 : 1;
   p.ring_cap = pkv::ring_capacity(num_seqs, G, head_dim, waves);
   char* ws = reinterpret_cast<char*>(workspace);
   p.wprefix = reinterpret_cast<int64_t*>(ws + wl.wprefix);

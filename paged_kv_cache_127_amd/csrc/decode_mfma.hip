@@ -50,7 +50,11 @@ struct StepRegs {
 
 // At least PKV_MFMA_WAVES_PER_EU resident wavefronts per SIMD: the compiler keeps the whole
 // state (two steps of K/V/Q operands, accumulators) within that register budget.
-template <typename T, int D, int B, int W>
+// STREAM: key/value rows through streaming (non-temporal) loads -- the choice for a decode that
+// reads its blocks once (GQA batch: 168 vs 177 us); plain loads when blocks are re-read from
+// the caches within the call (128 sequences over a shared 800-token prefix: 66 us plain vs
+// 94 us streaming; the suffix decode of the shared-prefix call: 40 vs 43 us).
+template <typename T, int D, int B, int W, bool STREAM = true>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES_PER_EU)))
 void decode_mfma(DecodeParams p) {
   static_assert(B == 16 || B == 32, "block size");
@@ -186,8 +190,8 @@ void decode_mfma(DecodeParams p) {
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      r.k[0][c] = load16_stream(ka + 32 * c * ES);
-      r.k[1][c] = load16_stream(kb + 32 * c * ES);
+      r.k[0][c] = STREAM ? load16_stream(ka + 32 * c * ES) : load16(ka + 32 * c * ES);
+      r.k[1][c] = STREAM ? load16_stream(kb + 32 * c * ES) : load16(kb + 32 * c * ES);
     }
   };
   auto load_v = [&](StepRegs<D>& r, const StepInfo& si) {
@@ -205,7 +209,7 @@ void decode_mfma(DecodeParams p) {
       if (sub && t == tn)
         a = reinterpret_cast<const char*>(p.v_new) + ((size_t)si.s * Hkv + si.g) * RB + 16 * vch;
       if (si.past) a = qp;
-      r.v[f] = load16_stream(a);
+      r.v[f] = STREAM ? load16_stream(a) : load16(a);
     }
   };
 
@@ -448,7 +452,12 @@ static hipError_t launch_t(const DecodeParams& p, int waves, hipStream_t st) {
   switch (waves) {
     case 1: hipLaunchKernelGGL((decode_mfma<T, D, B, 1>), dim3(grid), dim3(64), lds, st, p); break;
     case 2: hipLaunchKernelGGL((decode_mfma<T, D, B, 2>), dim3(grid), dim3(128), lds, st, p); break;
-    case 4: hipLaunchKernelGGL((decode_mfma<T, D, B, 4>), dim3(grid), dim3(256), lds, st, p); break;
+    case 4:
+      if (p.stream_loads)
+        hipLaunchKernelGGL((decode_mfma<T, D, B, 4>), dim3(grid), dim3(256), lds, st, p);
+      else
+        hipLaunchKernelGGL((decode_mfma<T, D, B, 4, false>), dim3(grid), dim3(256), lds, st, p);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

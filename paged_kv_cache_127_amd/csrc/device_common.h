@@ -177,6 +177,9 @@ struct DecodeParams {
   int block_size;
   int num_workers;     // wavefronts of the decode kernel
   int piece_weight;    // schedule weight of a segment start (a step weighs 4)
+  int stream_loads;    // 1: key/value rows through streaming loads (read once); 0: plain
+                       // loads (blocks re-read from the caches; matrix-core kernel with four
+                       // wavefronts per workgroup only)
   int ring_cap;        // staged piece results per wavefront (matrix-core kernel)
   float scale_log2;    // softmax scale * log2(e)
 };
