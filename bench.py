@@ -608,13 +608,94 @@ def headline_workload(name, block_size, W, torch, dev):
     return b, desc, append
 
 
+def row_state_line(args, pkv, W, torch, dev):
+    """One JSON line for a row-state call alone (for profiling the matrix-core kernel):
+    prefix800 / prefix4096 -- paged_attn_decode_shared_prefix on 128 sequences over an 800- or
+    4096-token shared prefix (the prefix-state kernel, the suffix decode and the merge);
+    prefill -- paged_attn_extend of a 256-token chunk on 8 sequences of 1024..4096 tokens;
+    verify -- paged_attn_extend of the last 4 tokens of every sequence of the GQA batch.
+    ``value`` is the call's causal-attention rate in TFLOP/s (prefix: the prefix-state kernel's
+    flops over the whole call)."""
+    import numpy as np
+    if args.workload.startswith("prefix"):
+        P = int(args.workload[6:])
+        b = W.config4a(prefix_len=P)
+        S, Hq, d = b.q.shape
+        q, kp, vp = b.q.to(dev), b.k_pool.to(dev), b.v_pool.to(dev)
+        tab, lens = torch.from_numpy(b.tables).to(dev), torch.from_numpy(b.lengths).to(dev)
+        mx = int(b.lengths.max())
+        out = torch.empty(S, Hq, d, dtype=torch.float32, device=dev)
+        pre = tab[0, :P // b.block_size].contiguous()
+        ws = pkv.shared_prefix_workspace(S, Hq, b.num_kv_heads, d, P, args.workers, dev)
+
+        def call():
+            pkv.paged_attn_decode_shared_prefix(out, q, kp, vp, pre, P, tab, lens, mx,
+                                                num_workers=args.workers, workspace=ws)
+        kname = "prefix_states"
+        flops = 4 * S * Hq * d * P
+        desc = (f"shared prefix: 128 sequences, {P}-token shared prefix + U{{1..512}} private "
+                "tokens, 64/8 heads, head_dim 128, bf16, block size 16; one "
+                "paged_attn_decode_shared_prefix call per step")
+    else:
+        if args.workload == "prefill":
+            b = W.small_batch(W.rng_for(W.SEED_BASE + 9, 0).integers(1024, 4096, size=8,
+                                                                    endpoint=True),
+                              64, 8, 128, 16, torch.bfloat16, seed=W.SEED_BASE + 9)
+            new = np.full(8, 256)
+            seed, desc = 72, ("prefill chunk: 8 sequences of 1024..4096 stored tokens (64/8 heads, "
+                              "d 128, bf16, B 16), the last 256 of each new; one paged_attn_extend "
+                              "call per step")
+        else:
+            b = W.config3(16)
+            new = np.minimum(4, b.lengths)
+            seed, desc = 71, ("speculative verification: the GQA decode batch, the last 4 stored "
+                              "tokens of each sequence as new query tokens; one paged_attn_extend "
+                              "call per step")
+        qn, start = W.extend_queries(b, new, seed=seed)
+        qd, sd = qn.to(dev), torch.from_numpy(start).to(dev)
+        kp, vp = b.k_pool.to(dev), b.v_pool.to(dev)
+        tab, lens = torch.from_numpy(b.tables).to(dev), torch.from_numpy(b.lengths).to(dev)
+        mx, maxq = int(b.lengths.max()), int(np.max(new))
+        out = torch.empty(qd.shape, dtype=torch.float32, device=dev)
+        ws = pkv.extend_workspace(b.num_seqs, qd.shape[0], b.num_q_heads, b.num_kv_heads,
+                                  b.head_dim, maxq, mx, dev)
+
+        def call():
+            pkv.paged_attn_extend(out, qd, sd, maxq, kp, vp, tab, lens, mx, workspace=ws)
+        kname = "extend_states"
+        att = sum(int(n) * (2 * int(L) - int(n) + 1) // 2 for L, n in zip(b.lengths, new))
+        flops = 4 * att * b.num_q_heads * b.head_dim
+    kt = kernel_loop(pkv, torch, call, (kname,), args.kernel_launches)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kus = kt[kname][0]
+    print(json.dumps({
+        "metric": "row-state call time (matrix-core kernel)", "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": desc, "flops_per_step": flops},
+        "kernel": {"name": kname, "avg_us": round(kus, 3), "launches": kt[kname][1],
+                   "tflops": round(flops / (kus * 1e-6) / 1e12, 2),
+                   "frac_of_dense_bf16_peak": round(flops / (kus * 1e-6) / 2.5e15, 4)}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="gqa", choices=("gqa", "mha", "long"),
-                    help="batch of the headline line (gqa is the graded one)")
+    ap.add_argument("--workload", default="gqa",
+                    choices=("gqa", "mha", "long", "prefix800", "prefix4096", "prefill", "verify"),
+                    help="batch of the headline line (gqa is the graded one; the last four run "
+                         "the matrix-core row-state calls alone, for profiling them)")
     ap.add_argument("--block-size", type=int, default=16, choices=(16, 32))
     ap.add_argument("--workers", type=int, default=0, help="decode wavefronts (0 = automatic)")
     ap.add_argument("--kernel-launches", type=int, default=KERNEL_LAUNCHES,
@@ -642,6 +723,9 @@ def main():
     import workloads as W
 
     dev = "cuda:0"
+    if args.workload in ("prefix800", "prefix4096", "prefill", "verify"):
+        row_state_line(args, pkv, W, torch, dev)
+        return
     t_gen = time.perf_counter()
     b, desc, fused_append = headline_workload(args.workload, args.block_size, W, torch, dev)
     S, Hq, Hkv, d = b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim
