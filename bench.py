@@ -32,6 +32,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 KERNEL_LAUNCHES = 100
+# untimed steps before any timing: the first ~60 decode launches of a process run 176-182 us and
+# later ones settle at ~165 us (rocprofv3 kernel traces), so the device is brought to that state
+DEVICE_WARMUP_STEPS = 100
 METRIC = "paged decode attention KV GB/s (fraction of HBM peak) and seq-steps/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_mfma_gqa256_b16_traffic.json")
 KERNEL_SOURCES = ["paged_kv_cache_127_amd/csrc/decode_mfma.hip",
@@ -665,6 +668,9 @@ def row_state_line(args, pkv, W, torch, dev):
         kname = "extend_states"
         att = sum(int(n) * (2 * int(L) - int(n) + 1) // 2 for L, n in zip(b.lengths, new))
         flops = 4 * att * b.num_q_heads * b.head_dim
+    for _ in range(DEVICE_WARMUP_STEPS):
+        call()
+    torch.cuda.synchronize()
     kt = kernel_loop(pkv, torch, call, (kname,), args.kernel_launches)
     for _ in range(args.warmup):
         call()
@@ -767,9 +773,12 @@ def main():
         pkv.paged_attn_decode(out, q, k_pool, v_pool, tables, lens, max_ctx,
                               num_workers=args.workers, workspace=ws)
 
-    # kernel durations first: a dedicated loop of its own (independent of --steps), hipEvents
-    # the library records on the launch stream around every launch of each kernel; it also
-    # brings the device up to speed before the timed steps
+    # the device to its steady state first (untimed), then the kernel durations: a dedicated
+    # loop of its own (independent of --steps), hipEvents stamped with each launch's own start
+    # and end by the library, on the launch stream
+    for _ in range(DEVICE_WARMUP_STEPS):
+        step()
+    torch.cuda.synchronize()
     kt = kernel_loop(pkv, torch, step, ("decode_partial", "splitk_reduce"), args.kernel_launches)
     kern_avg_us, kernel_n = kt["decode_partial"]
     reduce_us, _ = kt["splitk_reduce"]
@@ -856,9 +865,10 @@ def main():
             "traffic": traffic,
             "avg_kernel_us": round(kern_avg_us, 3),
             "timed_launches": kernel_n,
-            "timing": (f"hipEvents around each of {kernel_n} launches in a dedicated loop before "
-                       "the warm-up and timed steps; the headline steps ran with the library's "
-                       "timing off"),
+            "timing": (f"hipEvents stamped with the kernel's own start and end "
+                       f"(hipExtLaunchKernelGGL) for each of {kernel_n} launches in a dedicated loop, "
+                       f"after {DEVICE_WARMUP_STEPS} untimed steps and before the warm-up and timed "
+                       "steps; the headline steps ran with the library's timing off"),
         },
         "other_kernels_avg_us": {"splitk_reduce": round(reduce_us, 3)},
         "setup_s": round(gen_s, 2),

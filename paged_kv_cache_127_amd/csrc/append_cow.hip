@@ -84,11 +84,11 @@ hipError_t launch_append(const AppendParams& p, int elem_bytes, hipStream_t st) 
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (wide)
-    hipLaunchKernelGGL(append_kernel<u32x4>, dim3((unsigned)blocks), dim3(256), 0, st, p, units);
+    launch_kernel(append_kernel<u32x4>, dim3((unsigned)blocks), dim3(256), 0, st, p, units);
   else if (elem_bytes == 4)
-    hipLaunchKernelGGL(append_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, st, p, units);
+    launch_kernel(append_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, st, p, units);
   else
-    hipLaunchKernelGGL(append_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st, p, units);
+    launch_kernel(append_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st, p, units);
   return hipGetLastError();
 }
 
@@ -96,9 +96,9 @@ hipError_t launch_cow(const CowParams& p, int elem_bytes, hipStream_t st) {
   const int64_t grid = (int64_t)p.num_pairs * p.num_kv_heads;
   if (grid <= 0) return hipSuccess;
   if (elem_bytes == 4)
-    hipLaunchKernelGGL(cow_kernel<uint32_t>, dim3((unsigned)grid), dim3(256), 0, st, p);
+    launch_kernel(cow_kernel<uint32_t>, dim3((unsigned)grid), dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL(cow_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, st, p);
+    launch_kernel(cow_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

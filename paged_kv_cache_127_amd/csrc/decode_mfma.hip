@@ -450,13 +450,13 @@ static hipError_t launch_t(const DecodeParams& p, int waves, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   const size_t lds = mfma_lds_bytes(p.num_seqs, p.num_q_heads / p.num_kv_heads, D, waves);
   switch (waves) {
-    case 1: hipLaunchKernelGGL((decode_mfma<T, D, B, 1>), dim3(grid), dim3(64), lds, st, p); break;
-    case 2: hipLaunchKernelGGL((decode_mfma<T, D, B, 2>), dim3(grid), dim3(128), lds, st, p); break;
+    case 1: launch_kernel((decode_mfma<T, D, B, 1>), dim3(grid), dim3(64), lds, st, p); break;
+    case 2: launch_kernel((decode_mfma<T, D, B, 2>), dim3(grid), dim3(128), lds, st, p); break;
     case 4:
       if (p.stream_loads)
-        hipLaunchKernelGGL((decode_mfma<T, D, B, 4>), dim3(grid), dim3(256), lds, st, p);
+        launch_kernel((decode_mfma<T, D, B, 4>), dim3(grid), dim3(256), lds, st, p);
       else
-        hipLaunchKernelGGL((decode_mfma<T, D, B, 4, false>), dim3(grid), dim3(256), lds, st, p);
+        launch_kernel((decode_mfma<T, D, B, 4, false>), dim3(grid), dim3(256), lds, st, p);
       break;
     default: return hipErrorInvalidValue;
   }

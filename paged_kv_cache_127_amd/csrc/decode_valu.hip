@@ -335,9 +335,9 @@ static hipError_t launch_g(const DecodeParams& p, int waves, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   const size_t lds = decode_lds_bytes(p.num_seqs);
   switch (waves) {
-    case 1: hipLaunchKernelGGL((decode_valu<T, D, B, G, 1>), dim3(grid), dim3(64), lds, st, p); break;
-    case 2: hipLaunchKernelGGL((decode_valu<T, D, B, G, 2>), dim3(grid), dim3(128), lds, st, p); break;
-    case 4: hipLaunchKernelGGL((decode_valu<T, D, B, G, 4>), dim3(grid), dim3(256), lds, st, p); break;
+    case 1: launch_kernel((decode_valu<T, D, B, G, 1>), dim3(grid), dim3(64), lds, st, p); break;
+    case 2: launch_kernel((decode_valu<T, D, B, G, 2>), dim3(grid), dim3(128), lds, st, p); break;
+    case 4: launch_kernel((decode_valu<T, D, B, G, 4>), dim3(grid), dim3(256), lds, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -1,6 +1,7 @@
 // Internal launch interface between the C-ABI layer and the kernel translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -8,6 +9,29 @@
 #include "schedule.h"
 
 namespace pkv {
+
+// Kernel launches. When the library's timing layer has armed a pair of events for the calling
+// thread, the next launch goes through hipExtLaunchKernelGGL, which stamps those events with the
+// kernel's own start and end (the dispatch's timestamps, as a kernel-trace profiler reports
+// them) instead of separate event packets around the launch; otherwise a plain launch.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+  bool used = false;
+};
+LaunchEvents& launch_events();   // per host thread (api.hip)
+
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds,
+                          hipStream_t st, Args... args) {
+  LaunchEvents& ev = launch_events();
+  if (ev.start && !ev.used) {
+    ev.used = true;
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, ev.start, ev.stop, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+  }
+}
 
 // Decode over the balanced step schedule (schedule.h). kv_dtype: 0 f32, 1 f16, 2 bf16.
 hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, int head_dim, int block_size,

@@ -42,7 +42,7 @@ hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int
   const int64_t n16 = (int64_t)(bytes / 16);
   if (n16 <= 0) return hipSuccess;
   const int blocks = (num_cus > 0 ? num_cus : 256) * 32;
-  hipLaunchKernelGGL(stream_read, dim3(blocks), dim3(256), 0, st,
+  launch_kernel(stream_read, dim3(blocks), dim3(256), 0, st,
                      reinterpret_cast<const u32x4*>(src), n16, sink);
   return hipGetLastError();
 }
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void mfma_rate(int iters, float* sink) {
 
 hipError_t launch_mfma_rate(int workgroups, int iters, float* sink, hipStream_t st) {
   if (workgroups <= 0 || iters <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mfma_rate, dim3(workgroups), dim3(256), 0, st, iters, sink);
+  launch_kernel(mfma_rate, dim3(workgroups), dim3(256), 0, st, iters, sink);
   return hipGetLastError();
 }
 

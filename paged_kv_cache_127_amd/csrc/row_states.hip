@@ -49,17 +49,26 @@ constexpr int kMaxStepsPerWave = 32;  // planned 32-token steps of one wavefront
 constexpr int kMaxChunkGroups = 16;   // states per row
 constexpr int kMinExtendSteps = 8;    // extend mode: fewest 32-token steps a wavefront is given
 
-// Two fp32 probabilities (in [0, 1]) as packed 16-bit high parts and remainders. bf16: the high
-// part is the fp32 value truncated to its upper half (one AND), so the remainder p - hi is exact
-// and is rounded once; |hi + lo - p| <= 2^-17 p. fp16 keeps the rounding split.
+// Lazy softmax reference: the exponents of a row use its running reference m unless a step's
+// maximum exceeds m by more than this (log2 domain), so probabilities stay below 2^8 -- harmless
+// in fp32 and in the 16-bit split -- and the accumulators are rescaled only on those rare steps.
+constexpr float kLazyRescale = 8.f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 probabilities as packed 16-bit high parts and remainders. bf16: the high part is the
+// fp32 value truncated to its upper half (one AND each, packed by one byte permute), so the
+// remainder p - hi is exact and is rounded once (both remainders by one packed conversion);
+// |hi + lo - p| <= 2^-17 p. fp16 keeps the rounding split.
 template <typename T>
 __device__ __forceinline__ void split_hi_lo(float p0, float p1, uint32_t& hi, uint32_t& lo) {
   if constexpr (__is_same(T, bf16_t)) {
     const uint32_t u0 = __float_as_uint(p0) & 0xffff0000u;
     const uint32_t u1 = __float_as_uint(p1) & 0xffff0000u;
-    hi = (u0 >> 16) | u1;
-    lo = (uint32_t)Elem<T>::from_f32(p0 - __uint_as_float(u0)) |
-         ((uint32_t)Elem<T>::from_f32(p1 - __uint_as_float(u1)) << 16);
+    hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);   // u0's upper half low, u1's high
+    const f32x2_t r = f32x2_t{p0 - __uint_as_float(u0), p1 - __uint_as_float(u1)};
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
   } else {
     split_pair<T>(p0, p1, hi, lo);
   }
@@ -337,28 +346,31 @@ void row_states(RowStateParams p) {
       }
 #pragma unroll
       for (int rb = 0; rb < RBK; ++rb) {
+        // raw scores; masked tokens -inf (the scale is positive, so the row maximum of the
+        // raw scores, scaled, is the maximum of the scaled ones)
         float z[8];
         if (32 * k + 32 <= lim_min) {   // every token of the step counts for every row
 #pragma unroll
           for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) z[4 * a + e] = sacc[rb][a][e] * p.scale_log2;
+            for (int e = 0; e < 4; ++e) z[4 * a + e] = sacc[rb][a][e];
         } else {
 #pragma unroll
           for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int tok = vtok + 4 * a + e;
-              z[4 * a + e] = (tok < nvalid && 32 * k + tok < lim[rb])
-                                 ? sacc[rb][a][e] * p.scale_log2
-                                 : kNegInf;
+              z[4 * a + e] = (tok < nvalid && 32 * k + tok < lim[rb]) ? sacc[rb][a][e] : kNegInf;
             }
         }
         float mx = z[0];
 #pragma unroll
         for (int t = 1; t < 8; ++t) mx = fmaxf(mx, z[t]);
-        mx = rows_max(mx);
-        const float m_new = fmaxf(m_run[rb], mx);
+        const float m_step = rows_max(mx) * p.scale_log2;
+        // the reference moves only when this step's maximum exceeds it by more than
+        // kLazyRescale (a first finite maximum always moves it); otherwise alpha is exactly 1
+        const bool upd = m_step > m_run[rb] + kLazyRescale;
+        const float m_new = upd ? m_step : m_run[rb];
         // a row with nothing to attend yet (causal limit) keeps (-inf, 0, 0): exponents
         // against 0 instead of -inf, so that no -inf - -inf appears
         const float m_ref = m_new == kNegInf ? 0.f : m_new;
@@ -367,13 +379,11 @@ void row_states(RowStateParams p) {
         float ps = 0.f;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          pr[t] = fast_exp2(z[t] - m_ref);
+          pr[t] = fast_exp2(fmaf(z[t], p.scale_log2, -m_ref));
           ps += pr[t];
         }
         l_run[rb] = l_run[rb] * alpha + ps;
-        // the accumulators need rescaling only when some row's maximum moved (alpha is then
-        // exactly 1 everywhere else, and most steps move no maximum)
-        const bool moved = __builtin_amdgcn_ballot_w64(m_new != m_run[rb]) != 0;
+        const bool moved = __builtin_amdgcn_ballot_w64(upd) != 0;
         m_run[rb] = m_new;
         u32x4 phi, plo;
 #pragma unroll
@@ -532,7 +542,7 @@ int64_t row_groups(int64_t rows) { return (rows + 16 * kRowsRB - 1) / (16 * kRow
 
 template <typename T, int D, int B>
 static void launch_rows_tdb(const RowStateParams& p, int64_t grid, hipStream_t st) {
-  hipLaunchKernelGGL((row_states<T, D, B, kRowsRB>), dim3((unsigned)grid), dim3(64 * kRowWaves),
+  launch_kernel((row_states<T, D, B, kRowsRB>), dim3((unsigned)grid), dim3(64 * kRowWaves),
                      0, st, p);
 }
 
@@ -570,11 +580,11 @@ static void launch_finish_t(const ExtendFinishParams& p, hipStream_t st) {
   const int64_t chunks = (int64_t)p.rows * (D / 4);
   const dim3 grid((unsigned)((chunks + 255) / 256)), blk(256);
   const int C = p.chunk_groups;
-  if (C <= 1) hipLaunchKernelGGL((extend_finish<D, T, 1>), grid, blk, 0, st, p);
-  else if (C <= 2) hipLaunchKernelGGL((extend_finish<D, T, 2>), grid, blk, 0, st, p);
-  else if (C <= 4) hipLaunchKernelGGL((extend_finish<D, T, 4>), grid, blk, 0, st, p);
-  else if (C <= 8) hipLaunchKernelGGL((extend_finish<D, T, 8>), grid, blk, 0, st, p);
-  else hipLaunchKernelGGL((extend_finish<D, T, 16>), grid, blk, 0, st, p);
+  if (C <= 1) launch_kernel((extend_finish<D, T, 1>), grid, blk, 0, st, p);
+  else if (C <= 2) launch_kernel((extend_finish<D, T, 2>), grid, blk, 0, st, p);
+  else if (C <= 4) launch_kernel((extend_finish<D, T, 4>), grid, blk, 0, st, p);
+  else if (C <= 8) launch_kernel((extend_finish<D, T, 8>), grid, blk, 0, st, p);
+  else launch_kernel((extend_finish<D, T, 16>), grid, blk, 0, st, p);
 }
 
 hipError_t launch_extend_finish(const ExtendFinishParams& p, int kv_dtype, int head_dim,

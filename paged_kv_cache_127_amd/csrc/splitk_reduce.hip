@@ -293,13 +293,13 @@ static void launch_merge_w(const DecodeParams& p, hipStream_t st) {
   const dim3 grid((unsigned)((segs * WPS + 3) / 4)), blk(256);
   const int chunks = (p.num_q_heads / p.num_kv_heads * D / 4 + 63) / 64;
   if (chunks <= 1)
-    hipLaunchKernelGGL((splitk_merge<D, T, 1, WPS>), grid, blk, 0, st, p);
+    launch_kernel((splitk_merge<D, T, 1, WPS>), grid, blk, 0, st, p);
   else if (chunks <= 2)
-    hipLaunchKernelGGL((splitk_merge<D, T, 2, WPS>), grid, blk, 0, st, p);
+    launch_kernel((splitk_merge<D, T, 2, WPS>), grid, blk, 0, st, p);
   else if (chunks <= 4)
-    hipLaunchKernelGGL((splitk_merge<D, T, 4, WPS>), grid, blk, 0, st, p);
+    launch_kernel((splitk_merge<D, T, 4, WPS>), grid, blk, 0, st, p);
   else
-    hipLaunchKernelGGL((splitk_merge<D, T, 8, WPS>), grid, blk, 0, st, p);
+    launch_kernel((splitk_merge<D, T, 8, WPS>), grid, blk, 0, st, p);
 }
 
 // Fewer segments than workers means every segment spans several ranges on average: four

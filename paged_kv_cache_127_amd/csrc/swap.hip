@@ -79,7 +79,7 @@ hipError_t launch_block_copy(const SwapParams& p, int num_cus, hipStream_t st) {
   const int64_t items = (int64_t)p.num_pairs * chunks;
   if (items >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int grid = (int)std::min<int64_t>(items, std::max(num_cus, 1));
-  hipLaunchKernelGGL(block_copy_kernel, dim3(grid), dim3(kSwapThreads), 0, st, p, chunks);
+  launch_kernel(block_copy_kernel, dim3(grid), dim3(kSwapThreads), 0, st, p, chunks);
   return hipGetLastError();
 }
 
