@@ -833,19 +833,33 @@ int paged_attn_decode_shared_prefix(void* out, int out_dtype, const void* q, con
 
 namespace {
 
-// Workspace of paged_attn_extend: the row states of every chunk group.
+// Workspace of paged_attn_extend: the row states of every chunk group. Runs of new tokens whose
+// rows per KV head reach 128 (max_query_len * G) take the kernel with workgroup-shared key/value
+// tiles; shorter runs (speculative verification) the row-state kernel, whose four wavefronts
+// split a 32-row group's tokens.
 struct ExtLayout {
   size_t m, l, acc, total;
   int chunk_groups, steps_per_chunk, max_row_groups;
+  bool wide;
 };
+
+constexpr int64_t kWideExtendRows = 128;
 
 ExtLayout ext_layout(int num_seqs, int num_query_tokens, int num_q_heads, int num_kv_heads,
                      int head_dim, int max_query_len, int max_context_len) {
   const int G = num_q_heads / num_kv_heads;
   ExtLayout L;
-  L.max_row_groups = (int)pkv::row_groups((int64_t)max_query_len * G);
-  pkv::row_state_plan((int64_t)num_seqs * num_kv_heads * L.max_row_groups, max_context_len,
-                      cu_count(), &L.chunk_groups, &L.steps_per_chunk);
+  L.wide = (int64_t)max_query_len * G >= kWideExtendRows;
+  if (L.wide) {
+    L.max_row_groups = (int)pkv::wide_row_groups((int64_t)max_query_len * G);
+    pkv::wide_row_plan((int64_t)num_seqs * num_kv_heads * L.max_row_groups, max_context_len,
+                       cu_count(), &L.chunk_groups);
+    L.steps_per_chunk = 0;
+  } else {
+    L.max_row_groups = (int)pkv::row_groups((int64_t)max_query_len * G);
+    pkv::row_state_plan((int64_t)num_seqs * num_kv_heads * L.max_row_groups, max_context_len,
+                        cu_count(), &L.chunk_groups, &L.steps_per_chunk);
+  }
   const size_t rows = (size_t)num_query_tokens * num_q_heads;
   L.m = 0;
   L.l = align256((size_t)L.chunk_groups * rows * sizeof(float));
@@ -966,7 +980,8 @@ int paged_attn_extend(void* out, int out_dtype, const void* q, const int32_t* qu
   rp.out = direct ? out : nullptr;
   rp.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
   hipError_t e = timed("extend_states", st, [&] {
-    return pkv::launch_row_states(rp, kv_dtype, head_dim, block_size, st);
+    return el.wide ? pkv::launch_extend_rows_shared(rp, kv_dtype, head_dim, block_size, st)
+                   : pkv::launch_row_states(rp, kv_dtype, head_dim, block_size, st);
   });
   if (e != hipSuccess)
     return fail(PKV_ERR_LAUNCH, "%s: states kernel: %s", fn, hipGetErrorString(e));

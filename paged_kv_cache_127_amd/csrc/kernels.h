@@ -126,6 +126,13 @@ hipError_t launch_row_states(const RowStateParams& p, int kv_dtype, int head_dim
                              int block_size, hipStream_t st);
 hipError_t launch_extend_finish(const ExtendFinishParams& p, int kv_dtype, int head_dim,
                                 hipStream_t st);
+// Extend attention with workgroup-shared key/value tiles (runs of new tokens whose rows per KV
+// head reach 128): 128-row groups covering `rows`, and the chunk groups for `base_workgroups`
+// workgroups per chunk group over up to max_tokens tokens (one whenever they fill the CUs).
+int64_t wide_row_groups(int64_t rows);
+void wide_row_plan(int64_t base_workgroups, int max_tokens, int num_cus, int* chunk_groups);
+hipError_t launch_extend_rows_shared(const RowStateParams& p, int kv_dtype, int head_dim,
+                                     int block_size, hipStream_t st);
 
 struct AppendParams {
   void* k_pool;

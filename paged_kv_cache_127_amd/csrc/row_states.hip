@@ -18,7 +18,10 @@
 // positions 0 .. L - n + t of its sequence (causal). Its n * G rows of a KV head attend to the
 // sequence's own blocks with a per-row token limit. With one chunk group a workgroup's merged
 // state is its rows' whole softmax and is normalised into the output right here; with several,
-// extend_finish folds each row's states and normalises.
+// extend_finish folds each row's states and normalises. Runs long enough to give 128 or more rows
+// per KV head (prefill chunks) take extend_rows_shared below, whose workgroups share each step's
+// keys and values among four row tiles; row_states serves the short runs (speculative
+// verification), whose four wavefronts split one row tile's tokens.
 //
 // row_states. A workgroup of four wavefronts takes (row group of RB * 16 rows of one KV head,
 // chunk group); wavefront w runs chunk 4 * cg + w, a run of 32-token steps. Per step the MFMA
@@ -48,6 +51,7 @@ constexpr int kRowWaves = 4;          // chunks per workgroup
 constexpr int kMaxStepsPerWave = 32;  // planned 32-token steps of one wavefront
 constexpr int kMaxChunkGroups = 16;   // states per row
 constexpr int kMinExtendSteps = 8;    // extend mode: fewest 32-token steps a wavefront is given
+constexpr int kWideRows = 32 * kRowWaves;   // rows of an extend_rows_shared workgroup
 
 // Lazy softmax reference: the exponents of a row use its running reference m unless a step's
 // maximum exceeds m by more than this (log2 domain), so probabilities stay below 2^8 -- harmless
@@ -267,13 +271,14 @@ void row_states(RowStateParams p) {
   // physical blocks of step k (B = 16: two blocks; a second block past the prefix repeats the
   // first and its slots are masked); out-of-range ids read block 0 and poison the state
   // (scalar loads through the constant address space: their wait is not the vector-load
-  // counter that the key/value loads in flight use)
+  // counter that the key/value loads in flight use; no branch, so that a step is one
+  // scheduling region)
   auto step_blocks = [&](int k, int& b0, int& b1) {
     const int j0 = B == 16 ? 2 * k : k;
     b0 = blocks[j0];
-    b1 = (B == 16 && j0 + 1 < nb) ? blocks[j0 + 1] : b0;
+    b1 = B == 16 ? blocks[min(j0 + 1, nb - 1)] : b0;
   };
-  u32x4 kr[2][NC], vr[NF];
+  u32x4 kr[2][NC], vr[NF], va[NF];
   auto load_k = [&](int b0, int b1) {
     b0 = valid_block(b0, p.num_blocks) ? b0 : 0;
     b1 = valid_block(b1, p.num_blocks) ? b1 : 0;
@@ -298,21 +303,69 @@ void row_states(RowStateParams p) {
                      16 * vch);
     }
   };
+  auto stage_v = [&]() {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) *reinterpret_cast<u32x4*>(vstage + vw_ofs[f]) = vr[f];
+  };
 
+  // Softmax of row block rb's scores z at step k against its reference m_ref: probabilities
+  // as 16-bit high parts and remainders, their sum folded into l_run (l * alpha + sum).
+  auto softmax = [&](const float (&z)[8], float m_ref, float alpha, float& l, u32x4& phi,
+                     u32x4& plo) {
+    float pr[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      pr[t] = fast_exp2(fmaf(z[t], p.scale_log2, -m_ref));
+      ps += pr[t];
+    }
+    l = l * alpha + ps;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t h, lo;
+      split_hi_lo<T>(pr[2 * u], pr[2 * u + 1], h, lo);
+      phi[u] = h;
+      plo[u] = lo;
+    }
+  };
+  auto pv = [&](int rb, const u32x4& phi, const u32x4& plo) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) oacc[rb][f] = mfma16x16x32<T>(va[f], phi, oacc[rb][f]);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) oacc[rb][f] = mfma16x16x32<T>(va[f], plo, oacc[rb][f]);
+  };
+
+  // Step k in three stretches, each pairing matrix-core work with other work of the step:
+  //   the score MFMAs with the transposed reads of the step's value tile (written to LDS
+  //   during the previous step) and the next step's key loads;
+  //   (row maxima; a rare branch rescales the accumulators when a reference moves)
+  //   the first row block's P.V MFMAs with the second row block's softmax;
+  //   the second row block's P.V MFMAs with the next step's value rows going to LDS and the
+  //   loads of the values of the step after it.
+  // Keys are loaded one step ahead, values two (one step in registers, one in LDS), block ids
+  // three (the scalar loads).
   if (k0 < k1) {
-    int b0, b1, n0, n1;
+    const int kl = k1 - 1;
+    int b0, b1, n0, n1, nn0, nn1;
     step_blocks(k0, b0, b1);
     load_k(b0, b1);
     load_v(b0, b1);
-    step_blocks(min(k0 + 1, k1 - 1), n0, n1);
+    step_blocks(min(k0 + 1, kl), n0, n1);
+    step_blocks(min(k0 + 2, kl), nn0, nn1);
+    stage_v();
+    load_v(n0, n1);
 #pragma unroll 1
     for (int k = k0; k < k1; ++k) {
       const int nvalid = min(32, tok_end - 32 * k);
       poison = poison || !valid_block(b0, p.num_blocks) || !valid_block(b1, p.num_blocks);
-      // block ids two steps ahead, the data one step ahead (past the end: the last step again,
-      // so that every load stays unconditional)
-      int nn0, nn1;
-      step_blocks(min(k + 2, k1 - 1), nn0, nn1);
+      int n30, n31;
+      step_blocks(min(k + 3, kl), n30, n31);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const uint2 lo = lds_read_tr16(vstage + (vr_ofs[0] ^ (f << 5)));
+        const uint2 hi = lds_read_tr16(vstage + (vr_ofs[1] ^ (f << 5)));
+        va[f] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
       f32x4 sacc[RBK][2];
 #pragma unroll
       for (int rb = 0; rb < RBK; ++rb)
@@ -323,49 +376,50 @@ void row_states(RowStateParams p) {
           for (int c = 0; c < NC; ++c) sacc[rb][a] = mfma16x16x32<T>(kr[a][c], q[rb][c], sacc[rb][a]);
         }
       load_k(n0, n1);
-      wave_lds_sync();
 #pragma unroll
-      for (int f = 0; f < NF; ++f) *reinterpret_cast<u32x4*>(vstage + vw_ofs[f]) = vr[f];
-      load_v(n0, n1);
-      wave_lds_sync();
-      u32x4 va[NF];
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const uint2 lo = lds_read_tr16(vstage + (vr_ofs[0] ^ (f << 5)));
-        const uint2 hi = lds_read_tr16(vstage + (vr_ofs[1] ^ (f << 5)));
-        va[f] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      for (int i = 0; i < 2 * NF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
       }
-      if (nvalid < 32) {
-        const int nv = nvalid - vtok;
-        u32x4 msk;
+
+      // raw scores; masked tokens -inf (the scale is positive, so the row maximum of the
+      // raw scores, scaled, is the maximum of the scaled ones)
+      float z[RBK][8];
+      if (32 * k + 32 <= lim_min) {   // every token of the step counts for every row
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          msk[u] = (2 * u < nv ? 0xffffu : 0u) | (2 * u + 1 < nv ? 0xffff0000u : 0u);
-#pragma unroll
-        for (int f = 0; f < NF; ++f) va[f] &= msk;
-      }
-#pragma unroll
-      for (int rb = 0; rb < RBK; ++rb) {
-        // raw scores; masked tokens -inf (the scale is positive, so the row maximum of the
-        // raw scores, scaled, is the maximum of the scaled ones)
-        float z[8];
-        if (32 * k + 32 <= lim_min) {   // every token of the step counts for every row
+        for (int rb = 0; rb < RBK; ++rb)
 #pragma unroll
           for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) z[4 * a + e] = sacc[rb][a][e];
-        } else {
+            for (int e = 0; e < 4; ++e) z[rb][4 * a + e] = sacc[rb][a][e];
+      } else {
+        if (nvalid < 32) {   // value rows past the end: zero, so that 0 * garbage cannot appear
+          const int nv = nvalid - vtok;
+          u32x4 msk;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            msk[u] = (2 * u < nv ? 0xffffu : 0u) | (2 * u + 1 < nv ? 0xffff0000u : 0u);
+#pragma unroll
+          for (int f = 0; f < NF; ++f) va[f] &= msk;
+        }
+#pragma unroll
+        for (int rb = 0; rb < RBK; ++rb)
 #pragma unroll
           for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int tok = vtok + 4 * a + e;
-              z[4 * a + e] = (tok < nvalid && 32 * k + tok < lim[rb]) ? sacc[rb][a][e] : kNegInf;
+              z[rb][4 * a + e] =
+                  (tok < nvalid && 32 * k + tok < lim[rb]) ? sacc[rb][a][e] : kNegInf;
             }
-        }
-        float mx = z[0];
+      }
+      float m_ref[RBK], alpha[RBK];
+      bool upd_any = false;
 #pragma unroll
-        for (int t = 1; t < 8; ++t) mx = fmaxf(mx, z[t]);
+      for (int rb = 0; rb < RBK; ++rb) {
+        float mx = z[rb][0];
+#pragma unroll
+        for (int t = 1; t < 8; ++t) mx = fmaxf(mx, z[rb][t]);
         const float m_step = rows_max(mx) * p.scale_log2;
         // the reference moves only when this step's maximum exceeds it by more than
         // kLazyRescale (a first finite maximum always moves it); otherwise alpha is exactly 1
@@ -373,40 +427,55 @@ void row_states(RowStateParams p) {
         const float m_new = upd ? m_step : m_run[rb];
         // a row with nothing to attend yet (causal limit) keeps (-inf, 0, 0): exponents
         // against 0 instead of -inf, so that no -inf - -inf appears
-        const float m_ref = m_new == kNegInf ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run[rb] - m_ref);
-        float pr[8];
-        float ps = 0.f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          pr[t] = fast_exp2(fmaf(z[t], p.scale_log2, -m_ref));
-          ps += pr[t];
-        }
-        l_run[rb] = l_run[rb] * alpha + ps;
-        const bool moved = __builtin_amdgcn_ballot_w64(upd) != 0;
+        m_ref[rb] = m_new == kNegInf ? 0.f : m_new;
+        alpha[rb] = fast_exp2(m_run[rb] - m_ref[rb]);
         m_run[rb] = m_new;
-        u32x4 phi, plo;
+        upd_any = upd_any || upd;
+      }
+      if (__builtin_amdgcn_ballot_w64(upd_any) != 0) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          uint32_t h, l;
-          split_hi_lo<T>(pr[2 * u], pr[2 * u + 1], h, l);
-          phi[u] = h;
-          plo[u] = l;
-        }
-        if (moved) {
+        for (int rb = 0; rb < RBK; ++rb)
 #pragma unroll
-          for (int f = 0; f < NF; ++f) oacc[rb][f] *= alpha;
-        }
+          for (int f = 0; f < NF; ++f) oacc[rb][f] *= alpha[rb];
+      }
+
+      // (LDS operations of one wavefront complete in order, and the compiler keeps a store
+      // after the loads of the same tile that precede it: no fence is needed between this
+      // step's transposed reads, the next step's value rows written below and their reads at
+      // the top of the next step)
+      u32x4 phi[RBK], plo[RBK];
+      softmax(z[0], m_ref[0], alpha[0], l_run[0], phi[0], plo[0]);
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          oacc[rb][f] = mfma16x16x32<T>(va[f], phi, oacc[rb][f]);
-          oacc[rb][f] = mfma16x16x32<T>(va[f], plo, oacc[rb][f]);
+      for (int rb = 0; rb < RBK; ++rb) {
+        if (rb + 1 < RBK)
+          softmax(z[rb + 1], m_ref[rb + 1], alpha[rb + 1], l_run[rb + 1], phi[rb + 1], plo[rb + 1]);
+        if (rb + 1 == RBK) {
+          stage_v();            // the next step's values to LDS
+          load_v(nn0, nn1);     // the values of the step after it
         }
+        pv(rb, phi[rb], plo[rb]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * NF * (RBK - 1); ++i) {   // MFMA, then VALU of the next softmax
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);
+      }
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {       // last P.V block: MFMA with the LDS writes, then loads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 1);
+      }
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
       }
       b0 = n0;
       b1 = n1;
       n0 = nn0;
       n1 = nn1;
+      nn0 = n30;
+      nn1 = n31;
     }
   }
   float l_tot[RBK];
@@ -469,6 +538,337 @@ void row_states(RowStateParams p) {
     if (!p.out && wave == 0 && jg == 0) {
       store_nt(p.st_m + row, mx);
       store_nt(p.st_l + row, lsum);
+    }
+  }
+}
+
+// Position of 16-byte piece c of key row t in the LDS key tile: pieces XOR-swizzled per row so
+// that the 16 rows one score-operand read touches (t = 8q + 4a + 0..3, q = 0..3) fall on
+// distinct banks.
+template <int D>
+__device__ __forceinline__ int key_piece(int t, int c) {
+  if constexpr (D == 128) return c ^ ((t & 3) | (((t >> 3) & 3) << 2));
+  else return c ^ (((t >> 1) & 1) | (((t >> 3) & 3) << 1));
+}
+
+// extend_rows_shared: extend attention for long runs of new tokens (a prefill chunk), where one
+// sequence's (new token, head) rows of a KV head number at least kWideRows. The four wavefronts
+// of a workgroup take four different 32-row tiles (rows rg * 128 + 32 * wave + 16 * rb + r16)
+// over the same 32-token steps, and each step's key and value rows are loaded once for the
+// workgroup -- every thread loads its share -- and shared through LDS: per step and wavefront
+// 4 KB (d = 128) go through the CU's vector memory path instead of the 16 KB that row_states
+// loads for its own chunk. Two LDS stages of (keys, values): while the wavefronts read step k's
+// tile they write step k + 1's, loaded during step k - 1, into the other stage and load step
+// k + 2; one workgroup barrier per step separates a stage's writes from its reads. Keys are read
+// from LDS as the score MFMA's A operand (rows tau(a, i) as in row_states), values as in
+// row_states. The workgroup's token range ends at its last row's limit and is split evenly over
+// the chunk groups; with one chunk group each wavefront normalises its rows into the output,
+// otherwise it stores their states for extend_finish.
+template <typename T, int D, int B>
+__global__ __launch_bounds__(64 * kRowWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void extend_rows_shared(RowStateParams p) {
+  static_assert(B == 16 || B == 32, "block size");
+  constexpr int RBK = kRowsRB;
+  constexpr int NC = D / 32;
+  constexpr int NF = D / 16;
+  constexpr int ES = 2;
+  constexpr int ROWB = D * ES;                          // bytes per key / value row
+  constexpr int CPR = ROWB / 16;                        // 16-byte pieces per row
+  constexpr int TILE = 32 * ROWB;                       // one step's keys (or values)
+  constexpr int NT = 64 * kRowWaves;                    // threads
+  constexpr int NLD = 2 * 32 * CPR / NT;                // pieces per thread per step
+  constexpr int NLK = 32 * CPR / NT;                    // ... of them keys
+  static_assert(NLD * NT == 2 * 32 * CPR && NLK * NT == 32 * CPR, "load split");
+  __shared__ __attribute__((aligned(16))) char lds[2][2][TILE];   // [stage][keys, values]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uni((int)(threadIdx.x >> 6));
+  const int r16 = lane & 15;
+  const int jg = lane >> 4;
+  const int Hq = p.num_q_heads, Hkv = p.num_kv_heads;
+  const int G = Hq / Hkv;
+  const int cgroups = p.chunk_groups;
+  const int cg = blockIdx.x % cgroups;
+  const int mg = p.max_row_groups;
+  const int rg = (blockIdx.x / cgroups) % mg;
+  const int sg = blockIdx.x / (cgroups * mg);           // grid = S * Hkv * mg * cgroups
+  const int g = sg % Hkv;
+  const int s = sg / Hkv;
+  // out-of-contract starts are clamped into [0, T]: rows are never read or written outside
+  const int qs = uni(min(max(p.query_start[s], 0), p.num_query_tokens));
+  const int n = uni(min(max(p.query_start[s + 1] - qs, 0), p.num_query_tokens - qs));
+  const int L = uni(clamp_len(p.lens[s], p.max_blocks * B));
+  const int R = n * G;
+  if (rg * kWideRows >= R) return;                      // the whole workgroup: no barrier yet
+  const int t_last = (min((rg + 1) * kWideRows, R) - 1) / G;
+  const int tok_end = min(max(L - n + t_last + 1, 0), L);
+  const ctable_t blocks = (ctable_t)p.tables + (size_t)s * p.max_blocks;
+  const int nsteps = ceil_div(tok_end, 32);
+  const int spc = ceil_div(nsteps, cgroups);
+  const int k0 = min(cg * spc, nsteps);
+  const int k1 = min(k0 + spc, nsteps);
+  const int nb = ceil_div(tok_end, B);                  // blocks holding the tokens
+
+  // this wavefront's rows (padding rows repeat the last row and are never stored)
+  size_t qrow[RBK];
+  int lim[RBK];
+  bool live[RBK];
+#pragma unroll
+  for (int rb = 0; rb < RBK; ++rb) {
+    const int r0 = rg * kWideRows + 32 * wave + 16 * rb + r16;
+    live[rb] = r0 < R;
+    const int r = min(r0, R - 1);
+    const int a = r / G;                                 // new token
+    const int i = r - a * G;
+    qrow[rb] = ((size_t)(qs + a)) * Hq + (size_t)g * G + i;
+    lim[rb] = min(max(L - n + a + 1, 0), L);
+  }
+
+  // a chunk group with no step (or nothing to attend) writes the empty state (-inf, 0, 0) of
+  // its rows -- for the output, a zero row -- and leaves (uniform over the workgroup)
+  if (k0 >= k1) {
+#pragma unroll
+    for (int rb = 0; rb < RBK; ++rb) {
+      if (!live[rb]) continue;
+      if (p.out) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) store_row4<T>(p, qrow[rb] * D + 16 * f + 4 * jg,
+                                                    f32x4{0.f, 0.f, 0.f, 0.f}, 0.f);
+        continue;
+      }
+      const size_t row = (size_t)cg * p.state_rows + qrow[rb];
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        store_nt(p.st_acc + row * D + 16 * f + 4 * jg, f32x4{0.f, 0.f, 0.f, 0.f});
+      if (jg == 0) {
+        store_nt(p.st_m + row, kNegInf);
+        store_nt(p.st_l + row, 0.f);
+      }
+    }
+    return;
+  }
+
+  u32x4 q[RBK][NC];
+#pragma unroll
+  for (int rb = 0; rb < RBK; ++rb) {
+    const char* qp = reinterpret_cast<const char*>(p.q) + (qrow[rb] * D + 8 * jg) * ES;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) q[rb][c] = load16(qp + 32 * c * ES);
+  }
+
+  // this thread's share of a step's rows: piece u = j * NT + tid of the keys (j < NLK) or the
+  // values -- row t, piece c, from the first or second block of the step (B = 16) -- and its
+  // place in the stage
+  const char* kbase = reinterpret_cast<const char*>(p.k_pool);
+  const char* vbase = reinterpret_cast<const char*>(p.v_pool);
+  const size_t tile_stride = (size_t)B * D * ES;       // bytes per (block, head)
+  int gofs[NLD], wofs[NLD];
+  bool second[NLD];
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const int u = (j % NLK) * NT + (int)threadIdx.x;
+    const int t = u / CPR, c = u % CPR;
+    second[j] = B == 16 && t >= 16;
+    gofs[j] = (t & (B - 1)) * ROWB + 16 * c;
+    wofs[j] = j < NLK ? t * ROWB + (key_piece<D>(t, c) << 4)
+                      : TILE + t * ROWB + (((c >> 1) ^ piece_swizzle<D>(t)) << 5) + 16 * (c & 1);
+  }
+  // score-operand reads: key row tau(a, r16) = 8 * (r16 / 4) + 4a + r16 % 4, pieces jg + 4c
+  int kro[2][NC];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int t = 8 * (r16 >> 2) + 4 * a + (r16 & 3);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kro[a][c] = t * ROWB + (key_piece<D>(t, jg + 4 * c) << 4);
+  }
+  int vr_ofs[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int t = 8 * jg + 4 * hh + (r16 >> 2);
+    vr_ofs[hh] = TILE + t * ROWB + (piece_swizzle<D>(t) << 5) + 8 * (r16 & 3);
+  }
+  const int vtok = 8 * jg;
+
+  int lim_min = lim[0];
+#pragma unroll
+  for (int rb = 1; rb < RBK; ++rb) lim_min = min(lim_min, lim[rb]);
+  lim_min = uni((int)-cross_max<1>(-(float)lim_min));
+
+  float m_run[RBK], l_run[RBK];
+  f32x4 oacc[RBK][NF];
+#pragma unroll
+  for (int rb = 0; rb < RBK; ++rb) {
+    m_run[rb] = kNegInf;
+    l_run[rb] = 0.f;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) oacc[rb][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bool poison = false;
+
+  // physical blocks of step k, as in row_states (scalar loads, no branch)
+  auto step_blocks = [&](int k, int& b0, int& b1) {
+    const int j0 = B == 16 ? 2 * k : k;
+    b0 = blocks[j0];
+    b1 = B == 16 ? blocks[min(j0 + 1, nb - 1)] : b0;
+  };
+  u32x4 ld[NLD];
+  auto load_step = [&](int b0, int b1) {
+    b0 = valid_block(b0, p.num_blocks) ? b0 : 0;
+    b1 = valid_block(b1, p.num_blocks) ? b1 : 0;
+    const size_t o0 = ((size_t)b0 * Hkv + g) * tile_stride;
+    const size_t o1 = ((size_t)b1 * Hkv + g) * tile_stride;
+#pragma unroll
+    for (int j = 0; j < NLD; ++j)
+      ld[j] = load16((j < NLK ? kbase : vbase) + (second[j] ? o1 : o0) + gofs[j]);
+  };
+  auto write_step = [&](char* stage) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) *reinterpret_cast<u32x4*>(stage + wofs[j]) = ld[j];
+  };
+
+  const int kl = k1 - 1;
+  int b0, b1, n0, n1, nn0, nn1;
+  step_blocks(k0, b0, b1);
+  load_step(b0, b1);
+  write_step(&lds[0][0][0]);
+  step_blocks(min(k0 + 1, kl), n0, n1);
+  load_step(n0, n1);
+  step_blocks(min(k0 + 2, kl), nn0, nn1);
+  __syncthreads();
+#pragma unroll 1
+  for (int k = k0; k < k1; ++k) {
+    const int sti = (k - k0) & 1;
+    const char* stage = &lds[sti][0][0];
+    const int nvalid = min(32, tok_end - 32 * k);
+    poison = poison || !valid_block(b0, p.num_blocks) || !valid_block(b1, p.num_blocks);
+    int n30, n31;
+    step_blocks(min(k + 3, kl), n30, n31);
+    u32x4 kr[2][NC], va[NF];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kr[a][c] = *reinterpret_cast<const u32x4*>(stage + kro[a][c]);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const uint2 lo = lds_read_tr16(stage + (vr_ofs[0] ^ (f << 5)));
+      const uint2 hi = lds_read_tr16(stage + (vr_ofs[1] ^ (f << 5)));
+      va[f] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+    f32x4 sacc[RBK][2];
+#pragma unroll
+    for (int rb = 0; rb < RBK; ++rb)
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        sacc[rb][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) sacc[rb][a] = mfma16x16x32<T>(kr[a][c], q[rb][c], sacc[rb][a]);
+      }
+
+    // raw scores; masked tokens -inf
+    float z[RBK][8];
+    if (32 * k + 32 <= lim_min) {
+#pragma unroll
+      for (int rb = 0; rb < RBK; ++rb)
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[rb][4 * a + e] = sacc[rb][a][e];
+    } else {
+      if (nvalid < 32) {   // value rows past the end: zero, so that 0 * garbage cannot appear
+        const int nv = nvalid - vtok;
+        u32x4 msk;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          msk[u] = (2 * u < nv ? 0xffffu : 0u) | (2 * u + 1 < nv ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) va[f] &= msk;
+      }
+#pragma unroll
+      for (int rb = 0; rb < RBK; ++rb)
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int tok = vtok + 4 * a + e;
+            z[rb][4 * a + e] =
+                (tok < nvalid && 32 * k + tok < lim[rb]) ? sacc[rb][a][e] : kNegInf;
+          }
+    }
+    float m_ref[RBK], alpha[RBK];
+    bool upd_any = false;
+#pragma unroll
+    for (int rb = 0; rb < RBK; ++rb) {
+      float mx = z[rb][0];
+#pragma unroll
+      for (int t = 1; t < 8; ++t) mx = fmaxf(mx, z[rb][t]);
+      const float m_step = rows_max(mx) * p.scale_log2;
+      const bool upd = m_step > m_run[rb] + kLazyRescale;
+      const float m_new = upd ? m_step : m_run[rb];
+      m_ref[rb] = m_new == kNegInf ? 0.f : m_new;
+      alpha[rb] = fast_exp2(m_run[rb] - m_ref[rb]);
+      m_run[rb] = m_new;
+      upd_any = upd_any || upd;
+    }
+    if (__builtin_amdgcn_ballot_w64(upd_any) != 0) {
+#pragma unroll
+      for (int rb = 0; rb < RBK; ++rb)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) oacc[rb][f] *= alpha[rb];
+    }
+#pragma unroll
+    for (int rb = 0; rb < RBK; ++rb) {
+      float pr[8];
+      float ps = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        pr[t] = fast_exp2(fmaf(z[rb][t], p.scale_log2, -m_ref[rb]));
+        ps += pr[t];
+      }
+      l_run[rb] = l_run[rb] * alpha[rb] + ps;
+      u32x4 phi, plo;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        uint32_t h, lo;
+        split_hi_lo<T>(pr[2 * u], pr[2 * u + 1], h, lo);
+        phi[u] = h;
+        plo[u] = lo;
+      }
+#pragma unroll
+      for (int f = 0; f < NF; ++f) oacc[rb][f] = mfma16x16x32<T>(va[f], phi, oacc[rb][f]);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) oacc[rb][f] = mfma16x16x32<T>(va[f], plo, oacc[rb][f]);
+    }
+    // the next step's rows into the other stage (its reads ended before the last barrier),
+    // then the loads of the step after it (past the end: the last step again)
+    write_step(&lds[sti ^ 1][0][0]);
+    load_step(nn0, nn1);
+    __syncthreads();
+    b0 = n0;
+    b1 = n1;
+    n0 = nn0;
+    n1 = nn1;
+    nn0 = n30;
+    nn1 = n31;
+  }
+
+#pragma unroll
+  for (int rb = 0; rb < RBK; ++rb) {
+    float l_tot = cross_sum<16>(l_run[rb]);
+    if (poison) l_tot = __builtin_nanf("");
+    if (!live[rb]) continue;
+    if (p.out) {
+      // one chunk group: the row's whole softmax, normalised (0 for a row with nothing to attend)
+      const float sc = (m_run[rb] == kNegInf || l_tot == 0.f) ? 0.f : 1.0f / l_tot;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) store_row4<T>(p, qrow[rb] * D + 16 * f + 4 * jg, oacc[rb][f], sc);
+    } else {
+      const size_t row = (size_t)cg * p.state_rows + qrow[rb];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) store_nt(p.st_acc + row * D + 16 * f + 4 * jg, oacc[rb][f]);
+      if (jg == 0) {
+        store_nt(p.st_m + row, m_run[rb]);
+        store_nt(p.st_l + row, l_tot);
+      }
     }
   }
 }
@@ -585,6 +985,49 @@ static void launch_finish_t(const ExtendFinishParams& p, hipStream_t st) {
   else if (C <= 4) launch_kernel((extend_finish<D, T, 4>), grid, blk, 0, st, p);
   else if (C <= 8) launch_kernel((extend_finish<D, T, 8>), grid, blk, 0, st, p);
   else launch_kernel((extend_finish<D, T, 16>), grid, blk, 0, st, p);
+}
+
+template <typename T, int D>
+static void launch_wide_td(const RowStateParams& p, int64_t grid, int block_size,
+                           hipStream_t st) {
+  if (block_size == 16)
+    launch_kernel((extend_rows_shared<T, D, 16>), dim3((unsigned)grid), dim3(64 * kRowWaves), 0,
+                  st, p);
+  else
+    launch_kernel((extend_rows_shared<T, D, 32>), dim3((unsigned)grid), dim3(64 * kRowWaves), 0,
+                  st, p);
+}
+
+int64_t wide_row_groups(int64_t rows) { return (rows + kWideRows - 1) / kWideRows; }
+
+void wide_row_plan(int64_t base_workgroups, int max_tokens, int num_cus, int* chunk_groups) {
+  // one chunk group (the rows normalised in the kernel, no state round trip) whenever the
+  // workgroups fill the CUs; otherwise enough groups to fill them, at most one per step and
+  // at most kMaxChunkGroups
+  const int64_t base = std::max<int64_t>(base_workgroups, 1);
+  const int64_t nsteps = std::max((max_tokens + 31) / 32, 1);
+  const int64_t fill = (std::max(num_cus, 1) + base - 1) / base;
+  *chunk_groups = (int)std::max<int64_t>(
+      1, std::min<int64_t>(fill, std::min<int64_t>(nsteps, kMaxChunkGroups)));
+}
+
+hipError_t launch_extend_rows_shared(const RowStateParams& p, int kv_dtype, int head_dim,
+                                     int block_size, hipStream_t st) {
+  if (p.num_seqs <= 0) return hipSuccess;
+  const int64_t grid =
+      (int64_t)p.num_seqs * p.num_kv_heads * p.max_row_groups * p.chunk_groups;
+  if (grid <= 0) return hipSuccess;
+  if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if (kv_dtype == 2) {
+    if (head_dim == 128) launch_wide_td<bf16_t, 128>(p, grid, block_size, st);
+    else launch_wide_td<bf16_t, 64>(p, grid, block_size, st);
+  } else if (kv_dtype == 1) {
+    if (head_dim == 128) launch_wide_td<f16_t, 128>(p, grid, block_size, st);
+    else launch_wide_td<f16_t, 64>(p, grid, block_size, st);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_extend_finish(const ExtendFinishParams& p, int kv_dtype, int head_dim,

@@ -39,9 +39,14 @@ def _run(db, q, start, out_dtype=torch.float32, ws_fill=255):
     return out.cpu()
 
 
+# Runs whose rows per KV head (max new tokens x G) reach 128 take the kernel with
+# workgroup-shared key/value tiles, shorter ones the row-state kernel; the first and third cases
+# have a twin one token shorter that takes the other kernel.
 CASES = [
     # context lengths (including the new tokens), new tokens, Hq, Hkv, d, B, dtype
     ([40, 17, 64, 5, 300], [3, 1, 16, 5, 0], 16, 2, 128, 16, "bf16"),
+    ([40, 17, 64, 5, 300], [3, 1, 15, 5, 0], 16, 2, 128, 16, "bf16"),
+    ([31, 70, 9, 513], [7, 7, 7, 7], 32, 2, 64, 16, "f16"),
     ([100, 33, 1000], [33, 33, 70], 8, 4, 128, 32, "bf16"),      # whole-sequence prefill
     ([31, 70, 9, 513], [8, 8, 8, 8], 32, 2, 64, 16, "f16"),       # G = 16
     ([2048, 1, 129], [12, 1, 64], 64, 8, 128, 16, "bf16"),
@@ -49,7 +54,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"S{len(c[0])}-G{c[2] // c[3]}-d{c[4]}-B{c[5]}-{c[6]}")
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"S{len(c[0])}-n{max(c[1])}-G{c[2] // c[3]}-d{c[4]}-B{c[5]}-{c[6]}")
 def test_parity(case):
     lens, new, hq, hkv, d, B, dt = case
     seed = zlib.crc32(repr(case).encode()) % 10000
