@@ -585,15 +585,34 @@ void extend_rows_shared(RowStateParams p) {
   const int wave = uni((int)(threadIdx.x >> 6));
   const int r16 = lane & 15;
   const int jg = lane >> 4;
-  const int Hq = p.num_q_heads, Hkv = p.num_kv_heads;
+  const int S = p.num_seqs, Hq = p.num_q_heads, Hkv = p.num_kv_heads;
   const int G = Hq / Hkv;
   const int cgroups = p.chunk_groups;
-  const int cg = blockIdx.x % cgroups;
   const int mg = p.max_row_groups;
-  const int rg = (blockIdx.x / cgroups) % mg;
-  const int sg = blockIdx.x / (cgroups * mg);           // grid = S * Hkv * mg * cgroups
-  const int g = sg % Hkv;
-  const int s = sg / Hkv;
+  // Dispatch order (grid = S * Hkv * mg * cgroups): chunk groups fastest, then KV heads (with 8
+  // heads each XCD keeps one head's keys and values), then the row groups from the last one
+  // (the longest token range) down, then the sequences longest first -- their rank by context
+  // length, ties by index, when at most one per thread -- so that the longest workgroups start
+  // first and the short ones fill in at the end.
+  const int cg = blockIdx.x % cgroups;
+  const int g = (blockIdx.x / cgroups) % Hkv;
+  const int rg = mg - 1 - (int)((blockIdx.x / (cgroups * Hkv)) % mg);
+  const int rank = blockIdx.x / (cgroups * Hkv * mg);
+  int s = rank;
+  if (S > 1 && S <= NT) {
+    __shared__ int ranked;
+    int* sl = reinterpret_cast<int*>(&lds[0][0][0]);   // stage memory, not in use yet
+    for (int j = threadIdx.x; j < S; j += NT) sl[j] = clamp_len(p.lens[j], p.max_blocks * B);
+    __syncthreads();
+    if ((int)threadIdx.x < S) {
+      const int j = threadIdx.x, lj = sl[j];
+      int r = 0;
+      for (int i = 0; i < S; ++i) r += (sl[i] > lj || (sl[i] == lj && i < j)) ? 1 : 0;
+      if (r == rank) ranked = j;
+    }
+    __syncthreads();
+    s = uni(ranked);
+  }
   // out-of-contract starts are clamped into [0, T]: rows are never read or written outside
   const int qs = uni(min(max(p.query_start[s], 0), p.num_query_tokens));
   const int n = uni(min(max(p.query_start[s + 1] - qs, 0), p.num_query_tokens - qs));
