@@ -150,12 +150,29 @@ void row_states(RowStateParams p) {
     blocks = (ctable_t)p.prefix_blocks;
   } else {
     // extend mode: rows r = t * G + i of sequence s's n new tokens, its own blocks, tokens up
-    // to the group's last row's limit (grid = S * Hkv * max_row_groups * cgroups)
+    // to the group's last row's limit (grid = S * Hkv * max_row_groups * cgroups). Dispatch
+    // order: chunk groups fastest, then KV heads, then the row groups from the last one down,
+    // then the sequences longest first (rank by context length, ties by index, when at most
+    // one per thread), so that the longest workgroups start first.
     const int mg = p.max_row_groups;
-    rg = (blockIdx.x / cgroups) % mg;
-    const int sg = blockIdx.x / (cgroups * mg);
-    g = sg % Hkv;
-    const int s = sg / Hkv;
+    g = (blockIdx.x / cgroups) % Hkv;
+    rg = mg - 1 - (int)((blockIdx.x / (cgroups * Hkv)) % mg);
+    const int rank = blockIdx.x / (cgroups * Hkv * mg);
+    int s = rank;
+    if (S > 1 && S <= 64 * kRowWaves) {
+      __shared__ int ranked;
+      int* sl = reinterpret_cast<int*>(lds);          // value tiles, not in use yet
+      for (int j = threadIdx.x; j < S; j += blockDim.x) sl[j] = clamp_len(p.lens[j], p.max_blocks * B);
+      __syncthreads();
+      if ((int)threadIdx.x < S) {
+        const int j = threadIdx.x, lj = sl[j];
+        int r = 0;
+        for (int i = 0; i < S; ++i) r += (sl[i] > lj || (sl[i] == lj && i < j)) ? 1 : 0;
+        if (r == rank) ranked = j;
+      }
+      __syncthreads();
+      s = uni(ranked);
+    }
     // out-of-contract starts are clamped into [0, T]: rows are never read or written outside
     qs = min(max(p.query_start[s], 0), p.num_query_tokens);
     n = min(max(p.query_start[s + 1] - qs, 0), p.num_query_tokens - qs);
@@ -335,15 +352,13 @@ void row_states(RowStateParams p) {
     for (int f = 0; f < NF; ++f) oacc[rb][f] = mfma16x16x32<T>(va[f], plo, oacc[rb][f]);
   };
 
-  // Step k in three stretches, each pairing matrix-core work with other work of the step:
-  //   the score MFMAs with the transposed reads of the step's value tile (written to LDS
-  //   during the previous step) and the next step's key loads;
-  //   (row maxima; a rare branch rescales the accumulators when a reference moves)
-  //   the first row block's P.V MFMAs with the second row block's softmax;
-  //   the second row block's P.V MFMAs with the next step's value rows going to LDS and the
-  //   loads of the values of the step after it.
-  // Keys are loaded one step ahead, values two (one step in registers, one in LDS), block ids
-  // three (the scalar loads).
+  // Step k: the transposed reads of the step's value tile (written to LDS during the previous
+  // step) and the score MFMAs, the next step's key loads; the row maxima (a rare branch
+  // rescales the accumulators when a reference moves); the softmax and P.V products of each
+  // row block; the next step's value rows to LDS and the loads of the values of the step after
+  // it. Keys are loaded one step ahead, values two (one step in registers, one in LDS), block
+  // ids three (the scalar loads). (Scheduling hints that interleave the MFMAs with the softmax
+  // and the LDS writes gave no measurable gain and made the block-size-32 loop spill.)
   if (k0 < k1) {
     const int kl = k1 - 1;
     int b0, b1, n0, n1, nn0, nn1;
@@ -376,11 +391,6 @@ void row_states(RowStateParams p) {
           for (int c = 0; c < NC; ++c) sacc[rb][a] = mfma16x16x32<T>(kr[a][c], q[rb][c], sacc[rb][a]);
         }
       load_k(n0, n1);
-#pragma unroll
-      for (int i = 0; i < 2 * NF; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-      }
 
       // raw scores; masked tokens -inf (the scale is positive, so the row maximum of the
       // raw scores, scaled, is the maximum of the scaled ones)
@@ -454,21 +464,6 @@ void row_states(RowStateParams p) {
           load_v(nn0, nn1);     // the values of the step after it
         }
         pv(rb, phi[rb], plo[rb]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2 * NF * (RBK - 1); ++i) {   // MFMA, then VALU of the next softmax
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);
-      }
-#pragma unroll
-      for (int i = 0; i < NF; ++i) {       // last P.V block: MFMA with the LDS writes, then loads
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 1);
-      }
-#pragma unroll
-      for (int i = 0; i < NF; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
       }
       b0 = n0;
       b1 = n1;
