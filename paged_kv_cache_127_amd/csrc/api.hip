@@ -746,8 +746,10 @@ int paged_attn_decode_shared_prefix(void* out, int out_dtype, const void* q, con
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return fail(PKV_ERR_INVALID_ARG, "%s: max_context_len %d exceeds table capacity %d x %d",
                 fn, max_context_len, max_blocks_per_seq, block_size);
-  const int n = choose_workers(num_workers);
-  const SpLayout sl = sp_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, n, prefix_len);
+  // the workspace holds the partial slots of the automatic worker count's upper bound; the
+  // suffix decode itself picks its count as the plain decode does (every worker resident)
+  const SpLayout sl = sp_layout(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                choose_workers(num_workers), prefix_len);
   if (!workspace || workspace_bytes < sl.total)
     return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", fn,
                 workspace_bytes, sl.total);
@@ -823,8 +825,8 @@ int paged_attn_decode_shared_prefix(void* out, int out_dtype, const void* q, con
   const int rc = decode_impl(fn, o_suffix, PKV_F32, q, k_pool, v_pool, kv_dtype, nullptr,
                              nullptr, block_tables + nb, max_blocks_per_seq, suffix_lens,
                              max_context_len - prefix_len, num_seqs, num_q_heads, num_kv_heads,
-                             head_dim, block_size, num_blocks, scale, n, workspace, sl.decode,
-                             stream, &pf);
+                             head_dim, block_size, num_blocks, scale, num_workers, workspace,
+                             sl.decode, stream, &pf);
   if (rc != PKV_OK) return rc;
   return ok();
 }
