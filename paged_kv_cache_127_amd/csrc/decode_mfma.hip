@@ -8,17 +8,21 @@
 // contiguous copy). Whole segments are normalised and written to the output; split pieces
 // write partial states that the merge kernel combines.
 //
-// Per 32-token step (D = 128) a wavefront issues (per lane) 8 + 8 16-byte loads:
-//   K operand, sub-tile a (0/1), d-chunk c: key row tau(a, i) = 8*(i/4) + 4a + i%4 of the
-//     step, i = lane%16, head-dim slice [32c + 8*(lane/16), +8).
-//   V rows, instruction f: value row 4f + lane/16 of the step, head-dim slice
-//     [8*(lane%16), +8) -- four whole 256-byte rows per instruction.
+// Per 32-token step (D = 128) a wavefront issues (per lane) 8 + 8 16-byte loads, key rows and
+// value rows alike: instruction f reads row 4f + lane/16 of the step, head-dim slice
+// [8*(lane%16), +8) -- four whole 256-byte rows per instruction. (Loading the keys straight in
+// the score operand's layout -- 16 rows x 64 bytes per instruction -- streamed about 10 % slower
+// in a gather probe of the same tiles: 6.1-6.3 against 6.8 TB/s.) The key rows go through the
+// wavefront's LDS tile and come back as the score MFMA's A operand: sub-tile a (0/1), d-chunk c
+// is key row tau(a, i) = 8*(i/4) + 4a + i%4 of the step, i = lane%16, head-dim slice
+// [32c + 8*(lane/16), +8) (16-byte pieces XOR-swizzled per row, key_piece).
 // Scores S^T[token][head] = K . Q^T come out of v_mfma_f32_16x16x32 with lane l holding head
 // l%16 and tokens 8*(l/16) + 4a + e (e = 0..3), i.e. 8 consecutive tokens, which is the B
 // operand layout of the P.V MFMA (O^T[d][head] += V^T . P^T): the probabilities need no data
 // exchange. Its A operand wants, per lane, those 8 tokens of one head-dim column: the value
-// rows go through a per-wavefront LDS tile (32-byte pieces XOR-swizzled by row so that both
-// the row writes and the column reads spread over the banks) and come back transposed with
+// rows go through the same per-wavefront LDS tile after the keys (32-byte pieces XOR-swizzled by
+// row so that both the row writes and the column reads spread over the banks) and come back
+// transposed with
 // ds_read_b64_tr_b16 (in each 16-lane group, lane i receives element i%4 of the 4 x 16-bit
 // words that lanes 4k + i/4 address, k = 0..3: lanes 4k + c address token row k, head-dim
 // columns 4c .. 4c + 3 of the 16-column chunk).
@@ -39,8 +43,8 @@ namespace pkv {
 
 template <int D>
 struct StepRegs {
-  u32x4 k[2][D / 32];   // K operand per sub-tile and d-chunk
-  u32x4 v[D / 16];      // value rows, 16 bytes per lane per instruction
+  u32x4 k[D / 16];      // key rows, 16 bytes per lane per instruction
+  u32x4 v[D / 16];      // value rows, the same
   u32x4 q[D / 32];      // Q operand (the step's query rows)
 };
 
@@ -109,10 +113,7 @@ void decode_mfma(DecodeParams p) {
   const size_t kv_block_stride = (size_t)B * D * ES;   // bytes per (block, head)
   const int tokA0 = 8 * (r16 >> 2) + (r16 & 3);        // sub-tile 0 key row (sub-tile 1: +4)
   const int vtok = 8 * jg;                             // first of this lane's 8 value tokens
-  // per-lane byte offsets inside a (block, head) tile
-  const int kofs0 = ((tokA0 & (B - 1)) * D + 8 * jg) * ES;
-  const int kofs1 = (((tokA0 + 4) & (B - 1)) * D + 8 * jg) * ES;
-  constexpr int VLPR = D / 8;           // lanes per value row (16 bytes each)
+  constexpr int VLPR = D / 8;           // lanes per key / value row (16 bytes each)
   constexpr int VTPI = 64 / VLPR;       // value rows per load instruction
   constexpr int RB = D * ES;            // bytes per value row
   const int vrow = lane / VLPR;
@@ -129,15 +130,26 @@ void decode_mfma(DecodeParams p) {
   char* ring = reinterpret_cast<char*>(smem) + ring_offset(S) + (size_t)W * 32 * RB +
                (size_t)wave * R * (16 + (size_t)EF * 4);
   int64_t* rhdr = reinterpret_cast<int64_t*>(ring);
-  // value staging tile of this wavefront (before the rings), and the per-lane byte offsets of
-  // its row writes (instruction f) and transposed reads (token half hh, piece f: XOR f << 5)
+  // staging tile of this wavefront (before the rings): a step's key rows, then its value rows.
+  // Per-lane byte offsets of the key row writes (instruction f) and score-operand reads
+  // (sub-tile a, d-chunk c), of the value row writes and of the transposed reads (token half
+  // hh, piece f: XOR f << 5)
   char* vstage = reinterpret_cast<char*>(smem) + ring_offset(S) + (size_t)wave * 32 * RB;
-  int vw_ofs[NF];
+  int kw_ofs[NF], vw_ofs[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const int t = VTPI * f + vrow;
+    kw_ofs[f] = t * RB + (key_piece<D>(t, vch) << 4);
     vw_ofs[f] = t * RB + (((vch >> 1) ^ piece_swizzle<D>(t)) << 5) + 16 * (vch & 1);
   }
+  int kr_ofs[2][NC];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int t = tokA0 + 4 * a;
+      kr_ofs[a][c] = t * RB + (key_piece<D>(t, jg + 4 * c) << 4);
+    }
   int vr_ofs[2];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
@@ -167,51 +179,68 @@ void decode_mfma(DecodeParams p) {
   auto qrow_addr = [&](const StepInfo& si) {
     return qbase + (((size_t)si.s * p.num_q_heads + (size_t)si.g * G + qrow) * D + 8 * jg) * ES;
   };
-  auto load_kq = [&](StepRegs<D>& r, const StepInfo& si) {
+  auto load_q = [&](StepRegs<D>& r, const StepInfo& si) {
     const char* qp = qrow_addr(si);
 #pragma unroll
     for (int c = 0; c < NC; ++c) r.q[c] = load16(qp + 32 * c * ES);
+  };
+  // rows of a step from K (kv = 0) or V (kv = 1): instruction f reads row VTPI * f + lane / VLPR
+  auto load_rows = [&](u32x4 (&dst)[NF], const StepInfo& si, int kv) {
     const int b0 = valid_block(si.b0, p.num_blocks) ? si.b0 : 0;   // out-of-range: block 0,
     const int b1 = valid_block(si.b1, p.num_blocks) ? si.b1 : 0;   // then poison
-    const char* t0 = kbase + ((size_t)b0 * Hkv + si.g) * kv_block_stride;
-    const char* t1 = kbase + ((size_t)b1 * Hkv + si.g) * kv_block_stride;
-    const char* ka = ((B == 16 && tokA0 >= 16) ? t1 : t0) + kofs0;
-    const char* kb = ((B == 16 && tokA0 + 4 >= 16) ? t1 : t0) + kofs1;
-    if (p.k_new && si.k == si.ns - 1) {   // fused append: the newest token's row from k_new
-      const int tn = si.L - 1 - 32 * si.k;
-      const char* kn = reinterpret_cast<const char*>(p.k_new) +
-                       ((size_t)si.s * Hkv + si.g) * RB + 8 * jg * ES;
-      if (tokA0 == tn) ka = kn;
-      if (tokA0 + 4 == tn) kb = kn;
-    }
-    if (si.past) {
-      ka = qp;
-      kb = qp;
-    }
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      r.k[0][c] = STREAM ? load16_stream(ka + 32 * c * ES) : load16(ka + 32 * c * ES);
-      r.k[1][c] = STREAM ? load16_stream(kb + 32 * c * ES) : load16(kb + 32 * c * ES);
-    }
-  };
-  auto load_v = [&](StepRegs<D>& r, const StepInfo& si) {
-    const int b0 = valid_block(si.b0, p.num_blocks) ? si.b0 : 0;
-    const int b1 = valid_block(si.b1, p.num_blocks) ? si.b1 : 0;
-    const bool sub = p.k_new && si.k == si.ns - 1;   // fused append (see load_kq)
+    // fused append: in a segment's last step, the newest token's row from k_new / v_new
+    const bool sub = p.k_new && si.k == si.ns - 1;
     const int tn = si.L - 1 - 32 * si.k;
     const char* qp = qrow_addr(si);
+    const char* base = kv ? vbase : kbase;
+    const char* nrow = reinterpret_cast<const char*>(kv ? p.v_new : p.k_new) +
+                       ((size_t)si.s * Hkv + si.g) * RB + 16 * vch;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int t = VTPI * f + vrow;
       const int blk = (B == 16 && t >= 16) ? b1 : b0;
-      const char* a = vbase + ((size_t)blk * Hkv + si.g) * kv_block_stride +
+      const char* a = base + ((size_t)blk * Hkv + si.g) * kv_block_stride +
                       (size_t)(t & (B - 1)) * RB + 16 * vch;
-      if (sub && t == tn)
-        a = reinterpret_cast<const char*>(p.v_new) + ((size_t)si.s * Hkv + si.g) * RB + 16 * vch;
+      if (sub && t == tn) a = nrow;
       if (si.past) a = qp;
-      r.v[f] = STREAM ? load16_stream(a) : load16(a);
+      dst[f] = STREAM ? load16_stream(a) : load16(a);
     }
   };
+  // STREAM: key rows (through the LDS tile); otherwise straight in the score operand's layout,
+  // r.k[NC * a + c] = sub-tile a, d-chunk c -- for blocks re-read from the caches, whose latency
+  // bound the extra LDS round trip would lengthen
+  const int kofs0 = ((tokA0 & (B - 1)) * D + 8 * jg) * ES;
+  const int kofs1 = (((tokA0 + 4) & (B - 1)) * D + 8 * jg) * ES;
+  auto load_k = [&](StepRegs<D>& r, const StepInfo& si) {
+    if constexpr (STREAM) {
+      load_rows(r.k, si, 0);
+    } else {
+      const int b0 = valid_block(si.b0, p.num_blocks) ? si.b0 : 0;
+      const int b1 = valid_block(si.b1, p.num_blocks) ? si.b1 : 0;
+      const char* t0 = kbase + ((size_t)b0 * Hkv + si.g) * kv_block_stride;
+      const char* t1 = kbase + ((size_t)b1 * Hkv + si.g) * kv_block_stride;
+      const char* ka = ((B == 16 && tokA0 >= 16) ? t1 : t0) + kofs0;
+      const char* kb = ((B == 16 && tokA0 + 4 >= 16) ? t1 : t0) + kofs1;
+      if (p.k_new && si.k == si.ns - 1) {   // fused append, as in load_rows
+        const int tn = si.L - 1 - 32 * si.k;
+        const char* kn = reinterpret_cast<const char*>(p.k_new) +
+                         ((size_t)si.s * Hkv + si.g) * RB + 8 * jg * ES;
+        if (tokA0 == tn) ka = kn;
+        if (tokA0 + 4 == tn) kb = kn;
+      }
+      if (si.past) {
+        const char* qp = qrow_addr(si);
+        ka = qp;
+        kb = qp;
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        r.k[c] = load16(ka + 32 * c * ES);
+        r.k[NC + c] = load16(kb + 32 * c * ES);
+      }
+    }
+  };
+  auto load_v = [&](StepRegs<D>& r, const StepInfo& si) { load_rows(r.v, si, 1); };
 
   // Write the staged piece results: every store instruction covers 1 KB of contiguous memory
   // (the G rows of one (sequence, KV head) are adjacent in the output and in a partial slot).
@@ -271,23 +300,45 @@ void decode_mfma(DecodeParams p) {
   };
 
   // Step si from buffer r; the loads of step nx (two steps ahead) go into r as soon as each
-  // part of r has been consumed: K and Q after the score MFMAs, V after its rows went to LDS.
-  // The softmax and P.V of this step then run with two steps of loads in flight.
+  // part of r has been consumed: K once its rows are in LDS, Q after the score MFMAs, V once its
+  // rows are in LDS. The softmax and P.V of this step then run with two steps of loads in
+  // flight.
   auto compute_step = [&](StepRegs<D>& r, const StepInfo& si, const StepInfo& nx) {
     const int nvalid = si.L - 32 * si.k;             // valid tokens in this step (>= 1)
     poison = poison || !valid_block(si.b0, p.num_blocks) ||
              (B == 16 && nvalid > 16 && !valid_block(si.b1, p.num_blocks));
+    // key rows into the LDS tile, then back as the score MFMA's A operands
+    u32x4 kop[2][NC];
+    if constexpr (STREAM) {
+      wave_lds_sync();   // the previous step's transposed reads come first
+#pragma unroll
+      for (int f = 0; f < NF; ++f) *reinterpret_cast<u32x4*>(vstage + kw_ofs[f]) = r.k[f];
+      load_k(r, nx);
+      wave_lds_sync();
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          kop[a][c] = *reinterpret_cast<const u32x4*>(vstage + kr_ofs[a][c]);
+    } else {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) kop[a][c] = r.k[NC * a + c];
+    }
     f32x4 sacc[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       sacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) sacc[a] = mfma16x16x32<T>(r.k[a][c], r.q[c], sacc[a]);
+      for (int c = 0; c < NC; ++c) sacc[a] = mfma16x16x32<T>(kop[a][c], r.q[c], sacc[a]);
     }
-    load_kq(r, nx);
-    // value rows into the LDS tile, then back as A operands (head-dim column 16f + lane%16,
-    // tokens 8*(lane/16) .. +8 of the step)
-    wave_lds_sync();   // the previous step's transposed reads come first
+    if constexpr (!STREAM) load_k(r, nx);
+    load_q(r, nx);
+    // value rows into the LDS tile (over the key rows, whose reads come first, and the previous
+    // step's transposed reads), then back as A operands (head-dim column 16f + lane%16, tokens
+    // 8*(lane/16) .. +8 of the step)
+    wave_lds_sync();
 #pragma unroll
     for (int f = 0; f < NF; ++f) *reinterpret_cast<u32x4*>(vstage + vw_ofs[f]) = r.v[f];
     load_v(r, nx);
@@ -391,9 +442,11 @@ void decode_mfma(DecodeParams p) {
   StepRegs<D> BA, BB;
   StepInfo sa = ss.next();
   StepInfo sb = ss.next();
-  load_kq(BA, sa);
+  load_q(BA, sa);
+  load_k(BA, sa);
   load_v(BA, sa);
-  load_kq(BB, sb);
+  load_q(BB, sb);
+  load_k(BB, sb);
   load_v(BB, sb);
   StepInfo sc = ss.next();
   for (int64_t i = 0; i + 2 <= nsteps; i += 2) {

@@ -1,6 +1,7 @@
-// Matrix-core building blocks shared by the decode kernel and the shared-prefix kernel:
-// the 16x16x32 MFMA on 16-bit operands, the swizzled per-wavefront value tile in LDS that is
-// read back transposed, and the split of fp32 probabilities into two 16-bit operands.
+// Matrix-core building blocks shared by the decode kernel and the row-state kernels: the
+// 16x16x32 MFMA on 16-bit operands, the swizzled LDS layouts of key rows (read back as score
+// operands) and value rows (read back transposed), and the split of fp32 probabilities into
+// two 16-bit operands.
 #pragma once
 
 #include "device_common.h"
@@ -25,6 +26,15 @@ template <int D>
 __device__ __forceinline__ int piece_swizzle(int t) {
   if constexpr (D == 128) return (t & 3) | (((t >> 3) & 1) << 2);
   else return ((t >> 1) & 1) | (((t >> 3) & 1) << 1);
+}
+
+// Position of 16-byte piece c of key row t in an LDS key tile: pieces XOR-swizzled per row so
+// that the 16 rows one score-operand read touches (t = 8q + 4a + 0..3, q = 0..3) fall on
+// distinct banks, and the 16 pieces of one row written by 16 lanes stay distinct.
+template <int D>
+__device__ __forceinline__ int key_piece(int t, int c) {
+  if constexpr (D == 128) return c ^ ((t & 3) | (((t >> 3) & 3) << 2));
+  else return c ^ (((t >> 1) & 1) | (((t >> 3) & 3) << 1));
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));

@@ -537,15 +537,6 @@ void row_states(RowStateParams p) {
   }
 }
 
-// Position of 16-byte piece c of key row t in the LDS key tile: pieces XOR-swizzled per row so
-// that the 16 rows one score-operand read touches (t = 8q + 4a + 0..3, q = 0..3) fall on
-// distinct banks.
-template <int D>
-__device__ __forceinline__ int key_piece(int t, int c) {
-  if constexpr (D == 128) return c ^ ((t & 3) | (((t >> 3) & 3) << 2));
-  else return c ^ (((t >> 1) & 1) | (((t >> 3) & 3) << 1));
-}
-
 // extend_rows_shared: extend attention for long runs of new tokens (a prefill chunk), where one
 // sequence's (new token, head) rows of a KV head number at least kWideRows. The four wavefronts
 // of a workgroup take four different 32-row tiles (rows rg * 128 + 32 * wave + 16 * rb + r16)
