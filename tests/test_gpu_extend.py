@@ -51,6 +51,8 @@ CASES = [
     ([31, 70, 9, 513], [8, 8, 8, 8], 32, 2, 64, 16, "f16"),       # G = 16
     ([2048, 1, 129], [12, 1, 64], 64, 8, 128, 16, "bf16"),
     ([77, 200], [40, 9], 24, 4, 64, 32, "bf16"),                  # G = 6
+    ([150, 400, 60], [130, 200, 60], 4, 4, 128, 16, "bf16"),      # G = 1, whole-run prefill
+    ([150, 400, 60], [100, 127, 60], 4, 4, 64, 32, "f16"),        # G = 1, one row short
 ]
 
 
@@ -222,19 +224,26 @@ def test_shared_prefix_and_extend_replay_in_a_hip_graph():
     b = W.shared_prefix_batch([9, 120, 3, 300], 96, 16, 2, 128, 16, torch.bfloat16, seed=81,
                               poison=True)
     db = DeviceBatch(b)
+    # 12 new tokens x G = 8 rows per KV head: the row-state kernel; 20 x 8: the shared-tile one
     q, start = W.extend_queries(b, [5, 9, 3, 12], seed=82)
+    q2, start2 = W.extend_queries(b, [20, 17, 3, 18], seed=83)
     qd, sd = q.cuda(), torch.from_numpy(start).cuda()
+    qd2, sd2 = q2.cuda(), torch.from_numpy(start2).cuda()
     pre = db.tables[0, :6].contiguous()
     out_sp = torch.empty(db.q.shape, dtype=torch.float32, device="cuda")
     out_ex = torch.empty(qd.shape, dtype=torch.bfloat16, device="cuda")
+    out_ex2 = torch.empty(qd2.shape, dtype=torch.float32, device="cuda")
     ws_sp = pkv.shared_prefix_workspace(b.num_seqs, 16, 2, 128, 96)
     ws_ex = pkv.extend_workspace(b.num_seqs, qd.shape[0], 16, 2, 128, 12, db.max_ctx)
+    ws_ex2 = pkv.extend_workspace(b.num_seqs, qd2.shape[0], 16, 2, 128, 20, db.max_ctx)
 
     def step():
         pkv.paged_attn_decode_shared_prefix(out_sp, db.q, db.k_pool, db.v_pool, pre, 96,
                                             db.tables, db.lens, db.max_ctx, workspace=ws_sp)
         pkv.paged_attn_extend(out_ex, qd, sd, 12, db.k_pool, db.v_pool, db.tables, db.lens,
                               db.max_ctx, workspace=ws_ex)
+        pkv.paged_attn_extend(out_ex2, qd2, sd2, 20, db.k_pool, db.v_pool, db.tables, db.lens,
+                              db.max_ctx, workspace=ws_ex2)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -242,17 +251,21 @@ def test_shared_prefix_and_extend_replay_in_a_hip_graph():
         step()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    ref_sp, ref_ex = out_sp.clone(), out_ex.clone()
+    ref_sp, ref_ex, ref_ex2 = out_sp.clone(), out_ex.clone(), out_ex2.clone()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
     for _ in range(3):
         out_sp.fill_(float("nan"))
         out_ex.fill_(float("nan"))
+        out_ex2.fill_(float("nan"))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(bits(out_sp.cpu()), bits(ref_sp.cpu()))
         assert torch.equal(bits(out_ex.cpu()), bits(ref_ex.cpu()))
-    assert max_err(ref_sp.cpu(), oracle.shared_prefix_decode(
-        b.q, b.k_pool, b.v_pool, b.tables[0][:6], 96, b.tables, b.lengths, 16)) <= 2e-3
+        assert torch.equal(bits(out_ex2.cpu()), bits(ref_ex2.cpu()))
+    kw, vw = widened(b.k_pool), widened(b.v_pool)
+    assert max_err(ref_sp.cpu(), oracle.paged_decode(b.q, kw, vw, b.tables, b.lengths, 16)) <= 2e-3
+    assert max_err(ref_ex2.cpu(), oracle.extend_attention(q2, start2, b.k_pool, b.v_pool, b.tables,
+                                                          b.lengths, 16)) <= 2e-3
