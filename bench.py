@@ -39,6 +39,7 @@ METRIC = "paged decode attention KV GB/s (fraction of HBM peak) and seq-steps/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_mfma_gqa256_b16_traffic.json")
 KERNEL_SOURCES = ["paged_kv_cache_127_amd/csrc/decode_mfma.hip",
                   "paged_kv_cache_127_amd/csrc/device_common.h",
+                  "paged_kv_cache_127_amd/csrc/mfma_common.h",
                   "paged_kv_cache_127_amd/csrc/schedule.h"]
 
 
