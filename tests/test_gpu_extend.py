@@ -217,6 +217,25 @@ def test_rejections_and_validation():
     assert float(np.abs(out.cpu().double().numpy() - ref).max()) <= 2e-3
 
 
+@pytest.mark.parametrize("new", [[6, 5, 9], [20, 17, 30]], ids=["row-state", "shared-tile"])
+def test_out_of_range_table_entry_gives_nan_rows(new):
+    """An out-of-range block id among the blocks a sequence's new tokens attend (its first
+    block, which every causal row sees) poisons that sequence's rows (NaN) without any access
+    outside the pools; the other sequences match the oracle. Both kernels: 9 x 8 rows per KV
+    head take the row-state kernel, 30 x 8 the shared-tile one."""
+    b = W.small_batch([300, 90, 500], 16, 2, 128, 16, torch.bfloat16, seed=41)
+    q, start = W.extend_queries(b, new, seed=42)
+    db = DeviceBatch(b)
+    db.tables = db.tables.clone()
+    db.tables[1, 0] = b.num_blocks + 7
+    got = _run(db, q, start)
+    assert torch.isnan(got[int(start[1]):int(start[2])]).all()
+    ref = oracle.extend_attention(q, start, b.k_pool, b.v_pool, b.tables, b.lengths, 16)
+    for s in (0, 2):
+        r = slice(int(start[s]), int(start[s + 1]))
+        assert float(np.abs(got[r].double().numpy() - ref[r]).max()) <= 2e-3
+
+
 def test_shared_prefix_and_extend_replay_in_a_hip_graph():
     """Both calls allocate nothing, launch only on the caller's stream and record no memset:
     captured together in a HIP graph, three replays (with eager work and synchronisations
