@@ -345,7 +345,38 @@ def swap_figures(pkv, W, torch, dev: str, preempt: int = 32, launches: int = 10)
     dms, dn = pkv.timing_query("decode_partial")
     sms, sn = pkv.timing_query("swap_out")
     pkv.timing_enable(False)
-    del q, tab, lens, out, ws
+    # the copy-engine variant (host run 0..n-1): call time from torch events on its stream, and
+    # the decode with copy-engine swap-outs on the second stream meanwhile
+    staging = pkv.swap_staging(n, kp)
+
+    def call_us(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(launches)]
+        for a, e in ev:
+            a.record()
+            fn()
+            e.record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(e) * 1e3 for a, e in ev)
+        return t[len(t) // 2]
+
+    dma_out_us = call_us(lambda: pkv.kv_swap_out_dma(kp, vp, hk, hv, dev_ids, 0, staging))
+    dma_in_us = call_us(lambda: pkv.kv_swap_in_dma(kp, vp, hk, hv, 0, back_ids, staging))
+    pkv.timing_enable(True, every=1)
+    for _ in range(3):
+        pkv.kv_swap_out_dma(kp, vp, hk, hv, dev_ids, 0, staging, stream=s2)
+    for _ in range(20):
+        dec()
+    torch.cuda.synchronize()
+    dms2, dn2 = pkv.timing_query("decode_partial")
+    pkv.timing_enable(False)
+    dma_moved = (torch.equal(hk[n - 1].view(torch.int16), b.k_pool[blocks[-1]].view(torch.int16))
+                 and torch.equal(kp[free[0]].cpu().view(torch.int16),
+                                 b.k_pool[blocks[0]].view(torch.int16)))
+    del q, tab, lens, out, ws, staging
     moved = (torch.equal(hk[0].view(torch.int16), b.k_pool[blocks[0]].view(torch.int16)) and
              torch.equal(kp[free[-1]].cpu().view(torch.int16),
                          b.k_pool[blocks[-1]].view(torch.int16)))
@@ -387,9 +418,19 @@ def swap_figures(pkv, W, torch, dev: str, preempt: int = 32, launches: int = 10)
                     "decode_us_alone": round(dec_alone, 2),
                     "decode_us_during_swap": round(dms / dn * 1e3, 2),
                     "swap_out_gbs_during_decode": gbs(sms / sn * 1e3)},
+        "copy_engine": {"what": "kv_swap_out_dma / kv_swap_in_dma of the same blocks (gather or "
+                                "scatter through a device staging buffer, one DMA copy per "
+                                "pool); call time from torch events",
+                        "data_checked": bool(dma_moved),
+                        "swap_out_us": round(dma_out_us, 2), "swap_out_gbs": gbs(dma_out_us),
+                        "swap_in_us": round(dma_in_us, 2), "swap_in_gbs": gbs(dma_in_us),
+                        "decode_us_during_swap": round(dms2 / dn2 * 1e3, 2)},
     }
     print(f"bench: swap out {res['swap_out_gbs']} GB/s in {res['swap_in_gbs']} GB/s "
-          f"(DMA {res['dma_d2h_gbs']} / {res['dma_h2d_gbs']})", file=sys.stderr, flush=True)
+          f"(DMA {res['dma_d2h_gbs']} / {res['dma_h2d_gbs']}); copy-engine swap out "
+          f"{res['copy_engine']['swap_out_gbs']} in {res['copy_engine']['swap_in_gbs']} GB/s, "
+          f"decode meanwhile {res['copy_engine']['decode_us_during_swap']} us",
+          file=sys.stderr, flush=True)
     return res
 
 

@@ -297,6 +297,39 @@ int kv_swap_in(void* k_pool, void* v_pool, int kv_dtype, const void* host_k, con
                int num_pairs, int num_kv_heads, int head_dim, int block_size, int num_blocks,
                void* stream);
 
+/* Block swap through the copy engines (the same section of "Paged Attention and vLLM"). The
+ * same transfer as kv_swap_out / kv_swap_in for a contiguous run of host blocks
+ * [host_block0, host_block0 + num_pairs): the device side goes through a caller-owned staging
+ * buffer (one launch gathers device_blocks[i] into staging block i, or scatters staging block
+ * i to device_blocks[i]; keys first, then values, each num_pairs blocks), and the host side is
+ * one DMA copy per pool between the staging buffer and the host run (hipMemcpyAsync on
+ * `stream`). The host link is then carried by the copy engines instead of compute units, so a
+ * decode running on another stream meanwhile keeps its CUs for all but the short gather or
+ * scatter launch.
+ *   staging         device memory of at least pkv_swap_staging_size(...) bytes, 16-byte
+ *                   aligned, caller-owned; its contents are scratch.
+ *   host_k, host_v  as for kv_swap_out: pinned host memory of num_host_blocks blocks
+ *                   (PKV_ERR_INVALID_ARG otherwise, before anything is enqueued).
+ *   device_blocks   int32 [num_pairs], device memory. kv_swap_in_dma's must be distinct. An
+ *                   id outside [0, num_blocks) is skipped on the device side: kv_swap_in_dma
+ *                   writes no device block for it, and kv_swap_out_dma's host block for it
+ *                   receives whatever its staging block held (PAGEDKV_VALIDATE=1 rejects both).
+ * Errors: PKV_ERR_INVALID_ARG (sizes, null or misaligned pointers, a host run outside
+ * [0, num_host_blocks)), PKV_ERR_WORKSPACE_TOO_SMALL (staging), PKV_ERR_LAUNCH. Asynchronous:
+ * the copy is complete when the stream reaches it. */
+size_t pkv_swap_staging_size(int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                             int kv_dtype);
+int kv_swap_out_dma(const void* k_pool, const void* v_pool, int kv_dtype, void* host_k,
+                    void* host_v, int num_host_blocks, const int32_t* device_blocks,
+                    int host_block0, int num_pairs, int num_kv_heads, int head_dim,
+                    int block_size, int num_blocks, void* staging, size_t staging_bytes,
+                    void* stream);
+int kv_swap_in_dma(void* k_pool, void* v_pool, int kv_dtype, const void* host_k,
+                   const void* host_v, int num_host_blocks, int host_block0,
+                   const int32_t* device_blocks, int num_pairs, int num_kv_heads, int head_dim,
+                   int block_size, int num_blocks, void* staging, size_t staging_bytes,
+                   void* stream);
+
 /* ---------------------------------------------------------------------------------------
  * Host block pool: free list and reference counts of `num_blocks` physical block ids. No
  * device memory. A block returns to the free list only when its count reaches zero

@@ -15,7 +15,8 @@ import torch  # loaded first: the library then binds to the HIP runtime torch al
 
 __all__ = [
     "PagedKVError", "paged_attn_decode", "paged_attn_decode_append", "kv_cache_append",
-    "cow_block_copy", "kv_swap_out", "kv_swap_in", "paged_attn_decode_shared_prefix",
+    "cow_block_copy", "kv_swap_out", "kv_swap_in", "kv_swap_out_dma", "kv_swap_in_dma",
+    "swap_staging", "paged_attn_decode_shared_prefix",
     "shared_prefix_workspace", "paged_attn_extend", "paged_attn_decode_noalloc",
     "DECODE_STATIC_SCRATCH", "extend_workspace", "pkv_decode_workspace_size", "decode_workspace",
     "pkv_decode_auto_workers", "BlockPool", "timing_enable", "timing_query",
@@ -82,6 +83,11 @@ def _declare(L):
                                 c_int, c_int, c_int, c_int, c_int, c_void]),
         "kv_swap_in": (c_int, [c_void, c_void, c_int, c_void, c_void, c_int, c_void, c_void,
                                c_int, c_int, c_int, c_int, c_int, c_void]),
+        "pkv_swap_staging_size": (c_size, [c_int, c_int, c_int, c_int, c_int]),
+        "kv_swap_out_dma": (c_int, [c_void, c_void, c_int, c_void, c_void, c_int, c_void, c_int,
+                                    c_int, c_int, c_int, c_int, c_int, c_void, c_size, c_void]),
+        "kv_swap_in_dma": (c_int, [c_void, c_void, c_int, c_void, c_void, c_int, c_int, c_void,
+                                   c_int, c_int, c_int, c_int, c_int, c_void, c_size, c_void]),
         "pkv_prefix_index_create": (c_void, [c_void, c_int]),
         "pkv_prefix_index_destroy": (None, [c_void]),
         "pkv_prefix_index_match": (c_int, [c_void, i32p, c_int, i32p, c_int, P(c_int)]),
@@ -431,6 +437,52 @@ def kv_swap_in(k_pool, v_pool, host_k, host_v, host_blocks, device_blocks, strea
     pools (C: ``kv_swap_in``)."""
     _swap(load_library().kv_swap_in, k_pool, v_pool, host_k, host_v, host_blocks,
           device_blocks, stream)
+
+
+def swap_staging(num_pairs: int, k_pool: torch.Tensor) -> torch.Tensor:
+    """Staging buffer for the copy-engine swap of ``num_pairs`` blocks of ``k_pool``'s shape."""
+    N, Hkv, B, d = k_pool.shape
+    n = load_library().pkv_swap_staging_size(int(num_pairs), Hkv, d, B, _kv_dtype(k_pool))
+    return torch.empty(max(int(n), 16), dtype=torch.uint8, device=k_pool.device)
+
+
+def _swap_dma(fn, out, k_pool, v_pool, host_k, host_v, device_blocks, host_block0, staging,
+              stream):
+    N, Hkv, B, d = k_pool.shape
+    if v_pool.shape != k_pool.shape or host_v.shape != host_k.shape:
+        raise ValueError("K and V pools must have equal shapes")
+    if device_blocks.dim() != 1:
+        raise ValueError("device_blocks must be [num_pairs]")
+    n = int(device_blocks.shape[0])
+    hk, hv = _host_pool(host_k, "host_k", k_pool), _host_pool(host_v, "host_v", k_pool)
+    ids = _dev(device_blocks, "device_blocks", torch.int32)
+    st = _dev(staging, "staging", torch.uint8)
+    nh = int(host_k.shape[0])
+    if out:
+        rc = fn(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype), _kv_dtype(k_pool),
+                hk, hv, nh, ids, int(host_block0), n, Hkv, d, B, N, st, staging.numel(),
+                _stream(stream))
+    else:
+        rc = fn(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype), _kv_dtype(k_pool),
+                hk, hv, nh, int(host_block0), ids, n, Hkv, d, B, N, st, staging.numel(),
+                _stream(stream))
+    _check(rc)
+
+
+def kv_swap_out_dma(k_pool, v_pool, host_k, host_v, device_blocks, host_block0, staging,
+                    stream=None):
+    """Copy blocks device_blocks[i] to host blocks host_block0 + i through ``staging`` and the
+    copy engines (C: ``kv_swap_out_dma``)."""
+    _swap_dma(load_library().kv_swap_out_dma, True, k_pool, v_pool, host_k, host_v,
+              device_blocks, host_block0, staging, stream)
+
+
+def kv_swap_in_dma(k_pool, v_pool, host_k, host_v, host_block0, device_blocks, staging,
+                   stream=None):
+    """Copy host blocks host_block0 + i to device_blocks[i] through ``staging`` and the copy
+    engines (C: ``kv_swap_in_dma``)."""
+    _swap_dma(load_library().kv_swap_in_dma, False, k_pool, v_pool, host_k, host_v,
+              device_blocks, host_block0, staging, stream)
 
 
 def stream_read_probe(src: torch.Tensor, sink: torch.Tensor, stream=None):

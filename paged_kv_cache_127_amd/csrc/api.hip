@@ -668,6 +668,79 @@ int swap_impl(const char* fn, bool to_host, void* k_pool, void* v_pool, int kv_d
   return ok();
 }
 
+// Copy-engine swap: the device side through a contiguous staging buffer (one gather or scatter
+// launch), the host side one DMA copy per pool between the staging buffer and a contiguous run
+// of host blocks, so that no compute unit waits on the host link.
+int swap_dma_impl(const char* fn, bool to_host, void* k_pool, void* v_pool, int kv_dtype,
+                  void* host_k, void* host_v, int num_host_blocks, int host_block0,
+                  const int32_t* device_blocks, int num_pairs, int num_kv_heads, int head_dim,
+                  int block_size, int num_blocks, void* staging, size_t staging_bytes,
+                  void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0 || num_host_blocks <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "%s: non-positive size", fn);
+  if (!k_pool || !v_pool || !host_k || !host_v || !device_blocks || !staging)
+    return fail(PKV_ERR_INVALID_ARG, "%s: null pointer", fn);
+  const int es = elem_bytes(kv_dtype);
+  if (es == 0) return fail(PKV_ERR_UNSUPPORTED, "%s: kv_dtype %d", fn, kv_dtype);
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * es;
+  if (block_bytes % 16 != 0 || block_bytes / 16 >= ((int64_t)1 << 31))
+    return fail(PKV_ERR_UNSUPPORTED, "%s: block of %lld bytes", fn, (long long)block_bytes);
+  if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool) |
+       reinterpret_cast<uintptr_t>(host_k) | reinterpret_cast<uintptr_t>(host_v) |
+       reinterpret_cast<uintptr_t>(staging)) & 15)
+    return fail(PKV_ERR_INVALID_ARG, "%s: pools and staging must be 16-byte aligned", fn);
+  if (host_block0 < 0 || (int64_t)host_block0 + num_pairs > num_host_blocks)
+    return fail(PKV_ERR_INVALID_ARG, "%s: host blocks [%d, %lld) outside [0, %d)", fn,
+                host_block0, (long long)host_block0 + num_pairs, num_host_blocks);
+  const size_t run = (size_t)num_pairs * (size_t)block_bytes;
+  if (staging_bytes < 2 * run)
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "%s: staging %zu < %zu bytes", fn, staging_bytes,
+                2 * run);
+  if (num_pairs == 0) return ok();
+  if (!mapped_host_address(host_k) || !mapped_host_address(host_v))
+    return fail(PKV_ERR_INVALID_ARG, "%s: host_k / host_v must be pinned host memory", fn);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (validate_mode()) {
+    std::vector<int32_t> ids;
+    if (!copy_ints(ids, device_blocks, num_pairs, st))
+      return fail(PKV_ERR_LAUNCH, "%s: validation copy failed", fn);
+    std::unordered_set<int32_t> seen;
+    for (int i = 0; i < num_pairs; ++i) {
+      if (ids[i] < 0 || ids[i] >= num_blocks)
+        return fail(PKV_ERR_VALIDATION, "pair %d: device block %d outside [0, %d)", i, ids[i],
+                    num_blocks);
+      if (!to_host && !seen.insert(ids[i]).second)
+        return fail(PKV_ERR_VALIDATION, "pair %d: destination used twice", i);
+    }
+  }
+  char* sk = reinterpret_cast<char*>(staging);
+  char* sv = sk + run;
+  char* hk = reinterpret_cast<char*>(host_k) + (size_t)host_block0 * (size_t)block_bytes;
+  char* hv = reinterpret_cast<char*>(host_v) + (size_t)host_block0 * (size_t)block_bytes;
+  const int cus = cu_count();
+  const int units = (int)(block_bytes / 16);
+  hipError_t e;
+  if (to_host) {
+    const pkv::SwapParams p{k_pool, v_pool, sk, sv, device_blocks, nullptr, num_pairs,
+                            num_blocks, num_pairs, units};
+    e = timed("swap_gather", st, [&] { return pkv::launch_block_copy(p, cus, st); });
+    if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "%s: gather: %s", fn, hipGetErrorString(e));
+    e = hipMemcpyAsync(hk, sk, run, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(hv, sv, run, hipMemcpyDeviceToHost, st);
+    if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "%s: copy: %s", fn, hipGetErrorString(e));
+  } else {
+    e = hipMemcpyAsync(sk, hk, run, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(sv, hv, run, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "%s: copy: %s", fn, hipGetErrorString(e));
+    const pkv::SwapParams p{sk, sv, k_pool, v_pool, nullptr, device_blocks, num_pairs,
+                            num_pairs, num_blocks, units};
+    e = timed("swap_scatter", st, [&] { return pkv::launch_block_copy(p, cus, st); });
+    if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "%s: scatter: %s", fn, hipGetErrorString(e));
+  }
+  return ok();
+}
+
 // Workspace of the shared-prefix call: the suffix decode's workspace, then the suffix lengths,
 // the suffix rows' log-sum-exp, an fp32 suffix output (used when the output is 16-bit) and the
 // prefix states of every chunk group.
@@ -1013,6 +1086,36 @@ int kv_swap_in(void* k_pool, void* v_pool, int kv_dtype, const void* host_k, con
   return swap_impl("kv_swap_in", false, k_pool, v_pool, kv_dtype, const_cast<void*>(host_k),
                    const_cast<void*>(host_v), num_host_blocks, host_blocks, device_blocks,
                    num_pairs, num_kv_heads, head_dim, block_size, num_blocks, stream);
+}
+
+size_t pkv_swap_staging_size(int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                             int kv_dtype) {
+  const int es = elem_bytes(kv_dtype);
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || es == 0)
+    return 0;
+  return 2 * (size_t)num_pairs * (size_t)num_kv_heads * block_size * head_dim * es;
+}
+
+int kv_swap_out_dma(const void* k_pool, const void* v_pool, int kv_dtype, void* host_k,
+                    void* host_v, int num_host_blocks, const int32_t* device_blocks,
+                    int host_block0, int num_pairs, int num_kv_heads, int head_dim,
+                    int block_size, int num_blocks, void* staging, size_t staging_bytes,
+                    void* stream) {
+  return swap_dma_impl("kv_swap_out_dma", true, const_cast<void*>(k_pool),
+                       const_cast<void*>(v_pool), kv_dtype, host_k, host_v, num_host_blocks,
+                       host_block0, device_blocks, num_pairs, num_kv_heads, head_dim,
+                       block_size, num_blocks, staging, staging_bytes, stream);
+}
+
+int kv_swap_in_dma(void* k_pool, void* v_pool, int kv_dtype, const void* host_k,
+                   const void* host_v, int num_host_blocks, int host_block0,
+                   const int32_t* device_blocks, int num_pairs, int num_kv_heads, int head_dim,
+                   int block_size, int num_blocks, void* staging, size_t staging_bytes,
+                   void* stream) {
+  return swap_dma_impl("kv_swap_in_dma", false, k_pool, v_pool, kv_dtype,
+                       const_cast<void*>(host_k), const_cast<void*>(host_v), num_host_blocks,
+                       host_block0, device_blocks, num_pairs, num_kv_heads, head_dim,
+                       block_size, num_blocks, staging, staging_bytes, stream);
 }
 
 int pkv_set_validate(int on) {

@@ -174,8 +174,8 @@ struct SwapParams {
   const void* src_v;
   void* dst_k;
   void* dst_v;
-  const int32_t* src_ids;
-  const int32_t* dst_ids;
+  const int32_t* src_ids;         // null: pair i reads block i (a staging buffer)
+  const int32_t* dst_ids;         // null: pair i writes block i
   int num_pairs;
   int src_count;   // blocks in the source pool
   int dst_count;   // blocks in the destination pool

@@ -8,7 +8,9 @@
 // H_kv * B * d elements. A (pair, chunk) item is up to 16 KiB of keys and 16 KiB of values of
 // one pair, moved in 16-byte accesses; each lane issues its eight loads before its stores, and
 // each wave instruction covers one contiguous KiB. Pairs with an id outside its pool are
-// skipped (never dereferenced).
+// skipped (never dereferenced). The same kernel gathers blocks into (or scatters them out of) a
+// contiguous device staging buffer for the copy-engine variant, whose host side is one DMA
+// copy per pool (no id list on the staging side: pair i is staging block i).
 #include <algorithm>
 
 #include "device_common.h"
@@ -51,8 +53,8 @@ __global__ __launch_bounds__(kSwapThreads) void block_copy_kernel(SwapParams p, 
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
     const int pair = it / chunks;
     const int chunk = it - pair * chunks;
-    const int s = p.src_ids[pair];
-    const int d = p.dst_ids[pair];
+    const int s = p.src_ids ? p.src_ids[pair] : pair;   // no list: block i of a staging buffer
+    const int d = p.dst_ids ? p.dst_ids[pair] : pair;
     if ((unsigned)s >= (unsigned)p.src_count || (unsigned)d >= (unsigned)p.dst_count) continue;
     const int U = p.units;
     const u32x4* sk = reinterpret_cast<const u32x4*>(p.src_k) + (size_t)s * U;

@@ -1,6 +1,7 @@
-"""GPU parity of block swap (kv_swap_out / kv_swap_in) against the bookkeeping oracle: whole
-pools compared bit for bit, on both sides, including blocks no pair names; a preempt/resume
-cycle whose decode is bit-identical to the decode before preemption; argument rejection."""
+"""GPU parity of block swap (kv_swap_out / kv_swap_in, and the copy-engine kv_swap_out_dma /
+kv_swap_in_dma) against the bookkeeping oracle: whole pools compared bit for bit, on both
+sides, including blocks no pair names; a preempt/resume cycle whose decode is bit-identical to
+the decode before preemption; argument rejection."""
 import numpy as np
 import pytest
 import torch
@@ -86,6 +87,61 @@ def test_swap_in_bit_exact(case):
     assert np.array_equal(bits(dk.cpu()).numpy(), want_k)
     assert np.array_equal(bits(dv.cpu()).numpy(), want_v)
     assert torch.equal(bits(hk), bits(hk0)) and torch.equal(bits(hv), bits(hv0))
+
+
+@pytest.mark.parametrize("case", SHAPES, ids=lambda c: "-".join(map(str, c)))
+def test_copy_engine_swap_bit_exact(case):
+    """kv_swap_out_dma / kv_swap_in_dma against the bookkeeping oracle: device blocks out to a
+    contiguous run of host blocks (host blocks outside the run unchanged), then the run back into
+    other device blocks (device blocks no pair names unchanged), whole pools bit for bit; the
+    staging buffer starts out filled with 0xff."""
+    dt, H, B, d = case
+    N, NH, n, h0 = 40, 24, 11, 6
+    kp, vp = _pools(N, H, B, d, DT[dt], 14)
+    hk0, hv0 = _pools(NH, H, B, d, DT[dt], 15)
+    rng = np.random.default_rng(16)
+    perm = rng.permutation(N).tolist()
+    out_ids, in_ids = perm[:n], perm[n:2 * n]
+    run = list(range(h0, h0 + n))
+    want_hk, want_hv = _np_bits(hk0), _np_bits(hv0)
+    oracle.copy_blocks(want_hk, want_hv, _np_bits(kp), _np_bits(vp), out_ids, run)
+    want_k, want_v = _np_bits(kp), _np_bits(vp)
+    oracle.copy_blocks(want_k, want_v, want_hk, want_hv, run, in_ids)
+    hk, hv = _pinned_like(hk0), _pinned_like(hv0)
+    dk, dv = kp.cuda(), vp.cuda()
+    staging = pkv.swap_staging(n, dk)
+    staging.fill_(255)
+    pkv.kv_swap_out_dma(dk, dv, hk, hv, _ids(out_ids), h0, staging)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(hk).numpy(), want_hk) and np.array_equal(bits(hv).numpy(), want_hv)
+    assert torch.equal(bits(dk.cpu()), bits(kp)) and torch.equal(bits(dv.cpu()), bits(vp))
+    staging.fill_(255)
+    pkv.kv_swap_in_dma(dk, dv, hk, hv, h0, _ids(in_ids), staging)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(dk.cpu()).numpy(), want_k)
+    assert np.array_equal(bits(dv.cpu()).numpy(), want_v)
+
+
+def test_copy_engine_swap_rejections():
+    """A host run past the host pool, a staging buffer one byte short and pageable host pools
+    are rejected before anything is enqueued; nothing is moved."""
+    kp, vp = _pools(10, 2, 16, 64, torch.float16, 17)
+    dk, dv = kp.cuda(), vp.cuda()
+    hk = torch.zeros((6, 2, 16, 64), dtype=torch.float16, pin_memory=True)
+    hv = torch.zeros_like(hk).pin_memory()
+    staging = pkv.swap_staging(4, dk)
+    with pytest.raises(pkv.PagedKVError) as e:
+        pkv.kv_swap_out_dma(dk, dv, hk, hv, _ids([0, 1, 2, 3]), 3, staging)   # run [3, 7) > 6
+    assert e.value.code == -1
+    with pytest.raises(pkv.PagedKVError) as e:
+        pkv.kv_swap_out_dma(dk, dv, hk, hv, _ids([0, 1, 2, 3]), 0, staging[:-1])
+    assert e.value.code == -3
+    pageable = torch.zeros(hk.shape, dtype=hk.dtype)
+    with pytest.raises(ValueError):                    # the binding checks pinning first
+        pkv.kv_swap_in_dma(dk, dv, pageable, hv, 0, _ids([0, 1]), staging)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(hk), bits(torch.zeros_like(hk)))
+    assert torch.equal(bits(dk.cpu()), bits(kp))
 
 
 def test_round_trip_of_many_blocks():
