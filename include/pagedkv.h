@@ -101,7 +101,10 @@ const char* pkv_last_error(void);
  *                 clamped to that range)
  *   max_context_len  host int, an upper bound of context_lens, at most
  *                 max_blocks_per_seq * block_size
- *   num_seqs      at most 4096 per call
+ *   num_seqs      any number: a launch's schedule holds at most 4096 sequences, so a larger
+ *                 batch runs as consecutive launches of at most 4096 on `stream`, each reusing
+ *                 the workspace (sized for the whole batch); the results do not depend on the
+ *                 split. paged_attn_decode_shared_prefix takes at most 4096.
  *   scale         softmax scale; <= 0 selects 1/sqrt(head_dim)
  *   num_workers   0 = automatic (as many wavefronts as the chosen kernel keeps resident on
  *                 the current device, at most 8 per compute unit, and no more than

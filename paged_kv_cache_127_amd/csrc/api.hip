@@ -297,11 +297,33 @@ int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const v
     return fail(PKV_ERR_INVALID_ARG,
                 "%s: max_context_len %d exceeds table capacity %d x %d", fn,
                 max_context_len, max_blocks_per_seq, block_size);
-  if (num_seqs > pkv::kMaxSeqsPerCall)
-    return fail(PKV_ERR_UNSUPPORTED, "%s: %d sequences (at most %d per call)", fn,
-                num_seqs, pkv::kMaxSeqsPerCall);
   if (num_workers < 0 || num_workers > (1 << 20))
     return fail(PKV_ERR_INVALID_ARG, "%s: num_workers %d", fn, num_workers);
+  if (num_seqs > pkv::kMaxSeqsPerCall) {
+    // A launch's schedule keeps its sequences' prefixes in LDS: more sequences run as
+    // consecutive launches of at most kMaxSeqsPerCall sequences on the caller's stream, each
+    // reusing the workspace (sized for all of them, so large enough for any part). Sequences
+    // are independent, so the results are those of one launch over all of them.
+    if (pf)
+      return fail(PKV_ERR_UNSUPPORTED, "%s: %d sequences (at most %d per call)", fn, num_seqs,
+                  pkv::kMaxSeqsPerCall);
+    const size_t qb = (size_t)num_q_heads * head_dim * elem_bytes(kv_dtype);
+    const size_t ob = (size_t)num_q_heads * head_dim * elem_bytes(out_dtype);
+    const size_t nb = (size_t)num_kv_heads * head_dim * elem_bytes(kv_dtype);
+    for (int s0 = 0; s0 < num_seqs; s0 += pkv::kMaxSeqsPerCall) {
+      const int ns = std::min(pkv::kMaxSeqsPerCall, num_seqs - s0);
+      const int rc = decode_impl(
+          fn, reinterpret_cast<char*>(out) + s0 * ob, out_dtype,
+          reinterpret_cast<const char*>(q) + s0 * qb, k_pool, v_pool, kv_dtype,
+          k_new ? reinterpret_cast<const char*>(k_new) + s0 * nb : nullptr,
+          v_new ? reinterpret_cast<const char*>(v_new) + s0 * nb : nullptr,
+          block_tables + (size_t)s0 * max_blocks_per_seq, max_blocks_per_seq,
+          context_lens + s0, max_context_len, ns, num_q_heads, num_kv_heads, head_dim,
+          block_size, num_blocks, scale, num_workers, workspace, workspace_bytes, stream);
+      if (rc != PKV_OK) return rc;
+    }
+    return ok();
+  }
   static const int waves_env = env_int("PAGEDKV_DECODE_WAVES", 4);
   const int waves = (waves_env == 1 || waves_env == 2 || waves_env == 4) ? waves_env : 4;
   int n = num_workers;

@@ -149,6 +149,35 @@ def test_most_sequences_per_call(case):
     assert not torch.isnan(got).any()
 
 
+def test_more_sequences_than_one_launch_holds():
+    """9,000 sequences: three consecutive launches (4096 + 4096 + 808) over one workspace, every
+    row against the oracle, the fused-append variant's stored rows bit-exact, and the result
+    bit-identical to three separate calls over the same parts."""
+    lens = np.random.default_rng(72).integers(1, 40, size=9000)
+    b = W.small_batch(lens, 16, 2, 128, 16, torch.bfloat16, seed=72, poison=True)
+    db = DeviceBatch(b)
+    got = db.decode()
+    assert max_err(got, oracle_decode(b)) <= 2e-3
+    parts = []
+    for s0 in (0, 4096, 8192):
+        s1 = min(s0 + 4096, 9000)
+        parts.append(db.decode(q=db.q[s0:s1], tables=db.tables[s0:s1], lens=db.lens[s0:s1]))
+    assert torch.equal(bits(got.cpu()), bits(torch.cat([x.cpu() for x in parts])))
+    # fused append over the three launches: every sequence's newest row lands in its slot
+    kn, vn = (x.cuda() for x in W.new_tokens(b.seed, 1, 9000, 2, 128, torch.bfloat16))
+    kp, vp = db.k_pool.clone(), db.v_pool.clone()
+    out = torch.empty(db.q.shape, dtype=torch.float32, device="cuda")
+    pkv.paged_attn_decode_append(out, db.q, kp, vp, kn, vn, db.tables, db.lens, db.max_ctx)
+    torch.cuda.synchronize()
+    kr, vr = b.k_pool.clone(), b.v_pool.clone()
+    for s in range(9000):
+        blk, off = oracle.token_address(int(b.lengths[s]) - 1, b.tables[s], 16)
+        kr[blk, :, off] = kn[s].cpu()
+        vr[blk, :, off] = vn[s].cpu()
+    assert torch.equal(bits(kp.cpu()), bits(kr)) and torch.equal(bits(vp.cpu()), bits(vr))
+    assert max_err(out.cpu(), oracle_decode(b, k_pool=kr, v_pool=vr)) <= 2e-3
+
+
 # ---- config 1: the pages' three requests, growth by ten tokens into block 11 ------------
 def test_config1_flow():
     b = W.config1(poison=True)

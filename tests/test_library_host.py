@@ -111,7 +111,8 @@ def test_decode_argument_checks():
     assert _decode_call(Hq=17 * 2, Hkv=2)[0] == -2             # G = 17
     assert _decode_call(max_ctx=129)[0] == -1                  # > 8 blocks of 16
     assert _decode_call(part=-1)[0] == -1                      # negative worker count
-    assert _decode_call(S=5000)[0] == -2                       # more sequences than one call takes
+    rc, msg = _decode_call(S=5000)           # runs as launches of at most 4096 sequences,
+    assert rc == -3 and "workspace" in msg   # each checked against the (missing) workspace
     rc, msg = _decode_call(max_ctx=128, part=32)
     assert rc == -3 and "workspace" in msg
     rc, msg = _decode_call(ws=0x1000, ws_bytes=100, part=32)
