@@ -655,8 +655,9 @@ def headline_workload(name, block_size, W, torch, dev):
 
 def row_state_line(args, pkv, W, torch, dev):
     """One JSON line for a row-state call alone (for profiling the matrix-core kernel):
-    prefix800 / prefix4096 -- paged_attn_decode_shared_prefix on 128 sequences over an 800- or
-    4096-token shared prefix (the prefix-state kernel, the suffix decode and the merge);
+    prefix800 / prefix4096 / prefix8192 -- paged_attn_decode_shared_prefix on 128 sequences over
+    an 800-, 4096- or 8192-token shared prefix (the prefix-state kernel, the suffix decode and
+    the merge);
     prefill -- paged_attn_extend of a 256-token chunk on 8 sequences of 1024..4096 tokens;
     verify -- paged_attn_extend of the last 4 tokens of every sequence of the GQA batch.
     ``value`` is the call's causal-attention rate in TFLOP/s (prefix: the prefix-state kernel's
@@ -741,9 +742,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gqa",
-                    choices=("gqa", "mha", "long", "prefix800", "prefix4096", "prefill", "verify"),
-                    help="batch of the headline line (gqa is the graded one; the last four run "
-                         "the matrix-core row-state calls alone, for profiling them)")
+                    choices=("gqa", "mha", "long", "prefix800", "prefix4096", "prefix8192",
+                             "prefill", "verify"),
+                    help="batch of the headline line (gqa by default; prefix*, prefill and verify "
+                         "run the matrix-core row-state calls alone, for profiling them)")
     ap.add_argument("--block-size", type=int, default=16, choices=(16, 32))
     ap.add_argument("--workers", type=int, default=0, help="decode wavefronts (0 = automatic)")
     ap.add_argument("--kernel-launches", type=int, default=KERNEL_LAUNCHES,
@@ -771,7 +773,7 @@ def main():
     import workloads as W
 
     dev = "cuda:0"
-    if args.workload in ("prefix800", "prefix4096", "prefill", "verify"):
+    if args.workload in ("prefix800", "prefix4096", "prefix8192", "prefill", "verify"):
         row_state_line(args, pkv, W, torch, dev)
         return
     t_gen = time.perf_counter()

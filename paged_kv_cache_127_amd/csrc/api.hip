@@ -763,20 +763,42 @@ int swap_dma_impl(const char* fn, bool to_host, void* k_pool, void* v_pool, int 
   return ok();
 }
 
+// rows per KV head from which a workgroup's four wavefronts take four row tiles over the same
+// tokens (extend_rows_shared)
+constexpr int64_t kWideExtendRows = 128;
+
 // Workspace of the shared-prefix call: the suffix decode's workspace, then the suffix lengths,
 // the suffix rows' log-sum-exp, an fp32 suffix output (used when the output is 16-bit) and the
 // prefix states of every chunk group.
 struct SpLayout {
   size_t decode, suffix_lens, lse, o, m, l, acc, total;
   int chunk_groups, steps_per_chunk;
+  bool wide;
 };
+
+// Prefix states: at least 128 rows per KV head over more than kWidePrefixTokens take the kernel
+// whose workgroups share each step's keys and values among four 32-row tiles, with chunk groups
+// enough for kWidePrefixWgPerCu workgroups per CU; shorter prefixes the row-state kernel, whose
+// four wavefronts split one 32-row tile's tokens. Up to 4096 tokens the row-state kernel leaves
+// one state per row for the merge to read (four wavefronts of at most 32 steps); the wide
+// kernel's chunk groups (eight at 1024 rows per KV head) cost the merge about 1 us each, which
+// its faster steps repay only beyond that.
+constexpr int kWidePrefixTokens = 4096;
+constexpr int kWidePrefixWgPerCu = 2;
 
 SpLayout sp_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int n,
                    int prefix_len) {
   const int G = num_q_heads / num_kv_heads;
   SpLayout L;
-  pkv::row_state_plan((int64_t)num_kv_heads * pkv::row_groups((int64_t)num_seqs * G), prefix_len,
-                      cu_count(), &L.chunk_groups, &L.steps_per_chunk);
+  L.wide = (int64_t)num_seqs * G >= kWideExtendRows && prefix_len > kWidePrefixTokens;
+  if (L.wide) {
+    pkv::wide_row_plan((int64_t)num_kv_heads * pkv::wide_row_groups((int64_t)num_seqs * G),
+                       prefix_len, kWidePrefixWgPerCu * cu_count(), &L.chunk_groups);
+    L.steps_per_chunk = 0;
+  } else {
+    pkv::row_state_plan((int64_t)num_kv_heads * pkv::row_groups((int64_t)num_seqs * G),
+                        prefix_len, cu_count(), &L.chunk_groups, &L.steps_per_chunk);
+  }
   const size_t SH = (size_t)num_seqs * num_q_heads;
   L.decode = ws_layout(num_seqs, G, head_dim, n).total;
   L.suffix_lens = align256(L.decode);
@@ -909,7 +931,8 @@ int paged_attn_decode_shared_prefix(void* out, int out_dtype, const void* q, con
   pp.steps_per_chunk = sl.steps_per_chunk;
   pp.scale_log2 = sc * 1.4426950408889634f;
   hipError_t e = timed("prefix_states", st, [&] {
-    return pkv::launch_row_states(pp, kv_dtype, head_dim, block_size, st);
+    return sl.wide ? pkv::launch_wide_prefix_states(pp, kv_dtype, head_dim, block_size, st)
+                   : pkv::launch_row_states(pp, kv_dtype, head_dim, block_size, st);
   });
   if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "%s: prefix kernel: %s", fn,
                                    hipGetErrorString(e));
@@ -939,8 +962,6 @@ struct ExtLayout {
   int chunk_groups, steps_per_chunk, max_row_groups;
   bool wide;
 };
-
-constexpr int64_t kWideExtendRows = 128;
 
 ExtLayout ext_layout(int num_seqs, int num_query_tokens, int num_q_heads, int num_kv_heads,
                      int head_dim, int max_query_len, int max_context_len) {

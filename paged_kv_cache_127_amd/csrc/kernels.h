@@ -133,6 +133,10 @@ int64_t wide_row_groups(int64_t rows);
 void wide_row_plan(int64_t base_workgroups, int max_tokens, int num_cus, int* chunk_groups);
 hipError_t launch_extend_rows_shared(const RowStateParams& p, int kv_dtype, int head_dim,
                                      int block_size, hipStream_t st);
+// Prefix states (prefix mode of RowStateParams) on the same kernel: grid = KV heads x 128-row
+// groups of the S * G rows x chunk groups.
+hipError_t launch_wide_prefix_states(const RowStateParams& p, int kv_dtype, int head_dim,
+                                     int block_size, hipStream_t st);
 
 struct AppendParams {
   void* k_pool;

@@ -21,7 +21,8 @@
 // extend_finish folds each row's states and normalises. Runs long enough to give 128 or more rows
 // per KV head (prefill chunks) take extend_rows_shared below, whose workgroups share each step's
 // keys and values among four row tiles; row_states serves the short runs (speculative
-// verification), whose four wavefronts split one row tile's tokens.
+// verification), whose four wavefronts split one row tile's tokens. Prefixes past 4096 tokens
+// take extend_rows_shared's prefix mode.
 //
 // row_states. A workgroup of four wavefronts takes (row group of RB * 16 rows of one KV head,
 // chunk group); wavefront w runs chunk 4 * cg + w, a run of 32-token steps. Per step the MFMA
@@ -549,7 +550,9 @@ void row_states(RowStateParams p) {
 // from LDS as the score MFMA's A operand (rows tau(a, i) as in row_states), values as in
 // row_states. The workgroup's token range ends at its last row's limit and is split evenly over
 // the chunk groups; with one chunk group each wavefront normalises its rows into the output,
-// otherwise it stores their states for extend_finish.
+// otherwise it stores their states for extend_finish. The same kernel computes the prefix
+// states of long shared prefixes (prefix mode, as in row_states: the S * G rows of a KV head
+// against all P prefix tokens, one state per row and chunk group for the decode's merge).
 template <typename T, int D, int B>
 __global__ __launch_bounds__(64 * kRowWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void extend_rows_shared(RowStateParams p) {
@@ -574,40 +577,60 @@ void extend_rows_shared(RowStateParams p) {
   const int S = p.num_seqs, Hq = p.num_q_heads, Hkv = p.num_kv_heads;
   const int G = Hq / Hkv;
   const int cgroups = p.chunk_groups;
-  const int mg = p.max_row_groups;
-  // Dispatch order (grid = S * Hkv * mg * cgroups): chunk groups fastest, then KV heads (with 8
-  // heads each XCD keeps one head's keys and values), then the row groups from the last one
-  // (the longest token range) down, then the sequences longest first -- their rank by context
-  // length, ties by index, when at most one per thread -- so that the longest workgroups start
-  // first and the short ones fill in at the end.
-  const int cg = blockIdx.x % cgroups;
-  const int g = (blockIdx.x / cgroups) % Hkv;
-  const int rg = mg - 1 - (int)((blockIdx.x / (cgroups * Hkv)) % mg);
-  const int rank = blockIdx.x / (cgroups * Hkv * mg);
-  int s = rank;
-  if (S > 1 && S <= NT) {
-    __shared__ int ranked;
-    int* sl = reinterpret_cast<int*>(&lds[0][0][0]);   // stage memory, not in use yet
-    for (int j = threadIdx.x; j < S; j += NT) sl[j] = clamp_len(p.lens[j], p.max_blocks * B);
-    __syncthreads();
-    if ((int)threadIdx.x < S) {
-      const int j = threadIdx.x, lj = sl[j];
-      int r = 0;
-      for (int i = 0; i < S; ++i) r += (sl[i] > lj || (sl[i] == lj && i < j)) ? 1 : 0;
-      if (r == rank) ranked = j;
+  const bool extend = p.query_start != nullptr;         // uniform
+  int cg, g, rg, qs = 0, n = 0, L = 0, R, tok_end;
+  ctable_t blocks;
+  if (!extend) {
+    // prefix mode: rows r = s * G + i of all S sequences, the shared blocks, P tokens for all
+    // rows (grid = Hkv * wide row groups * cgroups). Dispatch order: KV heads fastest (with 8
+    // heads each XCD streams one head's prefix through its L2), then chunk groups, then row
+    // groups. The suffix lengths max(L_s - P, 0) are written one per thread over the grid.
+    const int P = p.prefix_len;
+    for (int j = blockIdx.x + (int)(gridDim.x * threadIdx.x); j < S;
+         j += (int)(gridDim.x * blockDim.x))
+      p.suffix_lens[j] = max(p.lens[j] - P, 0);
+    g = blockIdx.x % Hkv;
+    cg = (blockIdx.x / Hkv) % cgroups;
+    rg = blockIdx.x / (Hkv * cgroups);
+    R = S * G;
+    tok_end = P;
+    blocks = (ctable_t)p.prefix_blocks;
+  } else {
+    // extend mode (grid = S * Hkv * mg * cgroups). Dispatch order: chunk groups fastest, then
+    // KV heads (with 8 heads each XCD keeps one head's keys and values), then the row groups
+    // from the last one (the longest token range) down, then the sequences longest first --
+    // their rank by context length, ties by index, when at most one per thread -- so that the
+    // longest workgroups start first and the short ones fill in at the end.
+    const int mg = p.max_row_groups;
+    cg = blockIdx.x % cgroups;
+    g = (blockIdx.x / cgroups) % Hkv;
+    rg = mg - 1 - (int)((blockIdx.x / (cgroups * Hkv)) % mg);
+    const int rank = blockIdx.x / (cgroups * Hkv * mg);
+    int s = rank;
+    if (S > 1 && S <= NT) {
+      __shared__ int ranked;
+      int* sl = reinterpret_cast<int*>(&lds[0][0][0]);   // stage memory, not in use yet
+      for (int j = threadIdx.x; j < S; j += NT) sl[j] = clamp_len(p.lens[j], p.max_blocks * B);
+      __syncthreads();
+      if ((int)threadIdx.x < S) {
+        const int j = threadIdx.x, lj = sl[j];
+        int r = 0;
+        for (int i = 0; i < S; ++i) r += (sl[i] > lj || (sl[i] == lj && i < j)) ? 1 : 0;
+        if (r == rank) ranked = j;
+      }
+      __syncthreads();
+      s = uni(ranked);
     }
-    __syncthreads();
-    s = uni(ranked);
+    // out-of-contract starts are clamped into [0, T]: rows are never read or written outside
+    qs = uni(min(max(p.query_start[s], 0), p.num_query_tokens));
+    n = uni(min(max(p.query_start[s + 1] - qs, 0), p.num_query_tokens - qs));
+    L = uni(clamp_len(p.lens[s], p.max_blocks * B));
+    R = n * G;
+    if (rg * kWideRows >= R) return;                    // the whole workgroup: no barrier yet
+    const int t_last = (min((rg + 1) * kWideRows, R) - 1) / G;
+    tok_end = min(max(L - n + t_last + 1, 0), L);
+    blocks = (ctable_t)p.tables + (size_t)s * p.max_blocks;
   }
-  // out-of-contract starts are clamped into [0, T]: rows are never read or written outside
-  const int qs = uni(min(max(p.query_start[s], 0), p.num_query_tokens));
-  const int n = uni(min(max(p.query_start[s + 1] - qs, 0), p.num_query_tokens - qs));
-  const int L = uni(clamp_len(p.lens[s], p.max_blocks * B));
-  const int R = n * G;
-  if (rg * kWideRows >= R) return;                      // the whole workgroup: no barrier yet
-  const int t_last = (min((rg + 1) * kWideRows, R) - 1) / G;
-  const int tok_end = min(max(L - n + t_last + 1, 0), L);
-  const ctable_t blocks = (ctable_t)p.tables + (size_t)s * p.max_blocks;
   const int nsteps = ceil_div(tok_end, 32);
   const int spc = ceil_div(nsteps, cgroups);
   const int k0 = min(cg * spc, nsteps);
@@ -623,10 +646,10 @@ void extend_rows_shared(RowStateParams p) {
     const int r0 = rg * kWideRows + 32 * wave + 16 * rb + r16;
     live[rb] = r0 < R;
     const int r = min(r0, R - 1);
-    const int a = r / G;                                 // new token
+    const int a = r / G;                                 // sequence (prefix) or new token
     const int i = r - a * G;
     qrow[rb] = ((size_t)(qs + a)) * Hq + (size_t)g * G + i;
-    lim[rb] = min(max(L - n + a + 1, 0), L);
+    lim[rb] = extend ? min(max(L - n + a + 1, 0), L) : tok_end;
   }
 
   // a chunk group with no step (or nothing to attend) writes the empty state (-inf, 0, 0) of
@@ -1016,11 +1039,8 @@ void wide_row_plan(int64_t base_workgroups, int max_tokens, int num_cus, int* ch
       1, std::min<int64_t>(fill, std::min<int64_t>(nsteps, kMaxChunkGroups)));
 }
 
-hipError_t launch_extend_rows_shared(const RowStateParams& p, int kv_dtype, int head_dim,
-                                     int block_size, hipStream_t st) {
-  if (p.num_seqs <= 0) return hipSuccess;
-  const int64_t grid =
-      (int64_t)p.num_seqs * p.num_kv_heads * p.max_row_groups * p.chunk_groups;
+static hipError_t launch_wide(const RowStateParams& p, int64_t grid, int kv_dtype,
+                              int head_dim, int block_size, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   if (kv_dtype == 2) {
@@ -1033,6 +1053,22 @@ hipError_t launch_extend_rows_shared(const RowStateParams& p, int kv_dtype, int 
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_extend_rows_shared(const RowStateParams& p, int kv_dtype, int head_dim,
+                                     int block_size, hipStream_t st) {
+  if (p.num_seqs <= 0) return hipSuccess;
+  return launch_wide(p, (int64_t)p.num_seqs * p.num_kv_heads * p.max_row_groups * p.chunk_groups,
+                     kv_dtype, head_dim, block_size, st);
+}
+
+hipError_t launch_wide_prefix_states(const RowStateParams& p, int kv_dtype, int head_dim,
+                                     int block_size, hipStream_t st) {
+  if (p.num_seqs <= 0 || p.query_start) return hipErrorInvalidValue;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  return launch_wide(p, (int64_t)p.num_kv_heads * wide_row_groups((int64_t)p.num_seqs * G) *
+                            p.chunk_groups,
+                     kv_dtype, head_dim, block_size, st);
 }
 
 hipError_t launch_extend_finish(const ExtendFinishParams& p, int kv_dtype, int head_dim,

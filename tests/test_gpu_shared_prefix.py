@@ -60,6 +60,12 @@ CASES = [
     ([12] * 20, 800, 64, 8, 128, 16, "bf16"),           # 160 rows: three row groups
     ([500, 1, 250, 31], 16, 24, 4, 64, 16, "f16"),      # one prefix block, G = 6
     (list(range(1, 70)), 112, 16, 2, 128, 16, "bf16"),  # 69 sequences, 552 rows per head
+    # prefixes past 4096 tokens with at least 128 rows per KV head: the kernel whose four
+    # wavefronts share each step's keys and values among four 32-row tiles
+    ([3, 0, 40, 1, 17, 9, 2, 100, 5, 6, 7, 8, 11, 13, 64, 31, 1], 4128, 16, 2, 128, 16,
+     "bf16"),                                            # 136 rows: a second, ragged row group
+    ([1, 2, 3, 0, 50, 7, 9, 33, 12], 4160, 64, 4, 64, 32, "f16"),   # G = 16, 130 blocks of 32
+    ([5] * 64, 4112, 4, 2, 128, 16, "bf16"),            # G = 2, 128 rows, a half last step
 ]
 
 
@@ -89,8 +95,9 @@ def test_16bit_output_is_rounded_fp32_output():
 def test_shared_prefix_workload_full_size(prefix_len):
     """128 sequences over an 800-, 4096- or 8192-token prefix with U{1..512}-token suffixes
     (64/8 heads, head_dim 128, bf16, block size 16), in the launch configuration the benchmark
-    times (800 and 4096: one chunk group of up to 32 steps per wavefront; 8192: two groups);
-    every row of all 128 sequences against the oracle."""
+    times (800 and 4096: the row-state kernel, one chunk group of up to 32 steps per
+    wavefront; 8192: the kernel that shares key/value tiles among row tiles, eight chunk
+    groups); every row of all 128 sequences against the oracle."""
     b = W.config4a(prefix_len=prefix_len)
     db = DeviceBatch(b)
     got = _run(db, prefix_len)
