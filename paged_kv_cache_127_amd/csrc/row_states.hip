@@ -108,7 +108,7 @@ __device__ __forceinline__ void store_row4(const RowStateParams& p, size_t off, 
   }
 }
 
-template <typename T, int D, int B, int RBK>
+template <typename T, int D, int B, int RBK, bool NT>
 __global__ __launch_bounds__(64 * kRowWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void row_states(RowStateParams p) {
   static_assert(B == 16 || B == 32, "block size");
@@ -297,6 +297,10 @@ void row_states(RowStateParams p) {
     b1 = B == 16 ? blocks[min(j0 + 1, nb - 1)] : b0;
   };
   u32x4 kr[2][NC], vr[NF], va[NF];
+  // NT: streaming loads, for key/value rows this launch reads once (extend mode with one row
+  // group per sequence: the chunks split the tokens); shared prefix blocks, which every row
+  // group reads, stay on plain loads so that they remain in the caches
+  auto ld = [](const char* a) { return NT ? load16_stream(a) : load16(a); };
   auto load_k = [&](int b0, int b1) {
     b0 = valid_block(b0, p.num_blocks) ? b0 : 0;
     b1 = valid_block(b1, p.num_blocks) ? b1 : 0;
@@ -306,8 +310,8 @@ void row_states(RowStateParams p) {
     const char* kb = ((B == 16 && tokA0 + 4 >= 16) ? t1 : t0) + kofs1;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      kr[0][c] = load16(ka + 32 * c * ES);
-      kr[1][c] = load16(kb + 32 * c * ES);
+      kr[0][c] = ld(ka + 32 * c * ES);
+      kr[1][c] = ld(kb + 32 * c * ES);
     }
   };
   auto load_v = [&](int b0, int b1) {
@@ -317,8 +321,8 @@ void row_states(RowStateParams p) {
     for (int f = 0; f < NF; ++f) {
       const int t = VTPI * f + vrow;
       const int blk = (B == 16 && t >= 16) ? b1 : b0;
-      vr[f] = load16(vbase + ((size_t)blk * Hkv + g) * tile_stride + (size_t)(t & (B - 1)) * ROWB +
-                     16 * vch);
+      vr[f] = ld(vbase + ((size_t)blk * Hkv + g) * tile_stride + (size_t)(t & (B - 1)) * ROWB +
+                 16 * vch);
     }
   };
   auto stage_v = [&]() {
@@ -970,8 +974,12 @@ int64_t row_groups(int64_t rows) { return (rows + 16 * kRowsRB - 1) / (16 * kRow
 
 template <typename T, int D, int B>
 static void launch_rows_tdb(const RowStateParams& p, int64_t grid, hipStream_t st) {
-  launch_kernel((row_states<T, D, B, kRowsRB>), dim3((unsigned)grid), dim3(64 * kRowWaves),
-                     0, st, p);
+  if (p.query_start && p.max_row_groups == 1)
+    launch_kernel((row_states<T, D, B, kRowsRB, true>), dim3((unsigned)grid),
+                  dim3(64 * kRowWaves), 0, st, p);
+  else
+    launch_kernel((row_states<T, D, B, kRowsRB, false>), dim3((unsigned)grid),
+                  dim3(64 * kRowWaves), 0, st, p);
 }
 
 template <typename T, int D>
