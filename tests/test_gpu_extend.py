@@ -149,6 +149,36 @@ def test_one_chunk_group_writes_the_output_directly():
     assert torch.equal(bits(b16), bits(f32.to(torch.bfloat16)))
 
 
+@pytest.mark.parametrize("S,hq,hkv,d,B,dt,nmax", [
+    (41, 64, 8, 128, 16, "bf16", 4),    # G = 8: up to 32 rows per sequence
+    (70, 16, 8, 64, 32, "f16", 16),     # G = 2, head_dim 64, block size 32
+])
+def test_short_runs_one_row_group(S, hq, hkv, d, B, dt, nmax):
+    """Short runs with one row group per sequence and sequences x KV heads filling the CUs
+    (one chunk group, streaming key/value loads): a sequence's steps go to as many of its
+    workgroup's four wavefronts as get at least 8 steps each. Lengths straddle 256, 512 and
+    513 tokens, tie, and include a one-token context; some sequences have no new token. Every
+    row against the oracle, the workspace NaN-filled, and the 16-bit output = RNE of the fp32
+    output."""
+    rng = np.random.default_rng(S)
+    lens = [int(x) for x in rng.integers(1, 1500, size=S)]
+    lens[:8] = [512, 513, 512, 1, 1000, 1000, 256, 257]
+    new = [min(int(x), L) for x, L in zip(rng.integers(0, nmax + 1, size=S), lens)]
+    new[3] = 1
+    new[7] = 0
+    b = W.small_batch(lens, hq, hkv, d, B, DT[dt], seed=S + 1, poison=True)
+    q, start = W.extend_queries(b, new, seed=S + 2)
+    db = DeviceBatch(b)
+    f32 = _run(db, q, start)
+    ref = oracle.extend_attention(q, start, b.k_pool, b.v_pool, b.tables, b.lengths, B)
+    err = float(np.abs(f32.double().numpy() - ref).max())
+    print(f"short runs S={S} G={hq // hkv}: max-abs {err:.3g} over {f32.shape[0]} rows")
+    assert np.isfinite(f32.numpy()).all()
+    assert err <= TOL[DT[dt]], err
+    h16 = _run(db, q, start, out_dtype=DT[dt])
+    assert torch.equal(bits(h16), bits(f32.to(DT[dt])))
+
+
 def test_speculative_verification_at_gqa_shape():
     """The GQA decode workload (256 sequences, 64/8 heads, bf16, B 16, log-normal lengths), its
     last 4 stored tokens of each sequence taken as the new ones; every row of every sequence
