@@ -93,8 +93,10 @@ def cpu_baseline(batch, steps: int):
 def _kernel_times(pkv, torch, launch, names, launches: int):
     """({kernel name: mean us}, step p50 us) of `launch` (one call sequence): the step from
     torch events around every call with the library's own timing off, then the kernels from
-    hipEvents around every launch of each library kernel in a second run."""
-    for _ in range(5):
+    hipEvents around every launch of each library kernel in a second run. 60 untimed calls
+    first: launches over freshly allocated pools run a few percent slower for their first
+    few dozen calls."""
+    for _ in range(60):
         launch()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -142,7 +144,7 @@ def kernel_loop(pkv, torch, launch, names, launches: int):
     return out
 
 
-def other_configs(pkv, W, torch, dev: str, workers: int, launches: int = 30):
+def other_configs(pkv, W, torch, dev: str, workers: int, launches: int = 50):
     """Figures on the other batch configs: decode-kernel roofline for the HBM-bound ones (GQA
     at block size 32, multi-head fp16, long contexts with their 8-token append per step),
     logical GB/s for the shared-prefix batch (cache-assisted, no HBM claim), and latencies for
