@@ -225,8 +225,9 @@ int paged_attn_decode_shared_prefix(void* out, int out_dtype, const void* q, con
  *   workspace      device, 256-byte aligned, pkv_extend_workspace_size(...) bytes for the same
  *                  sizes
  * Other arguments as for paged_attn_decode. 16-bit caches only (PKV_ERR_UNSUPPORTED otherwise).
- * Each run of 32 query rows (32 / G new tokens of one KV head) reads its keys and values once,
- * so the call suits short runs (speculative verification, small prefill chunks). Starts outside
+ * Each tile of 32 query rows (32 / G new tokens of one KV head) reads its keys and values once
+ * when max_query_len * G < 128 (speculative verification); longer runs (prefill chunks) share
+ * each step's keys and values among a workgroup's four 32-row tiles. Starts outside
  * [0, num_query_tokens] are clamped (never read outside q or out); PAGEDKV_VALIDATE checks the
  * starts, n_s <= max_query_len, n_s <= L_s and the table entries.
  * --------------------------------------------------------------------------------------- */
