@@ -318,3 +318,30 @@ def test_shared_prefix_and_extend_replay_in_a_hip_graph():
     assert max_err(ref_sp.cpu(), oracle.paged_decode(b.q, kw, vw, b.tables, b.lengths, 16)) <= 2e-3
     assert max_err(ref_ex2.cpu(), oracle.extend_attention(q2, start2, b.k_pool, b.v_pool, b.tables,
                                                           b.lengths, 16)) <= 2e-3
+
+
+def test_random_shapes_sweep():
+    """Thirty seeded random problems across the supported space -- cache dtype, G from 1 to 16,
+    KV heads, head dim, block size, 1 to 12 sequences of 1 to 700 tokens with 0 to 40 new ones
+    (both kernels: at least 128 rows per KV head takes the tile-sharing one) -- every row
+    against the oracle, with the workspace NaN-filled."""
+    rng = np.random.default_rng(78)
+    for i in range(30):
+        dt = ["bf16", "f16"][i % 2]
+        G = int(rng.integers(1, 17))
+        hkv = int(rng.choice([1, 2, 4]))
+        d = int(rng.choice([64, 128]))
+        B = int(rng.choice([16, 32]))
+        S = int(rng.integers(1, 13))
+        lens = [int(x) for x in rng.integers(1, 701, size=S)]
+        new = [int(rng.integers(0, min(L, 40) + 1)) for L in lens]
+        j = int(rng.integers(0, S))
+        new[j] = max(1, new[j])                                    # at least one new token
+        case = (dt, G, hkv, d, B, lens, new)
+        print("case", case, flush=True)
+        b = W.small_batch(lens, G * hkv, hkv, d, B, DT[dt], seed=6000 + i, poison=True)
+        q, start = W.extend_queries(b, new, seed=6100 + i)
+        got = _run(DeviceBatch(b), q, start)
+        ref = oracle.extend_attention(q, start, b.k_pool, b.v_pool, b.tables, b.lengths, B)
+        assert np.isfinite(got.numpy()).all(), case
+        assert float(np.abs(got.double().numpy() - ref).max()) <= TOL[DT[dt]], case

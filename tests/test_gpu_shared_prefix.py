@@ -149,3 +149,38 @@ def test_rejections_and_validation():
     finally:
         pkv.set_validate(False)
     assert max_err(out.cpu(), _ref(b)) <= 2e-3
+
+
+def test_random_shapes_sweep():
+    """Twenty-four seeded random problems across the supported space -- cache dtype, G from 2
+    to 16, KV heads, head dim, block size, worker count, output dtype, prefix of 1 to 20 blocks,
+    ragged suffixes with empty ones -- and four with prefixes past 4096 tokens and at least 128
+    rows per KV head (the tile-sharing prefix kernel), every row against the plain oracle; a
+    16-bit output is the RNE of the fp32 one."""
+    rng = np.random.default_rng(77)
+    for i in range(28):
+        dt = ["bf16", "f16"][i % 2]
+        G = int(rng.integers(2, 17))
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        d = int(rng.choice([64, 128]))
+        B = int(rng.choice([16, 32]))
+        workers = int(rng.choice([0, 7, 64, 2000]))
+        if i < 24:
+            S = int(rng.integers(1, 41))
+            P = B * int(rng.integers(1, 21))
+        else:                                     # wide prefix mode: S * G >= 128, P > 4096
+            G = int(rng.choice([2, 4, 8, 16]))
+            hkv = int(rng.choice([1, 2]))
+            S = -(-128 // G) + int(rng.integers(0, 9))
+            P = 4096 + B * int(rng.integers(1, 5))
+        suf = [int(x) for x in rng.integers(0, 300, size=S)]
+        case = (dt, G, hkv, d, B, S, P, workers)
+        print("case", case, flush=True)
+        b = W.shared_prefix_batch(suf, P, G * hkv, hkv, d, B, DT[dt], seed=5000 + i, poison=True)
+        db = DeviceBatch(b)
+        got = _run(db, P, workers=workers)
+        assert np.isfinite(got.numpy()).all(), case
+        assert max_err(got, _ref(b)) <= TOL[DT[dt]], case
+        if i % 4 == 0:
+            h16 = _run(db, P, out_dtype=DT[dt], workers=workers)
+            assert torch.equal(bits(h16), bits(got.to(DT[dt]))), case
