@@ -32,11 +32,12 @@
 // through the wavefront's swizzled LDS tile and come back transposed as the A operand of
 // O^T[d][row] += V^T . P^T, with P split into a 16-bit high part and a remainder. Each
 // key/value fragment a wavefront loads serves its RB row blocks; two wavefronts per SIMD, so
-// that one computes while the other waits for memory. Block ids are scalar loads two steps
-// ahead, keys and values one step ahead. At the end the four wavefronts merge their states
-// through LDS (over the value tiles, no longer needed), each folding and storing a quarter of
-// the columns: one state (m, l, acc) per row and chunk group, m in the log2 domain, acc not
-// normalised (or, extend mode with one chunk group, the normalised rows). In prefix mode the first workgroup also writes the suffix lengths
+// that one computes while the other waits for memory. Block ids are scalar loads three steps
+// ahead, keys one step ahead, values two (one step in registers, one in LDS). At the end the
+// four wavefronts merge their states through LDS (over the value tiles, no longer needed), each
+// folding and storing a quarter of the columns: one state (m, l, acc) per row and chunk group,
+// m in the log2 domain, acc not normalised (or, extend mode with one chunk group, the
+// normalised rows). In prefix mode the first workgroup also writes the suffix lengths
 // max(L_s - P, 0).
 #include <algorithm>
 
