@@ -192,7 +192,7 @@ int paged_attn_decode_append(void* out, int out_dtype, const void* q, void* k_po
  *   context_lens   every context_lens[s] >= prefix_len (the suffix may be empty)
  *   workspace      device, 256-byte aligned, at least pkv_shared_prefix_workspace_size(...)
  *                  bytes for the same sizes, num_workers and prefix_len
- * 16-bit caches with 2 to 16 query heads per KV head (PKV_ERR_UNSUPPORTED otherwise); one call
+ * 16-bit caches with 1 to 16 query heads per KV head (PKV_ERR_UNSUPPORTED otherwise); one call
  * per group of sequences that share a prefix. Under PAGEDKV_VALIDATE the shared table entries,
  * the lengths and the prefix ids are checked first.
  * --------------------------------------------------------------------------------------- */

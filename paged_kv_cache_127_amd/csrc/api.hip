@@ -286,7 +286,9 @@ int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const v
   const int G = num_q_heads / num_kv_heads;
   const bool wide = kv_dtype != PKV_F32;
   bool use_mfma;
-  if (wide && G >= 2 && G <= 16) {
+  // the suffix decode of a shared-prefix call takes the matrix-core kernel at G = 1 too: only
+  // it writes the rows' log-sum-exp that the prefix fold needs
+  if (wide && ((G >= 2 && G <= 16) || (G == 1 && pf))) {
     use_mfma = true;
   } else if (G == 1 || (!wide && (G == 2 || G == 4 || G == 8))) {
     use_mfma = false;
@@ -854,8 +856,8 @@ int paged_attn_decode_shared_prefix(void* out, int out_dtype, const void* q, con
     return fail(PKV_ERR_INVALID_ARG, "%s: %d query heads not a multiple of %d KV heads", fn,
                 num_q_heads, num_kv_heads);
   const int G = num_q_heads / num_kv_heads;
-  if (G < 2 || G > 16)
-    return fail(PKV_ERR_UNSUPPORTED, "%s: %d query heads per KV head (2 to 16)", fn, G);
+  if (G < 1 || G > 16)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: %d query heads per KV head (1 to 16)", fn, G);
   if (prefix_len <= 0 || prefix_len % block_size != 0 || prefix_len > max_context_len)
     return fail(PKV_ERR_INVALID_ARG,
                 "%s: prefix_len %d must be a positive multiple of %d, at most %d", fn,

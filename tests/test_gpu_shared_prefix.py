@@ -66,6 +66,10 @@ CASES = [
      "bf16"),                                            # 136 rows: a second, ragged row group
     ([1, 2, 3, 0, 50, 7, 9, 33, 12], 4160, 64, 4, 64, 32, "f16"),   # G = 16, 130 blocks of 32
     ([5] * 64, 4112, 4, 2, 128, 16, "bf16"),            # G = 2, 128 rows, a half last step
+    # G = 1 (multi-head): the suffix decode on the matrix-core kernel with one real row
+    ([1, 15, 16, 17, 33, 100, 511, 0], 64, 4, 4, 128, 16, "bf16"),
+    ([3, 0, 250, 40, 9], 96, 8, 8, 64, 32, "f16"),
+    ([7] * 130, 4128, 2, 2, 128, 16, "bf16"),           # 130 rows: the tile-sharing prefix kernel
 ]
 
 
@@ -152,7 +156,7 @@ def test_rejections_and_validation():
 
 
 def test_random_shapes_sweep():
-    """Twenty-four seeded random problems across the supported space -- cache dtype, G from 2
+    """Twenty-four seeded random problems across the supported space -- cache dtype, G from 1
     to 16, KV heads, head dim, block size, worker count, output dtype, prefix of 1 to 20 blocks,
     ragged suffixes with empty ones -- and four with prefixes past 4096 tokens and at least 128
     rows per KV head (the tile-sharing prefix kernel), every row against the plain oracle; a
@@ -160,7 +164,7 @@ def test_random_shapes_sweep():
     rng = np.random.default_rng(77)
     for i in range(28):
         dt = ["bf16", "f16"][i % 2]
-        G = int(rng.integers(2, 17))
+        G = int(rng.integers(1, 17))
         hkv = int(rng.choice([1, 2, 4, 8]))
         d = int(rng.choice([64, 128]))
         B = int(rng.choice([16, 32]))
