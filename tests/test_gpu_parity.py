@@ -355,6 +355,22 @@ def test_config5_steps():
         assert err <= 2e-3
 
 
+def test_one_very_long_sequence():
+    """A 131,072-token sequence (8,192 blocks) beside a short and an empty one, 64/8 heads,
+    bf16: the long sequence's 8 segments are cut over every worker (automatic count, and 5,000
+    workers of about 7 steps each), so the merge folds hundreds of partials per segment; every
+    row against the oracle."""
+    b = W.small_batch([131072, 7, 0], 64, 8, 128, 16, torch.bfloat16, seed=131, poison=True)
+    db = DeviceBatch(b)
+    ref = oracle_decode(b)
+    for workers in (0, 5000):
+        got = db.decode(workers=workers)
+        err = max_err(got, ref)
+        print(f"131072-token sequence, workers={workers}: max-abs {err:.3g}")
+        assert np.isfinite(got.numpy()).all()
+        assert err <= 2e-3
+
+
 # ---- append / copy-on-write alone ------------------------------------------------------
 @pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("B", [16, 32])
