@@ -179,6 +179,23 @@ def test_short_runs_one_row_group(S, hq, hkv, d, B, dt, nmax):
     assert torch.equal(bits(h16), bits(f32.to(DT[dt])))
 
 
+def test_long_context_chunks():
+    """A 32,768-token context with its last 16 tokens new (128 rows per KV head: the tile-sharing
+    kernel with 16 chunk groups and the finish kernel) beside a 300-token one with 4 new tokens,
+    and a verification-sized run (4 new tokens) at the end of another 32,768-token context on the
+    row-state kernel; every row against the oracle."""
+    for lens, new in (([32768, 300], [16, 4]), ([32768, 40], [4, 4])):
+        b = W.small_batch(lens, 64, 8, 128, 16, torch.bfloat16, seed=32768 + new[0],
+                          poison=True)
+        q, start = W.extend_queries(b, new, seed=32769 + new[0])
+        got = _run(DeviceBatch(b), q, start)
+        ref = oracle.extend_attention(q, start, b.k_pool, b.v_pool, b.tables, b.lengths, 16)
+        err = float(np.abs(got.double().numpy() - ref).max())
+        print(f"{lens} {new}: max-abs {err:.3g}")
+        assert np.isfinite(got.numpy()).all()
+        assert err <= 2e-3, err
+
+
 def test_speculative_verification_at_gqa_shape():
     """The GQA decode workload (256 sequences, 64/8 heads, bf16, B 16, log-normal lengths), its
     last 4 stored tokens of each sequence taken as the new ones; every row of every sequence
