@@ -858,6 +858,11 @@ int paged_attn_decode_shared_prefix(void* out, int out_dtype, const void* q, con
   const int G = num_q_heads / num_kv_heads;
   if (G < 1 || G > 16)
     return fail(PKV_ERR_UNSUPPORTED, "%s: %d query heads per KV head (1 to 16)", fn, G);
+  // the suffix decode and the merge take every sharer in one launch (checked before anything
+  // is enqueued)
+  if (num_seqs > pkv::kMaxSeqsPerCall)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: %d sequences (at most %d per call)", fn, num_seqs,
+                pkv::kMaxSeqsPerCall);
   if (prefix_len <= 0 || prefix_len % block_size != 0 || prefix_len > max_context_len)
     return fail(PKV_ERR_INVALID_ARG,
                 "%s: prefix_len %d must be a positive multiple of %d, at most %d", fn,

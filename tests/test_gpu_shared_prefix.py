@@ -111,6 +111,23 @@ def test_shared_prefix_workload_full_size(prefix_len):
     assert err <= 2e-3, err
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 1), (16, 4)])
+def test_most_sharers_per_call(hq, hkv):
+    """4,096 sequences (the most one call takes) over a 4-block prefix with 0..40-token suffixes,
+    G = 8 and G = 4: every row against the plain oracle (4,097 is rejected on the host before
+    anything is enqueued: test_library_host)."""
+    rng = np.random.default_rng(4096 + hq)
+    suf = [int(x) for x in rng.integers(0, 41, size=4096)]
+    b = W.shared_prefix_batch(suf, 64, hq, hkv, 64, 16, torch.bfloat16, seed=4096 + hq,
+                              poison=True)
+    db = DeviceBatch(b)
+    got = _run(db, 64)
+    assert np.isfinite(got.numpy()).all()
+    err = max_err(got, _ref(b))
+    print(f"4096 sharers, G = {hq // hkv}: max-abs {err:.3g}")
+    assert err <= 2e-3, err
+
+
 def test_result_does_not_depend_on_workspace_contents():
     b = W.shared_prefix_batch([9, 120, 3], 96, 16, 2, 128, 16, torch.bfloat16, seed=8)
     db = DeviceBatch(b)
