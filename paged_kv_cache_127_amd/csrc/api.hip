@@ -863,6 +863,8 @@ int paged_attn_decode_shared_prefix(void* out, int out_dtype, const void* q, con
   if (num_seqs > pkv::kMaxSeqsPerCall)
     return fail(PKV_ERR_UNSUPPORTED, "%s: %d sequences (at most %d per call)", fn, num_seqs,
                 pkv::kMaxSeqsPerCall);
+  if (num_workers > (1 << 20))
+    return fail(PKV_ERR_INVALID_ARG, "%s: num_workers %d", fn, num_workers);
   if (prefix_len <= 0 || prefix_len % block_size != 0 || prefix_len > max_context_len)
     return fail(PKV_ERR_INVALID_ARG,
                 "%s: prefix_len %d must be a positive multiple of %d, at most %d", fn,
