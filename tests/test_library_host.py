@@ -196,8 +196,8 @@ def test_shared_prefix_argument_checks():
     assert call(kv_dtype=0) == -2                 # fp32 cache
     assert call(Hq=34, Hkv=2) == -2               # G = 17
     assert call(S=4097) == -2                     # more sharers than one launch takes
-    assert call(workers=(1 << 20) + 1) == -1
     assert b"at most 4096" in L.pkv_last_error()
+    assert call(workers=(1 << 20) + 1) == -1
     assert call(Hq=2) == -3                       # G = 1 is supported: only the workspace is missing
     assert call(P=24) == -1 and call(P=0) == -1 and call(P=144) == -1
     assert call(d=96) == -2 and call(B=8) == -2
