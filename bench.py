@@ -31,6 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak of MI355X
 KERNEL_LAUNCHES = 100
 # untimed steps before any timing: the first ~60 decode launches of a process run 176-182 us and
 # later ones settle at ~165 us (rocprofv3 kernel traces), so the device is brought to that state
@@ -217,8 +218,9 @@ def other_configs(pkv, W, torch, dev: str, workers: int, launches: int = 50):
     del t
     # shared prefix: 128 sequences over one 800-token prefix (logical bytes; the prefix blocks
     # are re-read by every sharer, so caches serve most of them), plain decode and the
-    # shared-prefix call; then the same over a 4096-token prefix
-    for P, key in ((800, "shared_prefix128"), (4096, "shared_prefix128_p4096")):
+    # shared-prefix call; then the same over 4096- and 8192-token prefixes
+    for P, key in ((800, "shared_prefix128"), (4096, "shared_prefix128_p4096"),
+                   (8192, "shared_prefix128_p8192")):
         b = W.config4a(prefix_len=P)
         t = stage(b)
         dus, mus, aus, cus, step = _decode_timing(pkv, torch, lambda: decode_call(t), launches)
@@ -247,6 +249,11 @@ def other_configs(pkv, W, torch, dev: str, workers: int, launches: int = 50):
                 "step_p50_us": round(sp_step, 2),
                 "logical_gbs": round(b.kv_bytes / (sp_step * 1e-6) / 1e9, 1),
                 "speedup_vs_plain_step": round(step / sp_step, 3)}}
+        # the prefix pass against the dense bf16 matrix peak: 4 * S * H_q * d * P flops
+        pf = 4 * S * Hq * d * P / (kt["prefix_states"] * 1e-6) / 1e12
+        res[key]["shared_prefix_call"]["prefix_states_roofline"] = {
+            "bound": "mfma", "achieved": round(pf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(pf / MFMA_BF16_PEAK_TFLOPS, 4)}
         del t, ws_sp
     # copy-on-write pairs: copy 8 slots of each pair's shared partial block, append B's token,
     # decode all 128 sequences (the copy and append rewrite the same slots every call)
@@ -444,7 +451,7 @@ def extend_figures(pkv, W, torch, dev: str, launches: int = 20):
     import numpy as np
     res = {}
 
-    def run(b, new, seed, key, desc):
+    def run(b, new, seed, key, desc, bound):
         q, start = W.extend_queries(b, new, seed=seed)
         qd, sd = q.to(dev), torch.from_numpy(start).to(dev)
         kp, vp = b.k_pool.to(dev), b.v_pool.to(dev)
@@ -465,6 +472,18 @@ def extend_figures(pkv, W, torch, dev: str, launches: int = 20):
              "step_p50_us": round(step, 2),
              "kv_gbs": round(b.kv_bytes / (step * 1e-6) / 1e9, 1),
              "tflops": round(flops / (step * 1e-6) / 1e12, 2)}
+        # the kernels' own time against the bound of the run: context bytes against the HBM
+        # peak for short runs, causal-attention flops against the dense bf16 matrix peak for
+        # prefill chunks
+        kus = sum(kt.values())
+        if bound == "hbm":
+            a = b.kv_bytes / (kus * 1e-6) / 1e9
+            r["roofline"] = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4)}
+        else:
+            a = flops / (kus * 1e-6) / 1e12
+            r["roofline"] = {"bound": "mfma", "achieved": round(a, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4)}
         del kp, vp, out, ws
         return r
 
@@ -473,13 +492,13 @@ def extend_figures(pkv, W, torch, dev: str, launches: int = 20):
     res["spec_verify4_gqa256"] = run(b, new, 71, "spec", "speculative verification: the GQA "
                                      "decode batch (256 sequences, 64/8 heads, d 128, bf16, B "
                                      "16), the last 4 stored tokens of each sequence as new "
-                                     "query tokens (1,024 rows per KV head)")
+                                     "query tokens (1,024 rows per KV head)", "hbm")
     b = W.small_batch(W.rng_for(W.SEED_BASE + 9, 0).integers(1024, 4096, size=8, endpoint=True),
                       64, 8, 128, 16, torch.bfloat16, seed=W.SEED_BASE + 9)
     new = np.full(8, 256)
     res["prefill_chunk256_x8"] = run(b, new, 72, "prefill", "prefill chunk: 8 sequences of "
                                      "1024..4096 stored tokens (64/8 heads, d 128, bf16, B 16), "
-                                     "the last 256 of each new (2,048 query tokens)")
+                                     "the last 256 of each new (2,048 query tokens)", "mfma")
     torch.cuda.empty_cache()
     for k, v in res.items():
         print(f"bench: {k} step p50 {v['step_p50_us']} us, {v['tflops']} TFLOP/s",
