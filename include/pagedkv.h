@@ -43,8 +43,10 @@
  * Logical-to-Physical Mapping", tau_s).
  *
  * Supported shapes: head_dim in {64, 128}; block_size in {16, 32}; kv_dtype PKV_F32, PKV_F16
- * or PKV_BF16; G = num_q_heads / num_kv_heads an integer in 1..16 for 16-bit caches and in
- * {1, 2, 4, 8} for PKV_F32.
+ * or PKV_BF16; G = num_q_heads / num_kv_heads any integer for the decode calls (query heads
+ * that one kernel segment cannot take -- more than 16 for 16-bit caches, a G outside
+ * {1, 2, 4, 8} for PKV_F32 -- run as several equal groups over the same KV head, each group
+ * reading its keys and values), 1..16 for the shared-prefix call.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -85,8 +87,10 @@ const char* pkv_last_error(void);
  * Work split: the 32-token steps of all (sequence, KV head) pairs form one line, cut into one
  * contiguous range per wavefront ("worker") of equal weight, where a step weighs one unit and
  * the start of a pair about one more; so all workers finish close together whatever the
- * length mix. A pair finished inside one range is written directly; a pair split across
- * ranges leaves one partial (m, l, acc) per range and a second kernel merges them with the
+ * length mix (a KV head whose query heads one kernel segment cannot take counts as the
+ * fewest equal groups that it can: of at most 16 query heads for 16-bit caches, of 1, 2, 4
+ * or 8 for fp32 caches). A pair finished inside one range is written directly; a pair split
+ * across ranges leaves one partial (m, l, acc) per range and a second kernel merges them with the
  * log-sum-exp rule of [P2] "Paged Attention CUDA Kernel" (exact up to rounding). The split
  * depends only on the lengths and num_workers, so a call is deterministic.
  * context_lens[s] == 0 gives a zero row.

@@ -256,6 +256,18 @@ struct PrefixFold {
   int groups;
 };
 
+// More query heads per KV head than one decode segment takes (16 on the matrix cores; 1, 2, 4
+// or 8 for fp32 caches, on the VALU kernel) run as kv_split schedule heads of G / kv_split
+// query heads each over the same pool KV head: the smallest such split (1 when G fits).
+int kv_split_for(int G, bool wide) {
+  for (int k = 1; k < G; ++k) {
+    if (G % k != 0) continue;
+    const int gv = G / k;
+    if (wide ? gv <= 16 : (gv == 1 || gv == 2 || gv == 4 || gv == 8)) return k;
+  }
+  return G > 0 ? G : 1;   // one query head per schedule head
+}
+
 // Decode (paged_attn_decode), optionally with each sequence's newest token taken from k_new /
 // v_new and stored into its slot by the same kernel (paged_attn_decode_append).
 int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const void* k_pool,
@@ -283,8 +295,12 @@ int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const v
   if (num_q_heads % num_kv_heads != 0)
     return fail(PKV_ERR_INVALID_ARG, "%s: %d query heads not a multiple of %d KV heads", fn,
                 num_q_heads, num_kv_heads);
-  const int G = num_q_heads / num_kv_heads;
   const bool wide = kv_dtype != PKV_F32;
+  // the schedule's KV heads and query heads per KV head (kv_split per pool KV head)
+  const int kv_split = kv_split_for(num_q_heads / num_kv_heads, wide);
+  const int pool_kv_heads = num_kv_heads;
+  num_kv_heads *= kv_split;
+  const int G = num_q_heads / num_kv_heads;
   bool use_mfma;
   // the suffix decode of a shared-prefix call takes the matrix-core kernel at G = 1 too: only
   // it writes the rows' log-sum-exp that the prefix fold needs
@@ -311,7 +327,7 @@ int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const v
                   pkv::kMaxSeqsPerCall);
     const size_t qb = (size_t)num_q_heads * head_dim * elem_bytes(kv_dtype);
     const size_t ob = (size_t)num_q_heads * head_dim * elem_bytes(out_dtype);
-    const size_t nb = (size_t)num_kv_heads * head_dim * elem_bytes(kv_dtype);
+    const size_t nb = (size_t)pool_kv_heads * head_dim * elem_bytes(kv_dtype);
     for (int s0 = 0; s0 < num_seqs; s0 += pkv::kMaxSeqsPerCall) {
       const int ns = std::min(pkv::kMaxSeqsPerCall, num_seqs - s0);
       const int rc = decode_impl(
@@ -320,7 +336,7 @@ int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const v
           k_new ? reinterpret_cast<const char*>(k_new) + s0 * nb : nullptr,
           v_new ? reinterpret_cast<const char*>(v_new) + s0 * nb : nullptr,
           block_tables + (size_t)s0 * max_blocks_per_seq, max_blocks_per_seq,
-          context_lens + s0, max_context_len, ns, num_q_heads, num_kv_heads, head_dim,
+          context_lens + s0, max_context_len, ns, num_q_heads, pool_kv_heads, head_dim,
           block_size, num_blocks, scale, num_workers, workspace, workspace_bytes, stream);
       if (rc != PKV_OK) return rc;
     }
@@ -395,6 +411,8 @@ int decode_impl(const char* fn, void* out, int out_dtype, const void* q, const v
   p.num_seqs = num_seqs;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
+  p.kv_split = kv_split;
+  p.pool_kv_heads = pool_kv_heads;
   p.num_blocks = num_blocks;
   p.block_size = block_size;
   p.num_workers = n;

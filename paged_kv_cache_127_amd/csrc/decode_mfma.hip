@@ -87,6 +87,7 @@ void decode_mfma(DecodeParams p) {
   const int r16 = lane & 15;
   const int jg = lane >> 4;
   const int Hkv = p.num_kv_heads;
+  const int Hp = p.pool_kv_heads;
   const int G = p.num_q_heads / Hkv;
   const int w = blockIdx.x * W + wave;
   if (w >= p.num_workers) return;
@@ -97,6 +98,7 @@ void decode_mfma(DecodeParams p) {
   ss.tables = (ctable_t)p.tables;
   ss.S = S;
   ss.Hkv = Hkv;
+  ss.ks = p.kv_split;
   ss.max_blocks = p.max_blocks;
   ss.num_blocks = p.num_blocks;
   ss.w = w;
@@ -194,12 +196,12 @@ void decode_mfma(DecodeParams p) {
     const char* qp = qrow_addr(si);
     const char* base = kv ? vbase : kbase;
     const char* nrow = reinterpret_cast<const char*>(kv ? p.v_new : p.k_new) +
-                       ((size_t)si.s * Hkv + si.g) * RB + 16 * vch;
+                       ((size_t)si.s * Hp + si.gp) * RB + 16 * vch;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int t = VTPI * f + vrow;
       const int blk = (B == 16 && t >= 16) ? b1 : b0;
-      const char* a = base + ((size_t)blk * Hkv + si.g) * kv_block_stride +
+      const char* a = base + ((size_t)blk * Hp + si.gp) * kv_block_stride +
                       (size_t)(t & (B - 1)) * RB + 16 * vch;
       if (sub && t == tn) a = nrow;
       if (si.past) a = qp;
@@ -217,14 +219,14 @@ void decode_mfma(DecodeParams p) {
     } else {
       const int b0 = valid_block(si.b0, p.num_blocks) ? si.b0 : 0;
       const int b1 = valid_block(si.b1, p.num_blocks) ? si.b1 : 0;
-      const char* t0 = kbase + ((size_t)b0 * Hkv + si.g) * kv_block_stride;
-      const char* t1 = kbase + ((size_t)b1 * Hkv + si.g) * kv_block_stride;
+      const char* t0 = kbase + ((size_t)b0 * Hp + si.gp) * kv_block_stride;
+      const char* t1 = kbase + ((size_t)b1 * Hp + si.gp) * kv_block_stride;
       const char* ka = ((B == 16 && tokA0 >= 16) ? t1 : t0) + kofs0;
       const char* kb = ((B == 16 && tokA0 + 4 >= 16) ? t1 : t0) + kofs1;
       if (p.k_new && si.k == si.ns - 1) {   // fused append, as in load_rows
         const int tn = si.L - 1 - 32 * si.k;
         const char* kn = reinterpret_cast<const char*>(p.k_new) +
-                         ((size_t)si.s * Hkv + si.g) * RB + 8 * jg * ES;
+                         ((size_t)si.s * Hp + si.gp) * RB + 8 * jg * ES;
         if (tokA0 == tn) ka = kn;
         if (tokA0 + 4 == tn) kb = kn;
       }

@@ -49,6 +49,7 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
   const int row = lane / LPR;
   const int ch = lane % LPR;
   const int Hkv = p.num_kv_heads;
+  const int Hp = p.pool_kv_heads;
   const int w = blockIdx.x * W + wave;
   if (w >= p.num_workers) return;
 
@@ -58,6 +59,7 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
   ss.tables = (ctable_t)p.tables;
   ss.S = S;
   ss.Hkv = Hkv;
+  ss.ks = p.kv_split;
   ss.max_blocks = p.max_blocks;
   ss.num_blocks = p.num_blocks;
   ss.w = w;
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
     // fused append: the newest token's rows come from k_new / v_new
     const bool sub = p.k_new && si.k == si.ns - 1;
     const int tn = si.L - 1 - 32 * si.k;
-    const size_t nofs = ((size_t)si.s * Hkv + si.g) * D * ES + (size_t)ch * 16;
+    const size_t nofs = ((size_t)si.s * Hp + si.gp) * D * ES + (size_t)ch * 16;
     // rows at or past the step's valid tokens (every row of a step described past the end of
     // the range) are masked out, so their lanes load the first query row's line, which this
     // step loads anyway: no HBM bytes are spent on them
@@ -114,7 +116,7 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams p) {
     for (int c = 0; c < NI; ++c) {
       const int tt = TPI * c + row;
       const int blk = (B == 16 && tt >= 16) ? b1 : b0;
-      const size_t ofs = ((size_t)blk * Hkv + si.g) * blk_stride +
+      const size_t ofs = ((size_t)blk * Hp + si.gp) * blk_stride +
                          (size_t)(tt & (B - 1)) * D * ES + (size_t)ch * 16;
       const bool nw = sub && tt == tn;
       const bool dead = tt >= nvalid;

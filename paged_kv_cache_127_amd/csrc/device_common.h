@@ -172,7 +172,11 @@ struct DecodeParams {
   int max_context_len;   // lengths are clamped to [0, max_context_len]
   int num_seqs;
   int num_q_heads;
-  int num_kv_heads;
+  int num_kv_heads;    // KV heads of the schedule: pool KV heads x kv_split
+  int kv_split;        // schedule KV heads per pool KV head (>= 1): more query heads per KV
+                       // head than one segment takes run as kv_split segments of
+                       // num_q_heads / num_kv_heads query heads each over the same KV head
+  int pool_kv_heads;   // KV heads of the pools and of k_new / v_new
   int num_blocks;
   int block_size;
   int num_workers;     // wavefronts of the decode kernel

@@ -204,19 +204,21 @@ __device__ inline void stage_lengths(const int32_t* lens, int S, int cap, int32_
 // Uniform description of one step of a worker's stream.
 struct StepInfo {
   int s, g, k, ns, L, b0, b1;
+  int gp;           // the pool KV head of schedule head g (g / kv_split)
   int range;        // the worker (its partial slots are 2*range, 2*range+1)
   bool rfirst;      // first step of the worker's range
   bool rlast;       // last step of the worker's range
   bool past;        // described past the end of the range (its loads are never used)
 };
 
-// Wave-uniform position in the step line: segment (s, g), step k of ns, sequence length L.
+// Wave-uniform position in the step line: segment (s, g), step k of ns, sequence length L;
+// g = gp * kv_split + gc, gp the pool KV head.
 struct Cursor {
-  int s, g, k, ns, L;
+  int s, g, k, ns, L, gp, gc;
 };
 
 __device__ inline Cursor cursor_at(const int64_t* sm_prefix, const int32_t* sm_len, int S,
-                                   int Hkv, int64_t r) {
+                                   int Hkv, int ks, int64_t r) {
   Cursor c;
   c.s = find_seq(sm_prefix, S, Hkv, r);
   const int64_t p0 = uni(sm_prefix[c.s]);
@@ -225,17 +227,27 @@ __device__ inline Cursor cursor_at(const int64_t* sm_prefix, const int32_t* sm_l
   c.g = (int)(rem / c.ns);
   c.k = (int)(rem - (int64_t)c.g * c.ns);
   c.L = uni(sm_len[c.s]);
+  c.gp = c.g / ks;
+  c.gc = c.g - c.gp * ks;
   return c;
 }
 
 // Next step of the line (the caller knows one exists; the walk stops at the last sequence
 // regardless, so that a broken caller cannot loop or leave the prefix array).
 __device__ inline void cursor_next(Cursor& c, const int64_t* sm_prefix, const int32_t* sm_len,
-                                   int S, int Hkv) {
+                                   int S, int Hkv, int ks) {
   if (++c.k < c.ns) return;
   c.k = 0;
-  if (++c.g < Hkv) return;
+  if (++c.g < Hkv) {
+    if (++c.gc == ks) {
+      c.gc = 0;
+      ++c.gp;
+    }
+    return;
+  }
   c.g = 0;
+  c.gp = 0;
+  c.gc = 0;
   do {
     ++c.s;
     c.ns = (int)(uni(sm_prefix[c.s + 1]) - uni(sm_prefix[c.s]));
@@ -260,7 +272,7 @@ struct StepStream {
   const int64_t* sm_prefix;
   const int32_t* sm_len;
   ctable_t tables;
-  int S, Hkv, max_blocks, num_blocks, w;
+  int S, Hkv, ks, max_blocks, num_blocks, w;   // ks: schedule KV heads per pool KV head
   int64_t b0, end, j;   // the range and the line index of the next step to describe
   Cursor c;             // position of step j
 
@@ -268,13 +280,14 @@ struct StepStream {
     b0 = range_b0;
     end = range_end;
     j = b0;
-    if (j < end) c = cursor_at(sm_prefix, sm_len, S, Hkv, j);
+    if (j < end) c = cursor_at(sm_prefix, sm_len, S, Hkv, ks, j);
   }
 
   __device__ StepInfo next() {
     StepInfo si;
     si.s = c.s;
     si.g = c.g;
+    si.gp = c.gp;
     si.k = c.k;
     si.ns = c.ns;
     si.L = c.L;
@@ -292,7 +305,7 @@ struct StepStream {
     si.rlast = j == end - 1;
     si.past = j >= end;
     ++j;
-    if (j < end) cursor_next(c, sm_prefix, sm_len, S, Hkv);
+    if (j < end) cursor_next(c, sm_prefix, sm_len, S, Hkv, ks);
     return si;
   }
 };

@@ -62,7 +62,12 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
   // the merge's own loads; a slot whose table entry is out of range is not written.
   constexpr int RB = D * (int)sizeof(T);   // bytes per row
   constexpr int LPR = RB / 16;
-  const bool app_wave = p.k_new != nullptr && wave == 0;      // uniform
+  // the pool KV head of schedule head g; of the kv_split segments that share it, the first
+  // stores the new row (the others would store the same bytes)
+  const int ks = p.kv_split;
+  const int gp = g / ks;
+  const int Hp = p.pool_kv_heads;
+  const bool app_wave = p.k_new != nullptr && wave == 0 && g - gp * ks == 0;   // uniform
   const bool app = app_wave && lane < 2 * LPR;
   const int kvsel = lane < LPR ? 0 : 1;
   const int ch = lane % LPR;
@@ -75,14 +80,14 @@ __global__ __launch_bounds__(256) void splitk_merge(DecodeParams p) {
       blk = ((ctable_t)p.tables)[(size_t)s * p.max_blocks + (Lnew - 1) / p.block_size];
       if (app)
         xnew = load16(reinterpret_cast<const char*>(kvsel ? p.v_new : p.k_new) +
-                      ((size_t)s * Hkv + g) * RB + 16 * ch);
+                      ((size_t)s * Hp + gp) * RB + 16 * ch);
     }
   }
   auto append_store = [&]() {
     if (app && Lnew > 0 && valid_block(blk, p.num_blocks)) {
       const int off = (Lnew - 1) % p.block_size;
       char* dst = reinterpret_cast<char*>(kvsel ? p.v_pool_w : p.k_pool_w) +
-                  (((size_t)blk * Hkv + g) * p.block_size + off) * RB + 16 * ch;
+                  (((size_t)blk * Hp + gp) * p.block_size + off) * RB + 16 * ch;
       *reinterpret_cast<u32x4*>(dst) = xnew;
     }
   };

@@ -355,6 +355,43 @@ def test_config5_steps():
         assert err <= 2e-3
 
 
+@pytest.mark.parametrize("dt,hq,hkv,d,B", [
+    ("bf16", 32, 1, 128, 16),    # multi-query: two schedule heads of 16 per KV head
+    ("f16", 48, 1, 64, 32),      # three of 16
+    ("bf16", 128, 2, 128, 16),   # four of 16 per KV head, two KV heads
+    ("bf16", 17, 1, 64, 16),     # prime G: seventeen of one (the VALU kernel)
+    ("f16", 18, 1, 128, 32),     # two of 9
+    ("f32", 12, 1, 64, 16),      # fp32 caches: three of 4
+    ("f32", 6, 2, 128, 32),      # three of 2
+    ("f32", 16, 1, 128, 16),     # two of 8
+])
+def test_many_query_heads_per_kv_head(dt, hq, hkv, d, B):
+    """More query heads per KV head than one kernel segment takes (16 on the matrix cores; 1, 2,
+    4 or 8 for fp32 caches) run as several schedule heads over the same KV head: plain decode
+    at two worker counts and the fused append + decode (each new row stored once, the pools
+    bit-exact), every row against the oracle."""
+    lens = [1, 15, 16, 17, 33, 100, 511, 1000, 0]
+    seed = zlib.crc32(repr((dt, hq, hkv, d, B)).encode()) % 10000
+    b = W.small_batch(lens, hq, hkv, d, B, DT[dt], seed=seed, poison=True)
+    ref = oracle_decode(b)
+    for workers in (0, 7):
+        got = DeviceBatch(b).decode(workers=workers)
+        assert np.isfinite(got[:8].numpy()).all()
+        assert max_err(got, ref) <= TOL[DT[dt]], workers
+    k_new, v_new = W.new_tokens(seed, 3, len(lens), hkv, d, DT[dt])
+    db = DeviceBatch(b)
+    got2 = db.decode_append(k_new.cuda(), v_new.cuda())
+    kr, vr = b.k_pool.clone(), b.v_pool.clone()
+    for s, L in enumerate(lens):
+        if L > 0:
+            blk, off = oracle.token_address(L - 1, b.tables[s], B)
+            kr[blk, :, off] = k_new[s]
+            vr[blk, :, off] = v_new[s]
+    assert torch.equal(bits(db.k_pool.cpu()), bits(kr))
+    assert torch.equal(bits(db.v_pool.cpu()), bits(vr))
+    assert max_err(got2, oracle.paged_decode(b.q, kr, vr, b.tables, b.lengths, B)) <= TOL[DT[dt]]
+
+
 def test_one_very_long_sequence():
     """A 131,072-token sequence (8,192 blocks) beside a short and an empty one, 64/8 heads,
     bf16: the long sequence's 8 segments are cut over every worker (automatic count, and 5,000

@@ -107,8 +107,12 @@ def test_decode_argument_checks():
     assert _decode_call(d=96)[0] == -2
     assert _decode_call(B=8)[0] == -2
     assert _decode_call(Hq=6, Hkv=4)[0] == -1
-    assert _decode_call(kv_dtype=0, Hq=3, Hkv=1)[0] == -2      # fp32 with G = 3
-    assert _decode_call(Hq=17 * 2, Hkv=2)[0] == -2             # G = 17
+    # any G: more query heads per KV head than one kernel segment takes run as several
+    # schedule heads over the same KV head (fp32 G = 3: three of one; G = 17: seventeen of one)
+    rc, msg = _decode_call(kv_dtype=0, Hq=3, Hkv=1)
+    assert rc == -3 and "workspace" in msg
+    rc, msg = _decode_call(Hq=17 * 2, Hkv=2)
+    assert rc == -3 and "workspace" in msg
     assert _decode_call(max_ctx=129)[0] == -1                  # > 8 blocks of 16
     assert _decode_call(part=-1)[0] == -1                      # negative worker count
     rc, msg = _decode_call(S=5000)           # runs as launches of at most 4096 sequences,
