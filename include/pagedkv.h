@@ -46,7 +46,7 @@
  * or PKV_BF16; G = num_q_heads / num_kv_heads any integer for the decode calls (query heads
  * that one kernel segment cannot take -- more than 16 for 16-bit caches, a G outside
  * {1, 2, 4, 8} for PKV_F32 -- run as several equal groups over the same KV head, each group
- * reading its keys and values), 1..16 for the shared-prefix call.
+ * reading its keys and values).
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -196,7 +196,7 @@ int paged_attn_decode_append(void* out, int out_dtype, const void* q, void* k_po
  *   context_lens   every context_lens[s] >= prefix_len (the suffix may be empty)
  *   workspace      device, 256-byte aligned, at least pkv_shared_prefix_workspace_size(...)
  *                  bytes for the same sizes, num_workers and prefix_len
- * 16-bit caches with 1 to 16 query heads per KV head (PKV_ERR_UNSUPPORTED otherwise); one call
+ * 16-bit caches (PKV_ERR_UNSUPPORTED otherwise), any number of query heads per KV head; one call
  * per group of sequences that share a prefix. Under PAGEDKV_VALIDATE the shared table entries,
  * the lengths and the prefix ids are checked first.
  * --------------------------------------------------------------------------------------- */

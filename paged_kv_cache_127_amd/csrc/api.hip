@@ -874,8 +874,6 @@ int paged_attn_decode_shared_prefix(void* out, int out_dtype, const void* q, con
     return fail(PKV_ERR_INVALID_ARG, "%s: %d query heads not a multiple of %d KV heads", fn,
                 num_q_heads, num_kv_heads);
   const int G = num_q_heads / num_kv_heads;
-  if (G < 1 || G > 16)
-    return fail(PKV_ERR_UNSUPPORTED, "%s: %d query heads per KV head (1 to 16)", fn, G);
   // the suffix decode and the merge take every sharer in one launch (checked before anything
   // is enqueued)
   if (num_seqs > pkv::kMaxSeqsPerCall)

@@ -70,6 +70,10 @@ CASES = [
     ([1, 15, 16, 17, 33, 100, 511, 0], 64, 4, 4, 128, 16, "bf16"),
     ([3, 0, 250, 40, 9], 96, 8, 8, 64, 32, "f16"),
     ([7] * 130, 4128, 2, 2, 128, 16, "bf16"),           # 130 rows: the tile-sharing prefix kernel
+    # more than 16 query heads per KV head: the suffix decode as several schedule heads
+    ([1, 15, 16, 17, 33, 100, 0], 64, 32, 1, 128, 16, "bf16"),    # G = 32: two of 16
+    ([3, 250, 40, 9], 96, 17, 1, 64, 32, "f16"),                  # G = 17: seventeen of one
+    ([2] * 8, 4112, 48, 1, 64, 16, "bf16"),                       # G = 48, the wide prefix kernel
 ]
 
 

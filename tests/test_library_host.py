@@ -198,7 +198,7 @@ def test_shared_prefix_argument_checks():
     assert call(S=0) == 0
     assert call(pre=None) == -1
     assert call(kv_dtype=0) == -2                 # fp32 cache
-    assert call(Hq=34, Hkv=2) == -2               # G = 17
+    assert call(Hq=34, Hkv=2) == -3               # G = 17 is supported: no workspace
     assert call(S=4097) == -2                     # more sharers than one launch takes
     assert b"at most 4096" in L.pkv_last_error()
     assert call(workers=(1 << 20) + 1) == -1
