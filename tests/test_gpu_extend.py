@@ -53,6 +53,8 @@ CASES = [
     ([77, 200], [40, 9], 24, 4, 64, 32, "bf16"),                  # G = 6
     ([150, 400, 60], [130, 200, 60], 4, 4, 128, 16, "bf16"),      # G = 1, whole-run prefill
     ([150, 400, 60], [100, 127, 60], 4, 4, 64, 32, "f16"),        # G = 1, one row short
+    ([90, 300, 17], [3, 4, 1], 32, 1, 128, 16, "bf16"),           # G = 32 (multi-query): 128 rows
+    ([90, 300, 17], [1, 3, 2], 34, 2, 64, 32, "f16"),             # G = 17
 ]
 
 
